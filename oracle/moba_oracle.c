@@ -1,0 +1,320 @@
+/*
+ * MoBA forward pass -- plain fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code with
+ * the GPU path and must never be used to produce a product result.
+ *
+ * Sources (cited by page title and section):
+ *  [S] "MoBA: Mixture of Block Attention for Long-Context LLMs", summary page on
+ *      paper-graph-ui.vercel.app, section 3.4 "Detailed, Sentence-Based
+ *      Technical Breakdown" and its sub-headings.
+ *  [R] the paperhub.cn review page for the same paper, authors' rebuttal (W1).
+ *  [C] "MoBA (Mixture of Block Attention)" concept note (research-hub),
+ *      "Key math / How it works".
+ *
+ * Layout (packed variable-length batch, "THD"):
+ *   q[T][Hq][d], k[T][Hkv][d], v[T][Hkv][d]; elements are fp32, or bf16 given
+ *   as raw 16-bit patterns; both are widened to double exactly.
+ *   cu_seqlens[S+1]: sequence s owns rows [cu[s], cu[s+1]).
+ *
+ * Readings taken where the pages are silent or disagree (listed in the design
+ * notes as well):
+ *   - blocks are 0-indexed per sequence: block j of a sequence of length L
+ *     covers local rows [jB, min((j+1)B, L)); the last block may be short;
+ *   - the query's own block c is always selected and counts toward k, so at
+ *     most k-1 earlier blocks are picked by score;
+ *   - candidates for the score-based pick are blocks j < c only (future blocks
+ *     are -inf and the current block is forced);
+ *   - ties in score are broken by the lower block index;
+ *   - the gate score is the raw inner product (no temperature); attention
+ *     logits use the caller's softmax scale (1/sqrt(d) by default);
+ *   - each query head selects its own blocks; query head h reads kv head
+ *     h / (Hq/Hkv);
+ *   - lse is the natural-log log-sum-exp of the scaled logits.
+ *
+ * Pinned by tests/test_oracle_pins.py (dense special case, block-local case,
+ * brute-force subset search, explicit-mask softmax, closed forms, varlen and
+ * merge identities, printed sparsities).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double load_elem(const void *p, int64_t i, int is_bf16) {
+  if (is_bf16) {
+    uint32_t u = ((uint32_t)((const uint16_t *)p)[i]) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float *)p)[i];
+}
+
+/* Sequence that owns global row t (cu is non-decreasing). */
+static int seq_of_row(const int32_t *cu, int S, int64_t t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) / 2;
+    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  /* skip empty sequences that start at the same offset */
+  while (lo + 1 < S && (int64_t)cu[lo + 1] <= t) lo++;
+  return lo;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+/* Number of blocks of each sequence, and the first global block index of each
+ * sequence: first[s] = sum_{s'<s} ceil(L_s'/B), first[S] = total. */
+int64_t oracle_block_first(const int32_t *cu, int S, int B, int64_t *first) {
+  int64_t acc = 0;
+  for (int s = 0; s < S; ++s) {
+    if (first) first[s] = acc;
+    acc += ceil_div((int64_t)cu[s + 1] - cu[s], B);
+  }
+  if (first) first[S] = acc;
+  return acc;
+}
+
+/* [S] "Affinity Scoring": the block representative is the mean of the block's
+ * key vectors (over the rows it actually has).
+ * kbar: [total_blocks][Hkv][d], global block index = first[s] + j. */
+void oracle_meanpool(const void *k, int is_bf16, int64_t T, int Hkv, int d,
+                     const int32_t *cu, int S, int B, double *kbar) {
+  (void)T;
+  int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (S + 1));
+  oracle_block_first(cu, S, B, first);
+  for (int s = 0; s < S; ++s) {
+    int64_t a = cu[s], L = (int64_t)cu[s + 1] - cu[s];
+    int64_t nb = ceil_div(L, B);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < nb; ++j) {
+      int64_t r0 = j * B, r1 = (j + 1) * B < L ? (j + 1) * B : L;
+      for (int g = 0; g < Hkv; ++g) {
+        double *dst = kbar + ((first[s] + j) * Hkv + g) * (int64_t)d;
+        for (int e = 0; e < d; ++e) dst[e] = 0.0;
+        for (int64_t r = r0; r < r1; ++r)
+          for (int e = 0; e < d; ++e)
+            dst[e] += load_elem(k, ((a + r) * Hkv + g) * (int64_t)d + e, is_bf16);
+        for (int e = 0; e < d; ++e) dst[e] /= (double)(r1 - r0);
+      }
+    }
+  }
+  free(first);
+}
+
+typedef struct { double s; int j; } cand_t;
+
+/* Order used by the top-k gate: higher score first, then lower block index. */
+static int cand_cmp(const void *pa, const void *pb) {
+  const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return (a->j > b->j) - (a->j < b->j);
+}
+
+/* Block selection for a list of query rows (all heads).
+ * [S] "Affinity Scoring" (s_i = <q, meanpool(K[I_i])>), "Top-k Gating" (g_i,
+ * shared-expert current block), "Causality Enforcement" mechanism 1 (future
+ * blocks get -inf); [R] rebuttal W1: every query head selects its own blocks.
+ *
+ * rows: global row indices (NULL = all T rows in order), n_rows entries.
+ * sel: [n_rows][Hq][topk] local block ids, ascending, -1 padded.
+ * near_tie: [n_rows][Hq], 1 when the k-th and (k+1)-th ranked gate scores
+ *   (the (k-1)-th and k-th ranked historical scores, the current block being
+ *   rank 1) differ by less than 1e-3 relative to the larger magnitude.
+ * scores: optional [n_rows][Hq][max_blocks] raw scores of candidate blocks
+ *   j < c, NAN elsewhere. */
+void oracle_select(const void *q, int is_bf16, const double *kbar, int64_t T,
+                   int Hq, int Hkv, int d, const int32_t *cu, int S, int B,
+                   int topk, const int64_t *rows, int64_t n_rows, int32_t *sel,
+                   uint8_t *near_tie, double *scores, int max_blocks) {
+  int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (S + 1));
+  oracle_block_first(cu, S, B, first);
+  int G = Hq / Hkv;
+  if (!rows) n_rows = T;
+#pragma omp parallel
+  {
+    cand_t *cand = NULL;
+    int64_t cap = 0;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t rh = 0; rh < n_rows * Hq; ++rh) {
+      int64_t ri = rh / Hq;
+      int h = (int)(rh % Hq);
+      int64_t t = rows ? rows[ri] : ri;
+      int s = seq_of_row(cu, S, t);
+      int64_t local = t - cu[s];
+      int c = (int)(local / B);            /* current block */
+      int g = h / G;                       /* kv head of this query head */
+      if (c > cap) { free(cand); cap = c + 64; cand = (cand_t *)malloc(sizeof(cand_t) * cap); }
+      /* scores of all earlier blocks; later blocks are never candidates */
+      for (int j = 0; j < c; ++j) {
+        const double *kb = kbar + ((first[s] + j) * Hkv + g) * (int64_t)d;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e)
+          acc += load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16) * kb[e];
+        cand[j].s = acc;
+        cand[j].j = j;
+      }
+      if (scores) {
+        double *dst = scores + rh * (int64_t)max_blocks;
+        for (int j = 0; j < max_blocks; ++j) dst[j] = NAN;
+        for (int j = 0; j < c && j < max_blocks; ++j) dst[j] = cand[j].s;
+      }
+      qsort(cand, (size_t)c, sizeof(cand_t), cand_cmp);
+      int n_hist = topk - 1 < c ? topk - 1 : c;  /* the current block takes one of the k */
+      uint8_t flag = 0;
+      if (topk - 1 >= 1 && c > topk - 1) {
+        double a = cand[topk - 2].s, b = cand[topk - 1].s;
+        double m = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
+        flag = fabs(a - b) < 1e-3 * m;
+      }
+      if (near_tie) near_tie[rh] = flag;
+      /* emit ascending: chosen earlier blocks sorted by index, then c */
+      int32_t *out = sel + rh * (int64_t)topk;
+      int n = 0;
+      for (int j = 0; j < c && n < n_hist; ++j) {
+        int chosen = 0;
+        for (int r = 0; r < n_hist; ++r) chosen |= (cand[r].j == j);
+        if (chosen) out[n++] = j;
+      }
+      out[n++] = c;
+      while (n < topk) out[n++] = -1;
+    }
+    free(cand);
+  }
+  free(first);
+}
+
+/* Attention of one query row over an explicit key-row set.
+ * [S] "The Core MoBA Attention Equation": Softmax(q K[I]^T) V[I], with the
+ * caller's logit scale; lse = log sum_u exp(z_u). */
+static void attend_rows(const void *q, const void *k, const void *v, int is_bf16,
+                        int Hq, int Hkv, int d, int64_t t, int h, int g,
+                        const int64_t *keys, int64_t nk, double scale,
+                        double *z, double *out, double *lse) {
+  double m = -INFINITY;
+  for (int64_t i = 0; i < nk; ++i) {
+    double acc = 0.0;
+    for (int e = 0; e < d; ++e)
+      acc += load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16) *
+             load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+    z[i] = scale * acc;
+    if (z[i] > m) m = z[i];
+  }
+  double l = 0.0;
+  for (int e = 0; e < d; ++e) out[e] = 0.0;
+  for (int64_t i = 0; i < nk; ++i) {
+    double p = exp(z[i] - m);
+    l += p;
+    for (int e = 0; e < d; ++e)
+      out[e] += p * load_elem(v, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+  }
+  for (int e = 0; e < d; ++e) out[e] /= l;
+  *lse = m + log(l);
+}
+
+/* Attention over the union of the selected blocks.
+ * [S] "Top-k Gating" (I = union of selected blocks), "Causality Enforcement"
+ * mechanism 2 (causal mask inside the current block, none in earlier blocks);
+ * [C] "Key math / How it works".
+ * sel: [n_rows][Hq][topk] local block ids as produced by oracle_select (or any
+ * other selection that contains the current block and no later block).
+ * out: [n_rows][Hq][d], lse: [n_rows][Hq]. */
+void oracle_attend(const void *q, const void *k, const void *v, int is_bf16,
+                   int64_t T, int Hq, int Hkv, int d, const int32_t *cu, int S,
+                   int B, int topk, const int32_t *sel, const int64_t *rows,
+                   int64_t n_rows, double scale, double *out, double *lse) {
+  int G = Hq / Hkv;
+  if (!rows) n_rows = T;
+#pragma omp parallel
+  {
+    int64_t cap = 0;
+    int64_t *keys = NULL;
+    double *z = NULL;
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t rh = 0; rh < n_rows * Hq; ++rh) {
+      int64_t ri = rh / Hq;
+      int h = (int)(rh % Hq);
+      int64_t t = rows ? rows[ri] : ri;
+      int s = seq_of_row(cu, S, t);
+      int64_t a = cu[s], L = (int64_t)cu[s + 1] - cu[s], local = t - a;
+      int64_t c = local / B;
+      const int32_t *my = sel + rh * (int64_t)topk;
+      int64_t need = (int64_t)topk * B + 1;
+      if (need > cap) {
+        free(keys); free(z);
+        cap = need;
+        keys = (int64_t *)malloc(sizeof(int64_t) * cap);
+        z = (double *)malloc(sizeof(double) * cap);
+      }
+      int64_t nk = 0;
+      for (int i = 0; i < topk; ++i) {
+        int64_t j = my[i];
+        if (j < 0) continue;
+        int64_t r0 = j * B;
+        int64_t r1 = (j == c) ? local + 1 : ((j + 1) * B < L ? (j + 1) * B : L);
+        for (int64_t r = r0; r < r1; ++r) keys[nk++] = a + r;
+      }
+      attend_rows(q, k, v, is_bf16, Hq, Hkv, d, t, h, h / G, keys, nk, scale, z,
+                  out + rh * (int64_t)d, lse + rh);
+    }
+    free(keys); free(z);
+  }
+}
+
+/* Full MoBA forward for a list of rows: meanpool, select, attend.
+ * sel_out / near_tie_out may be NULL. */
+void oracle_moba(const void *q, const void *k, const void *v, int is_bf16,
+                 int64_t T, int Hq, int Hkv, int d, const int32_t *cu, int S,
+                 int B, int topk, double scale, const int64_t *rows,
+                 int64_t n_rows, double *out, double *lse, int32_t *sel_out,
+                 uint8_t *near_tie_out) {
+  int64_t nb = oracle_block_first(cu, S, B, NULL);
+  double *kbar = (double *)malloc(sizeof(double) * (nb > 0 ? nb : 1) * Hkv * d);
+  oracle_meanpool(k, is_bf16, T, Hkv, d, cu, S, B, kbar);
+  int64_t nr = rows ? n_rows : T;
+  int32_t *sel = sel_out ? sel_out : (int32_t *)malloc(sizeof(int32_t) * (nr > 0 ? nr : 1) * Hq * topk);
+  oracle_select(q, is_bf16, kbar, T, Hq, Hkv, d, cu, S, B, topk, rows, nr, sel,
+                near_tie_out, NULL, 0);
+  oracle_attend(q, k, v, is_bf16, T, Hq, Hkv, d, cu, S, B, topk, sel, rows, nr,
+                scale, out, lse);
+  if (!sel_out) free(sel);
+  free(kbar);
+}
+
+/* Dense causal attention (the full-attention baseline the pages compare to):
+ * [S] "Standard Attention Baseline" with the usual causal mask, per sequence. */
+void oracle_dense_causal(const void *q, const void *k, const void *v, int is_bf16,
+                         int64_t T, int Hq, int Hkv, int d, const int32_t *cu,
+                         int S, const int64_t *rows, int64_t n_rows, double scale,
+                         double *out, double *lse) {
+  int G = Hq / Hkv;
+  if (!rows) n_rows = T;
+#pragma omp parallel
+  {
+    int64_t cap = 0;
+    int64_t *keys = NULL;
+    double *z = NULL;
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t rh = 0; rh < n_rows * Hq; ++rh) {
+      int64_t ri = rh / Hq;
+      int h = (int)(rh % Hq);
+      int64_t t = rows ? rows[ri] : ri;
+      int s = seq_of_row(cu, S, t);
+      int64_t a = cu[s], nk = t - a + 1;
+      if (nk > cap) {
+        free(keys); free(z);
+        cap = nk;
+        keys = (int64_t *)malloc(sizeof(int64_t) * cap);
+        z = (double *)malloc(sizeof(double) * cap);
+      }
+      for (int64_t i = 0; i < nk; ++i) keys[i] = a + i;
+      attend_rows(q, k, v, is_bf16, Hq, Hkv, d, t, h, h / G, keys, nk, scale, z,
+                  out + rh * (int64_t)d, lse + rh);
+    }
+    free(keys); free(z);
+  }
+}
