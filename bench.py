@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoBA forward pass on one MI355X.
+
+One step = the whole forward pass over one batch (block table, pooled keys,
+gate, dispatch, own-block and earlier-block attention, merge), launched through
+the C ABI's stage entry points on torch's current stream so that each stage
+can be bracketed by HIP events on that same stream. Inputs are seeded synthetic
+tensors already resident in HBM when timing starts.
+
+Prints one JSON line (see the design doc for the fields): the value is effective
+TFLOP/s, i.e. 4*d*sum over (row, head) of the keys actually attended (earlier
+blocks in full, own block causally) divided by the step time.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+DEFAULT_WORKLOAD = "gqa32x8_t1m_b4096_k12_bf16"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+HEAD_DIM = 128
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def effective_flop(lengths, B, k, Hq, d=HEAD_DIM):
+    """4*d*Hq*sum_t |I(t)|: earlier chosen blocks count B keys each, the own
+    block counts the keys up to and including the query."""
+    tot = 0
+    for L in lengths:
+        t = np.arange(L, dtype=np.int64)
+        c = t // B
+        tot += int(((np.minimum(k, c + 1) - 1) * B + (t % B) + 1).sum())
+    return 4.0 * d * Hq * tot
+
+
+def dense_flop(lengths, Hq, d=HEAD_DIM):
+    return float(sum(2.0 * d * Hq * L * (L + 1) for L in lengths))
+
+
+class Timer:
+    """Pairs of HIP events (torch.cuda.Event records on the current stream)."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def run(self, name, fn):
+        import torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def totals(self):
+        return {n: (sum(a.elapsed_time(b) for a, b in v), len(v)) for n, v in self.pairs.items()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows the CPU oracle times (0 = sized for about 15 s)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON with measured HBM bytes per launch of the dominant kernel")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the forward pass "
+              "would shard by kv-head group with no exchange; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_moba_amd import moba, synth
+    from block_sparse_long_moba_amd.tensors import to_device, workspace_view
+
+    w = synth.WORKLOADS[args.workload]
+    B, k, Hq, Hkv = w.block_size, w.topk, w.num_q_heads, w.num_kv_heads
+    T = w.total_tokens
+    log("workload %s: generating seeded inputs" % w.name)
+    t0 = time.time()
+    inp = synth.generate(w)
+    log("inputs ready in %.1f s; uploading" % (time.time() - t0))
+    torch.cuda.set_device(0)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    shape = moba.shape_of(q, kk, cu, max_seqlen=max(w.lengths))
+    P = Hkv
+    while P > 1 and moba.moba_fwd_workspace_size(shape, B, k, P) > (48 << 30):
+        P //= 2
+    lay = moba.moba_plan(shape, B, k, P)
+    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    passes = list(range(0, Hkv, lay.kv_heads_per_pass))
+    log("workspace %.1f GiB, %d pass(es) of %d kv heads" % (lay.total_bytes / 2**30, len(passes),
+                                                         lay.kv_heads_per_pass))
+
+    def step(tm):
+        tm.run("seqtable", lambda: moba.moba_seqtable(cu, shape, B, lay, ws))
+        tm.run("meanpool", lambda: moba.moba_meanpool(kk, shape, B, lay, ws))
+        for g0 in passes:
+            tm.run("gate", lambda: moba.moba_gate(q, shape, B, k, lay, ws, g0))
+            tm.run("dispatch", lambda: moba.moba_dispatch(shape, B, k, lay, ws, g0))
+            tm.run("attn_diag", lambda: moba.moba_attn_fwd_diag(q, kk, v, shape, B, k, lay, ws, g0))
+            tm.run("attn_hist", lambda: moba.moba_attn_fwd_hist(q, kk, shape, B, k, lay, ws, g0))
+            tm.run("merge", lambda: moba.moba_merge(shape, B, k, lay, ws, out, lse, g0))
+
+    # earlier-block rows dispatched per pass (for the dominant kernel's flops)
+    nbins = lay.kv_heads_per_pass * lay.num_blocks_bound
+    hist_rows = []
+    moba.moba_seqtable(cu, shape, B, lay, ws)
+    moba.moba_meanpool(kk, shape, B, lay, ws)
+    for g0 in passes:
+        moba.moba_gate(q, shape, B, k, lay, ws, g0)
+        moba.moba_dispatch(shape, B, k, lay, ws, g0)
+        torch.cuda.synchronize()
+        off = workspace_view(ws, lay.bins_offset + 4 * nbins, nbins + 1, torch.int32)
+        hist_rows.append(int(off[-1].item()) & 0xFFFFFFFF)
+
+    log("warmup %d step(s)" % args.warmup)
+    for _ in range(args.warmup):
+        step(Timer())
+    torch.cuda.synchronize()
+    log("timing %d step(s)" % args.steps)
+    tm = Timer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(tm)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stages = {n: (tot / args.steps, cnt) for n, (tot, cnt) in tm.totals().items()}
+    log("step %.2f ms; stages %s" % (ms, {n: round(v[0], 3) for n, v in stages.items()}))
+
+    eff = effective_flop(w.lengths, B, k, Hq)
+    value = eff / (ms * 1e-3) / 1e12
+    es = 2 if w.dtype == "bf16" else 4
+    # dominant kernel: earlier-block attention, MFMA bound
+    hist_ms_total, hist_launches = tm.totals()["attn_hist"]
+    hist_flop_per_step = 4.0 * HEAD_DIM * B * sum(hist_rows)
+    hist_avg_ms = hist_ms_total / hist_launches
+    hist_flop_per_launch = hist_flop_per_step / len(passes)
+    achieved = hist_flop_per_launch / (hist_avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    traffic = None
+    if args.traffic:
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    roofline = {"kernel": "attn_hist (earlier-block attention)", "bound": "mfma",
+                "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "avg_launch_ms": round(hist_avg_ms, 4), "launches_per_step": len(passes),
+                "flop_per_launch": hist_flop_per_launch}
+
+    # memory-bound stages against the HBM roofline
+    nb = sum(-(-L // B) for L in w.lengths)
+    mp_bytes = T * Hkv * HEAD_DIM * es + nb * Hkv * HEAD_DIM * 4
+    gate_bytes = T * Hq * HEAD_DIM * es + T * Hq * k * 4
+    hbm = {}
+    for name, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes)):
+        sm = stages[name][0]
+        hbm[name] = {"ms": round(sm, 4), "GB/s": round(nbytes / (sm * 1e-3) / 1e9, 1),
+                     "frac": round(nbytes / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    attn_ms = stages["attn_diag"][0] + stages["attn_hist"][0]
+    attn_eff = eff / (attn_ms * 1e-3) / 1e12
+
+    dense = None
+    if not args.no_dense:
+        log("dense causal baseline")
+        dws = torch.empty(moba.moba_dense_causal_workspace_size(shape), dtype=torch.uint8,
+                          device="cuda")
+        dout = torch.empty_like(q)
+        moba.moba_dense_causal_fwd(q, kk, v, cu, out=dout, workspace=dws,
+                                   max_seqlen=max(w.lengths))
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moba.moba_dense_causal_fwd(q, kk, v, cu, out=dout, workspace=dws,
+                                   max_seqlen=max(w.lengths))
+        b.record()
+        torch.cuda.synchronize()
+        dms = a.elapsed_time(b)
+        dfl = dense_flop(w.lengths, Hq)
+        dense = {"ms": round(dms, 3), "TFLOP/s": round(dfl / (dms * 1e-3) / 1e12, 1),
+                 "mfma_frac": round(dfl / (dms * 1e-3) / 1e12 / peak, 4),
+                 "speedup_moba_vs_dense": round(dms / ms, 3)}
+        del dws, dout
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, w, args.cpu_rows)
+
+    res = {
+        "metric": "MoBA fwd ms + effective TFLOP/s at 128K/1M tokens (8B heads), % MFMA peak",
+        "value": round(value, 3), "unit": "TFLOP/s (effective)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, per-block key offsets)",
+        "config": {"workload": w.name, "seq_lens": list(w.lengths), "total_tokens": T,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": HEAD_DIM, "block_size": B,
+                   "topk": k, "kv_heads_per_pass": lay.kv_heads_per_pass,
+                   "parallelism": "single GPU"},
+        "effective_flop": eff,
+        "attention_effective_TFLOPs": round(attn_eff, 2),
+        "attention_mfma_frac": round(attn_eff / peak, 4),
+        "stage_ms": {n: round(v[0], 4) for n, v in stages.items()},
+        "hbm": hbm,
+        "dense_causal": dense,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(inp, w, n_rows):
+    """The fp64 oracle on a bounded sample of the same workload: pooled keys of
+    every block, then selection and attention for n sampled rows (all heads)."""
+    import oracle
+    B, k, Hq = w.block_size, w.topk, w.num_q_heads
+    rng = np.random.default_rng(w.seed + 77)
+    T = w.total_tokens
+    if n_rows <= 0:
+        # about 15 s of attention work at ~1.5 GFLOP/s per thread (fp64, plain loops)
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        per_row = 4.0 * HEAD_DIM * Hq * (k * B)
+        n_rows = int(max(8, min(T, 15 * 1.5e9 * threads / per_row)))
+    rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False)).astype(np.int64)
+    log("cpu baseline: oracle on %d sampled rows" % len(rows))
+    t0 = time.time()
+    kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+    sel, _, _ = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows)
+    oracle.attend(inp.q, inp.k, inp.v, inp.cu_seqlens, B, k, sel, rows=rows)
+    dt = time.time() - t0
+    cu = inp.cu_seqlens
+    seq = np.searchsorted(cu, rows, side="right") - 1
+    local = rows - cu[seq]
+    c = local // B
+    keys = (np.minimum(k, c + 1) - 1) * B + local % B + 1
+    flop = 4.0 * HEAD_DIM * Hq * float(keys.sum())
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s (effective)",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "%d random rows x %d heads of %s (pooled keys of all blocks, then "
+                      "selection and attention for the sampled rows)" % (len(rows), Hq, w.name)}
+
+
+if __name__ == "__main__":
+    main()

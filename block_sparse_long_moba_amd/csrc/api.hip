@@ -1,0 +1,499 @@
+// C ABI of the MoBA forward pass: argument checks, workspace plan, and the
+// order in which the stages are enqueued. Declared in include/moba.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <string>
+
+#include "moba_internal.h"
+
+using namespace moba;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moba_status_t fail(moba_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+moba_status_t fail(moba_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moba_status_t hip_fail(hipError_t e, const char *where) {
+  return fail(MOBA_ERROR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define MOBA_HIP(call, where)                          \
+  do {                                                 \
+    hipError_t e_ = (call);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, where);  \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+moba_status_t check_shape(const moba_shape_t *sh) {
+  if (!sh) return fail(MOBA_ERROR_INVALID_VALUE, "shape is NULL");
+  if (sh->total_tokens < 0) return fail(MOBA_ERROR_INVALID_VALUE, "total_tokens < 0");
+  if (sh->num_seqs < 0 || (sh->num_seqs == 0 && sh->total_tokens != 0))
+    return fail(MOBA_ERROR_INVALID_VALUE, "num_seqs must be >= 1 when total_tokens > 0");
+  if (sh->max_seqlen < 0) return fail(MOBA_ERROR_INVALID_VALUE, "max_seqlen < 0");
+  if (sh->num_q_heads < 1 || sh->num_kv_heads < 1)
+    return fail(MOBA_ERROR_INVALID_VALUE, "head counts must be >= 1");
+  if (sh->num_q_heads % sh->num_kv_heads != 0)
+    return fail(MOBA_ERROR_INVALID_VALUE, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                sh->num_q_heads, sh->num_kv_heads);
+  if (sh->dtype != MOBA_DTYPE_FP32 && sh->dtype != MOBA_DTYPE_BF16)
+    return fail(MOBA_ERROR_INVALID_VALUE, "unknown dtype %d", (int)sh->dtype);
+  if (sh->head_dim < 1) return fail(MOBA_ERROR_INVALID_VALUE, "head_dim < 1");
+  if (sh->head_dim != kHeadDim)
+    return fail(MOBA_ERROR_UNSUPPORTED, "head_dim %d: only %d is supported", sh->head_dim, kHeadDim);
+  if (sh->total_tokens >= (int64_t(1) << 31))
+    return fail(MOBA_ERROR_UNSUPPORTED, "total_tokens must be < 2^31");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t check_moba_args(const moba_shape_t *sh, int32_t B, int32_t k) {
+  moba_status_t st = check_shape(sh);
+  if (st != MOBA_SUCCESS) return st;
+  if (B < 1) return fail(MOBA_ERROR_INVALID_VALUE, "block_size must be >= 1");
+  if (k < 1) return fail(MOBA_ERROR_INVALID_VALUE, "topk must be >= 1");
+  if (B % kKeyTile != 0)
+    return fail(MOBA_ERROR_UNSUPPORTED, "block_size %d: must be a multiple of %d", B, kKeyTile);
+  if ((uint64_t)sh->total_tokens * (uint64_t)sh->num_q_heads * (uint64_t)k >= (uint64_t(1) << 32))
+    return fail(MOBA_ERROR_UNSUPPORTED, "total_tokens * num_q_heads * topk must be < 2^32");
+  const int64_t T = sh->total_tokens;
+  const int64_t maxlen = sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, T) : T;
+  const int64_t maxblk = ceil_div(maxlen, B);
+  if (k - 1 > kMaxHistPick && k < maxblk)
+    return fail(MOBA_ERROR_UNSUPPORTED,
+                "topk %d: at most %d unless topk >= the block count of the longest sequence (%lld)",
+                k, kMaxHistPick + 1, (long long)maxblk);
+  return MOBA_SUCCESS;
+}
+
+// Table region: blk_first[S+1], a copy of cu_seqlens[S+1], then (16-byte
+// aligned) blk_info[NBb].
+size_t cu_copy_offset(int S) { return sizeof(int32_t) * (S + 1); }
+size_t info_offset(int S) { return (2 * sizeof(int32_t) * (S + 1) + 15) / 16 * 16; }
+size_t table_bytes(int S, int64_t NBb) { return info_offset(S) + 16 * (size_t)NBb; }
+
+int largest_divisor_at_most(int n, int cap) {
+  for (int d = std::min(n, cap); d >= 1; --d)
+    if (n % d == 0) return d;
+  return 1;
+}
+
+moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_req,
+                        moba_layout_t *L) {
+  moba_status_t st = check_moba_args(sh, B, k);
+  if (st != MOBA_SUCCESS) return st;
+  if (!L) return fail(MOBA_ERROR_INVALID_VALUE, "layout is NULL");
+  const int64_t T = sh->total_tokens;
+  const int S = sh->num_seqs, Hq = sh->num_q_heads, Hkv = sh->num_kv_heads, G = Hq / Hkv;
+  const size_t es = sh->dtype == MOBA_DTYPE_BF16 ? 2 : 4;
+  const int64_t maxlen = sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, T) : T;
+  const int64_t maxblk = std::max<int64_t>(1, ceil_div(maxlen, B));
+  if (maxblk > kLdsBins)
+    return fail(MOBA_ERROR_UNSUPPORTED, "a sequence may have %lld blocks; at most %d supported",
+                (long long)maxblk, kLdsBins);
+  int P = P_req <= 0 ? Hkv : std::min(P_req, Hkv);
+  P = largest_divisor_at_most(Hkv, P);
+  while (P > 1 && (int64_t)P * maxblk > kLdsBins) P = largest_divisor_at_most(Hkv, P - 1);
+  const int Hp = P * G;
+  const int64_t NBb = ceil_div(T, B) + S;
+  const int64_t nbins = (int64_t)P * NBb;
+  const int64_t hist_items = T * Hp * (k - 1);
+  const int64_t max_tiles = ceil_div(hist_items, kRowTile) + nbins;
+  const int64_t slots = T * Hp * k;
+
+  *L = moba_layout_t{};
+  L->num_blocks_bound = NBb;
+  L->padded_tokens = ceil_div(T, kKeyTile) * kKeyTile;
+  L->kv_heads_per_pass = P;
+  L->q_heads_per_pass = Hp;
+  L->max_blocks_per_seq = (int32_t)maxblk;
+  size_t off = 0;
+  L->table_offset = off;     off = align_up(off + table_bytes(S, NBb));
+  L->kbar_offset = off;      off = align_up(off + sizeof(float) * (size_t)NBb * Hkv * kHeadDim);
+  L->vt_offset = off;        off = align_up(off + es * (size_t)P * NBb * kHeadDim * B);
+  L->idx_offset = off;       off = align_up(off + sizeof(int32_t) * (size_t)slots);
+  L->bins_offset = off;      off = align_up(off + sizeof(uint32_t) * (size_t)(4 * nbins + 2 + max_tiles));
+  L->items_offset = off;     off = align_up(off + sizeof(uint32_t) * (size_t)std::max<int64_t>(1, hist_items));
+  L->part_o_offset = off;    off = align_up(off + sizeof(float) * (size_t)slots * kHeadDim);
+  L->part_lse_offset = off;  off = align_up(off + sizeof(float) * (size_t)slots);
+  L->total_bytes = off;
+  return MOBA_SUCCESS;
+}
+
+Problem make_problem(const moba_shape_t *sh, int32_t B, int32_t k, float scale,
+                     const moba_layout_t *L) {
+  Problem pb{};
+  pb.T = sh->total_tokens;
+  pb.S = sh->num_seqs;
+  pb.maxlen = (int)(sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, pb.T) : pb.T);
+  pb.Hq = sh->num_q_heads;
+  pb.Hkv = sh->num_kv_heads;
+  pb.G = pb.Hq / pb.Hkv;
+  pb.bf16 = sh->dtype == MOBA_DTYPE_BF16;
+  pb.B = B;
+  pb.k = k;
+  pb.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)kHeadDim);
+  pb.NBb = L->num_blocks_bound;
+  pb.P = L->kv_heads_per_pass;
+  pb.Hp = L->q_heads_per_pass;
+  pb.maxblk = L->max_blocks_per_seq;
+  return pb;
+}
+
+Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
+  char *b = (char *)ws;
+  Work w{};
+  w.blk_first = (int32_t *)(b + L->table_offset);
+  w.cu = (int32_t *)(b + L->table_offset + cu_copy_offset(pb.S));
+  w.blk_info = (int4 *)(b + L->table_offset + info_offset(pb.S));
+  w.kbar = (float *)(b + L->kbar_offset);
+  w.vt = b + L->vt_offset;
+  w.idx = (int32_t *)(b + L->idx_offset);
+  const int64_t nbins = (int64_t)pb.P * pb.NBb;
+  uint32_t *bins = (uint32_t *)(b + L->bins_offset);
+  w.bin_count = bins;
+  w.bin_off = bins + nbins;
+  w.tile_off = bins + 2 * nbins + 1;
+  w.cursor = bins + 3 * nbins + 2;
+  w.tile_bin = bins + 4 * nbins + 2;
+  w.items = (uint32_t *)(b + L->items_offset);
+  w.part_o = (float *)(b + L->part_o_offset);
+  w.part_lse = (float *)(b + L->part_lse_offset);
+  w.max_tiles = ceil_div(pb.T * pb.Hp * (pb.k - 1), kRowTile) + nbins;
+  return w;
+}
+
+// Shared checks of the stage entry points: the layout must be the plan of
+// these arguments (same pass size) and the workspace non-NULL.
+moba_status_t check_stage(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L,
+                          void *ws, moba_layout_t *fresh) {
+  if (!L) return fail(MOBA_ERROR_INVALID_VALUE, "layout is NULL");
+  moba_status_t st = plan_impl(sh, B, k, L->kv_heads_per_pass, fresh);
+  if (st != MOBA_SUCCESS) return st;
+  if (fresh->total_bytes != L->total_bytes || fresh->kv_heads_per_pass != L->kv_heads_per_pass)
+    return fail(MOBA_ERROR_INVALID_VALUE, "layout does not match shape/block_size/topk");
+  if (!ws && sh->total_tokens > 0) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t check_pass(const moba_shape_t *sh, const moba_layout_t *L, int32_t g0) {
+  if (g0 < 0 || g0 >= sh->num_kv_heads || g0 % L->kv_heads_per_pass != 0)
+    return fail(MOBA_ERROR_INVALID_VALUE, "kv_head_begin %d must be a multiple of %d below %d", g0,
+                L->kv_heads_per_pass, sh->num_kv_heads);
+  return MOBA_SUCCESS;
+}
+
+moba_status_t run_pass(const Problem &pb, const Work &w, const void *q, const void *k,
+                       const void *v, int g0, void *out, float *lse, hipStream_t s) {
+  MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
+  MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
+  MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+           "vtrans");
+  MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
+  MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
+  MOBA_HIP(launch_merge(pb, w, g0, out, lse, s), "merge");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t check_io(const void *q, const void *k, const void *v, const int32_t *cu,
+                       const void *out, const moba_shape_t *sh) {
+  if (sh->total_tokens > 0 && (!q || !k || !v || !out))
+    return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v and out must be non-NULL");
+  if (sh->num_seqs > 0 && !cu) return fail(MOBA_ERROR_INVALID_VALUE, "cu_seqlens is NULL");
+  return MOBA_SUCCESS;
+}
+
+// Table-only stages (seqtable, meanpool) accept a layout planned with any
+// topk: only the block bound and the table/kbar offsets are used.
+moba_status_t check_table_stage(const moba_shape_t *sh, int32_t B, const moba_layout_t *L,
+                                const void *ws) {
+  moba_status_t st = check_shape(sh);
+  if (st != MOBA_SUCCESS) return st;
+  if (B < 1) return fail(MOBA_ERROR_INVALID_VALUE, "block_size must be >= 1");
+  if (B % kKeyTile) return fail(MOBA_ERROR_UNSUPPORTED, "block_size %d: must be a multiple of %d", B, kKeyTile);
+  if (!L) return fail(MOBA_ERROR_INVALID_VALUE, "layout is NULL");
+  if (L->num_blocks_bound != ceil_div(sh->total_tokens, B) + sh->num_seqs)
+    return fail(MOBA_ERROR_INVALID_VALUE, "layout does not match shape/block_size");
+  if (!ws && sh->total_tokens > 0) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
+  return MOBA_SUCCESS;
+}
+
+size_t dense_table_bytes(const moba_shape_t *sh) {
+  const int64_t NB64 = ceil_div(sh->total_tokens, kKeyTile) + sh->num_seqs;
+  return align_up(table_bytes(sh->num_seqs, NB64));
+}
+
+size_t dense_ws_bytes(const moba_shape_t *sh) {
+  const int64_t NB64 = ceil_div(sh->total_tokens, kKeyTile) + sh->num_seqs;
+  const size_t es = sh->dtype == MOBA_DTYPE_BF16 ? 2 : 4;
+  return dense_table_bytes(sh) +
+         align_up(es * (size_t)sh->num_kv_heads * NB64 * kHeadDim * kKeyTile);
+}
+
+size_t workspace_limit_bytes() {
+  double gib = 48.0;
+  if (const char *e = getenv("MOBA_WORKSPACE_LIMIT_GIB")) {
+    double v = atof(e);
+    if (v > 0) gib = v;
+  }
+  return (size_t)(gib * (double)(size_t(1) << 30));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moba_status_string(moba_status_t s) {
+  switch (s) {
+    case MOBA_SUCCESS: return "MOBA_SUCCESS";
+    case MOBA_ERROR_INVALID_VALUE: return "MOBA_ERROR_INVALID_VALUE";
+    case MOBA_ERROR_UNSUPPORTED: return "MOBA_ERROR_UNSUPPORTED";
+    case MOBA_ERROR_WORKSPACE_TOO_SMALL: return "MOBA_ERROR_WORKSPACE_TOO_SMALL";
+    case MOBA_ERROR_HIP: return "MOBA_ERROR_HIP";
+  }
+  return "MOBA_ERROR_UNKNOWN";
+}
+
+const char *moba_last_error(void) { return g_last_error.c_str(); }
+
+moba_status_t moba_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                        int32_t kv_heads_per_pass, moba_layout_t *layout) {
+  return plan_impl(shape, block_size, topk, kv_heads_per_pass, layout);
+}
+
+size_t moba_fwd_workspace_size(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                               int32_t kv_heads_per_pass) {
+  moba_layout_t L;
+  if (plan_impl(shape, block_size, topk, kv_heads_per_pass, &L) != MOBA_SUCCESS) return 0;
+  return L.total_bytes;
+}
+
+moba_status_t moba_seqtable(const int32_t *cu, const moba_shape_t *sh, int32_t B,
+                            const moba_layout_t *L, void *ws, hipStream_t s) {
+  moba_status_t st = check_table_stage(sh, B, L, ws);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->num_seqs > 0 && !cu) return fail(MOBA_ERROR_INVALID_VALUE, "cu_seqlens is NULL");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  char *b = (char *)ws + L->table_offset;
+  MOBA_HIP(launch_seqtable(cu, sh->num_seqs, B, L->num_blocks_bound, (int32_t *)b,
+                           (int32_t *)(b + cu_copy_offset(sh->num_seqs)),
+                           (int4 *)(b + info_offset(sh->num_seqs)), s),
+           "seqtable");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_meanpool(const void *k, const moba_shape_t *sh, int32_t B,
+                            const moba_layout_t *L, void *ws, hipStream_t s) {
+  moba_status_t st = check_table_stage(sh, B, L, ws);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if (!k) return fail(MOBA_ERROR_INVALID_VALUE, "k is NULL");
+  Problem pb = make_problem(sh, B, 1, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_gate(const void *q, const moba_shape_t *sh, int32_t B, int32_t k,
+                        const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q) return fail(MOBA_ERROR_INVALID_VALUE, "q is NULL");
+  Problem pb = make_problem(sh, B, k, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_dispatch(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L,
+                            void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  Problem pb = make_problem(sh, B, k, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_fwd(const void *q, const void *k, const void *v, const moba_shape_t *sh,
+                            int32_t B, int32_t topk, float scale, const moba_layout_t *L,
+                            void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q || !k || !v) return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v must be non-NULL");
+  Problem pb = make_problem(sh, B, topk, scale, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+           "vtrans");
+  MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
+  MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_fwd_diag(const void *q, const void *k, const void *v,
+                                 const moba_shape_t *sh, int32_t B, int32_t topk, float scale,
+                                 const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q || !k || !v) return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v must be non-NULL");
+  Problem pb = make_problem(sh, B, topk, scale, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+           "vtrans");
+  MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_fwd_hist(const void *q, const void *k, const moba_shape_t *sh, int32_t B,
+                                 int32_t topk, float scale, const moba_layout_t *L, void *ws,
+                                 int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q || !k) return fail(MOBA_ERROR_INVALID_VALUE, "q and k must be non-NULL");
+  Problem pb = make_problem(sh, B, topk, scale, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_merge(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L,
+                         void *ws, int32_t g0, void *out, float *lse, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!out) return fail(MOBA_ERROR_INVALID_VALUE, "out is NULL");
+  Problem pb = make_problem(sh, B, k, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_merge(pb, w, g0, out, lse, s), "merge");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int32_t *cu,
+                          const moba_shape_t *sh, int32_t B, int32_t topk, float scale,
+                          void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+  moba_status_t st = check_moba_args(sh, B, topk);
+  if (st != MOBA_SUCCESS) return st;
+  if ((st = check_io(q, k, v, cu, out, sh)) != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  moba_layout_t L;
+  if ((st = plan_impl(sh, B, topk, sh->num_kv_heads, &L)) != MOBA_SUCCESS) return st;
+  // largest pass (a divisor of Hkv) whose workspace fits
+  while (L.total_bytes > ws_bytes && L.kv_heads_per_pass > 1) {
+    if ((st = plan_impl(sh, B, topk, L.kv_heads_per_pass - 1, &L)) != MOBA_SUCCESS) return st;
+  }
+  if (L.total_bytes > ws_bytes)
+    return fail(MOBA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes; need at least %zu",
+                ws_bytes, L.total_bytes);
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if (!ws) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
+  Problem pb = make_problem(sh, B, topk, scale, &L);
+  Work w = carve(pb, &L, ws);
+  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
+  MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
+  for (int g0 = 0; g0 < pb.Hkv; g0 += pb.P)
+    if ((st = run_pass(pb, w, q, k, v, g0, out, lse, s)) != MOBA_SUCCESS) return st;
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_t *cu,
+                       const moba_shape_t *sh, int32_t B, int32_t topk, void *out, float *lse,
+                       hipStream_t s) {
+  moba_status_t st = check_moba_args(sh, B, topk);
+  if (st != MOBA_SUCCESS) return st;
+  if ((st = check_io(q, k, v, cu, out, sh)) != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  const size_t cap = workspace_limit_bytes();
+  moba_layout_t L;
+  if ((st = plan_impl(sh, B, topk, sh->num_kv_heads, &L)) != MOBA_SUCCESS) return st;
+  while (L.total_bytes > cap && L.kv_heads_per_pass > 1)
+    if ((st = plan_impl(sh, B, topk, L.kv_heads_per_pass - 1, &L)) != MOBA_SUCCESS) return st;
+  void *ws = nullptr;
+  MOBA_HIP(hipMallocAsync(&ws, L.total_bytes, s), "hipMallocAsync");
+  st = moba_fwd_ex(q, k, v, cu, sh, B, topk, 0.f, out, lse, ws, L.total_bytes, s);
+  hipError_t e = hipFreeAsync(ws, s);
+  if (st != MOBA_SUCCESS) return st;
+  if (e != hipSuccess) return hip_fail(e, "hipFreeAsync");
+  return MOBA_SUCCESS;
+}
+
+size_t moba_dense_causal_workspace_size(const moba_shape_t *sh) {
+  if (check_shape(sh) != MOBA_SUCCESS) return 0;
+  return dense_ws_bytes(sh);
+}
+
+moba_status_t moba_dense_causal_fwd(const void *q, const void *k, const void *v, const int32_t *cu,
+                                    const moba_shape_t *sh, float scale, void *out, float *lse,
+                                    void *ws, size_t ws_bytes, hipStream_t s) {
+  moba_status_t st = check_shape(sh);
+  if (st != MOBA_SUCCESS) return st;
+  if ((st = check_io(q, k, v, cu, out, sh)) != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  const size_t need = dense_ws_bytes(sh);
+  if (ws && ws_bytes < need)
+    return fail(MOBA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes; need %zu", ws_bytes, need);
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  bool own = false;
+  if (!ws) {
+    MOBA_HIP(hipMallocAsync(&ws, need, s), "hipMallocAsync");
+    own = true;
+  }
+  const int S = sh->num_seqs;
+  const int64_t T = sh->total_tokens;
+  const int64_t NB64 = ceil_div(T, kKeyTile) + S;
+  const int bf16 = sh->dtype == MOBA_DTYPE_BF16;
+  const int maxlen = (int)(sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, T) : T);
+  char *b = (char *)ws;
+  int32_t *first = (int32_t *)b;
+  int4 *info = (int4 *)(b + info_offset(S));
+  void *vt = b + dense_table_bytes(sh);
+  hipError_t e = launch_seqtable(cu, S, kKeyTile, NB64, first, (int32_t *)(b + cu_copy_offset(S)),
+                                 info, s);
+  if (e == hipSuccess)
+    e = launch_vtrans(v, bf16, T, sh->num_kv_heads, 0, sh->num_kv_heads, NB64, kKeyTile, info, vt, s);
+  if (e == hipSuccess)
+    e = launch_dense(q, k, vt, cu, first, bf16, T, S, maxlen, sh->num_q_heads, sh->num_kv_heads,
+                     NB64, scale > 0.f ? scale : 1.0f / sqrtf((float)kHeadDim), out, lse, s);
+  if (own) {
+    hipError_t e2 = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) return hip_fail(e, "dense_causal");
+  return MOBA_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,310 @@
+// Memory-bound stages: block table, mean-pooled keys, value transpose, and
+// the log-sum-exp merge of partial outputs.
+#include <math.h>
+
+#include "moba_internal.h"
+
+namespace moba {
+namespace {
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, uint32_t value, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+// Inclusive scan of one value per thread over a 1024-thread workgroup.
+__device__ int block_scan_incl_1024(int x, int *wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int v = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int y = __shfl_up(v, o);
+      if (lane >= o) v += y;
+    }
+    if (lane < 16) wsum[lane] = v;
+  }
+  __syncthreads();
+  int r = x + (w > 0 ? wsum[w - 1] : 0);
+  __syncthreads();
+  return r;
+}
+
+// blk_first[s] = sum over earlier sequences of ceil(L/B) ("Context
+// Partitioning" of the MoBA summary page, section 3.4: blocks restart in every
+// sequence, the last one may be short). One workgroup of 1024 threads.
+// Also keeps a copy of cu_seqlens next to the table for later stages.
+__global__ __launch_bounds__(1024) void seqtable_scan_kernel(const int32_t *cu, int S, int B,
+                                                             int32_t *blk_first,
+                                                             int32_t *cu_copy) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < S; base += 1024) {
+    int s = base + threadIdx.x;
+    int v = 0;
+    if (s < S) v = (cu[s + 1] - cu[s] + B - 1) / B;
+    if (s <= S) cu_copy[s] = cu[s];
+    int incl = block_scan_incl_1024(v, wsum) + carry;
+    if (s < S) blk_first[s] = incl - v;
+    __syncthreads();
+    if (threadIdx.x == 1023) carry = incl;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    blk_first[S] = carry;
+    cu_copy[S] = cu[S];
+  }
+}
+
+// blk_info[gb] = {sequence, first row, rows, local block index}; -1 past the end.
+__global__ __launch_bounds__(256) void seqtable_fill_kernel(const int32_t *cu,
+                                                            const int32_t *blk_first, int S,
+                                                            int B, int64_t NBb, int4 *info) {
+  int64_t gb = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gb >= NBb) return;
+  if (gb >= blk_first[S]) {
+    info[gb] = make_int4(-1, 0, 0, 0);
+    return;
+  }
+  int lo = 0, hi = S - 1;  // largest s with blk_first[s] <= gb (skips empty sequences)
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (blk_first[mid] <= gb) lo = mid; else hi = mid - 1;
+  }
+  int j = (int)(gb - blk_first[lo]);
+  int len = cu[lo + 1] - cu[lo];
+  int rows = min(B, len - j * B);
+  info[gb] = make_int4(lo, cu[lo] + j * B, rows, j);
+}
+
+template <typename T> struct Vec16;
+template <> struct Vec16<__bf16> {
+  static constexpr int N = 8;
+  __device__ static void load(const __bf16 *p, float *f) {
+    uint4 u = *(const uint4 *)p;
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float *p, float *f) {
+    float4 u = *(const float4 *)p;
+    f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+  }
+};
+
+// kbar[gb][g][:] = mean of the block's key rows ("Affinity Scoring", section
+// 3.4 of the MoBA summary page; step 1 of its implementation). One workgroup
+// per (block, kv head): 16 row groups x 16 column threads, fp64 accumulation so
+// the stored fp32 mean is the correctly rounded block mean up to one rounding.
+template <typename T>
+__global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
+                                                       const int4 *__restrict__ info, int Hkv,
+                                                       float *__restrict__ kbar) {
+  constexpr int N = Vec16<T>::N;        // elements per 16-byte load
+  constexpr int COLS = kHeadDim / N;    // threads per row: 16 (bf16) or 32 (fp32)
+  constexpr int RG = 256 / COLS;        // row groups
+  const int gb = blockIdx.x, g = blockIdx.y;
+  const int4 bi = info[gb];
+  if (bi.x < 0) return;
+  const int col = threadIdx.x % COLS, rg = threadIdx.x / COLS;
+  double acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.0;
+  const int64_t stride = (int64_t)Hkv * kHeadDim;
+  const T *base = k + ((int64_t)bi.y * Hkv + g) * kHeadDim + col * N;
+  int r = rg;
+  for (; r + 3 * RG < bi.z; r += 4 * RG) {
+    float f[4][N];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Vec16<T>::load(base + (int64_t)(r + u * RG) * stride, f[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += (double)f[u][i];
+  }
+  for (; r < bi.z; r += RG) {
+    float f[N];
+    Vec16<T>::load(base + (int64_t)r * stride, f);
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] += (double)f[i];
+  }
+  __shared__ double red[RG][kHeadDim];
+#pragma unroll
+  for (int i = 0; i < N; ++i) red[rg][col * N + i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) s += red[i][threadIdx.x];
+    kbar[((int64_t)gb * Hkv + g) * kHeadDim + threadIdx.x] = (float)(s / (double)bi.z);
+  }
+}
+
+// vt[p][gb][e][j] = v[first row of gb + j][g0 + p][e], zero past the block's
+// rows: each block's values transposed so the attention kernels can feed them
+// to the matrix cores with keys along the contraction. One 64-key tile per
+// workgroup, transposed through LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void vtrans_kernel(const T *__restrict__ v, int64_t T_, int Hkv,
+                                                     int g0, int64_t NBb, int B,
+                                                     const int4 *__restrict__ info,
+                                                     T *__restrict__ vt) {
+  constexpr int N = 16 / sizeof(T);
+  constexpr int VPR = kHeadDim / N;   // 16-byte vectors per source row
+  constexpr int PITCH = kHeadDim + 2; // LDS row pitch in elements
+  const int ntile = B / kKeyTile;
+  const int64_t gb = blockIdx.x / ntile;
+  const int jt = blockIdx.x % ntile;
+  const int p = blockIdx.y;
+  const int4 bi = info[gb];
+  if (bi.x < 0) return;
+  __shared__ T tile[kKeyTile * PITCH];
+  for (int c = threadIdx.x; c < kKeyTile * VPR; c += 256) {
+    int r = c / VPR, col = c % VPR;
+    int j = jt * kKeyTile + r;
+    T tmp[N];
+    if (j < bi.z) {
+      *(uint4 *)tmp = *(const uint4 *)(v + ((int64_t)(bi.y + j) * Hkv + g0 + p) * kHeadDim + col * N);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) tmp[i] = (T)0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) tile[r * PITCH + col * N + i] = tmp[i];
+  }
+  __syncthreads();
+  constexpr int OVPR = kKeyTile / N;  // 16-byte vectors per output row
+  T *dst = vt + (((int64_t)p * NBb + gb) * kHeadDim) * B + jt * kKeyTile;
+  for (int c = threadIdx.x; c < kHeadDim * OVPR; c += 256) {
+    int e = c / OVPR, col = c % OVPR;
+    T tmp[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) tmp[i] = tile[(col * N + i) * PITCH + e];
+    *(uint4 *)(dst + (int64_t)e * B + col * N) = *(const uint4 *)tmp;
+  }
+}
+
+__device__ __forceinline__ int seq_of_row(const int32_t *cu, int S, int64_t t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename TO> __device__ __forceinline__ void store4(TO *p, float4 v);
+template <> __device__ __forceinline__ void store4<float>(float *p, float4 v) { *(float4 *)p = v; }
+template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, float4 v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 b;
+  b[0] = (__bf16)v.x; b[1] = (__bf16)v.y; b[2] = (__bf16)v.z; b[3] = (__bf16)v.w;
+  *(bf16x4 *)p = b;
+}
+
+// Log-sum-exp combination of the per-block partial outputs (step 4 of the
+// implementation in section 3.4 of the MoBA summary page: rescale each part by
+// its normaliser). Slots are combined in ascending block order.
+// 32 threads per (row, head), 4 head-dim elements each.
+template <typename TO>
+__global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part_o,
+                                                    const float *__restrict__ part_lse,
+                                                    const int32_t *__restrict__ cu, int S,
+                                                    int64_t T_, int Hq, int h0, int Hp, int B,
+                                                    int k, TO *__restrict__ out,
+                                                    float *__restrict__ lse_out) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= T_ * Hp) return;
+  const int lane = threadIdx.x & 31;
+  const int64_t t = row / Hp;
+  const int hl = (int)(row % Hp);
+  const int s = seq_of_row(cu, S, t);
+  const int c = (int)((t - cu[s]) / B);
+  const int nsel = min(k, c + 1);
+  const float *pl = part_lse + row * k;
+  float m = -INFINITY;
+  for (int i = 0; i < nsel; ++i) m = fmaxf(m, pl[i]);
+  float sum = 0.f;
+  for (int i = 0; i < nsel; ++i) sum += expf(pl[i] - m);
+  const float L = m + logf(sum);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < nsel; ++i) {
+    const float wgt = expf(pl[i] - L);
+    const float4 o = *(const float4 *)(part_o + (row * k + i) * kHeadDim + lane * 4);
+    acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
+  }
+  store4<TO>(out + (t * Hq + h0 + hl) * kHeadDim + lane * 4, acc);
+  if (lane == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = L;
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_u32_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p, value, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t NBb, int32_t *blk_first,
+                           int32_t *cu_copy, int4 *blk_info, hipStream_t s) {
+  seqtable_scan_kernel<<<1, 1024, 0, s>>>(cu, S, B, blk_first, cu_copy);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  seqtable_fill_kernel<<<dim3((unsigned)((NBb + 255) / 256)), dim3(256), 0, s>>>(cu, blk_first, S,
+                                                                                 B, NBb, blk_info);
+  return hipGetLastError();
+}
+
+hipError_t launch_meanpool(const Problem &pb, const Work &w, const void *k, hipStream_t s) {
+  dim3 grid((unsigned)pb.NBb, (unsigned)pb.Hkv);
+  if (pb.bf16)
+    meanpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, w.blk_info, pb.Hkv, w.kbar);
+  else
+    meanpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kbar);
+  return hipGetLastError();
+}
+
+hipError_t launch_vtrans(const void *v, int bf16, int64_t T, int Hkv, int g0, int P, int64_t NBb,
+                         int B, const int4 *blk_info, void *vt, hipStream_t s) {
+  dim3 grid((unsigned)(NBb * (B / kKeyTile)), (unsigned)P);
+  if (bf16)
+    vtrans_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)v, T, Hkv, g0, NBb, B, blk_info,
+                                               (__bf16 *)vt);
+  else
+    vtrans_kernel<float><<<grid, 256, 0, s>>>((const float *)v, T, Hkv, g0, NBb, B, blk_info,
+                                              (float *)vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, float *lse,
+                        hipStream_t s) {
+  const int32_t *cu = w.cu;
+  const int64_t rows = pb.T * pb.Hp;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 7) / 8));
+  const int h0 = g0 * pb.G;
+  if (pb.bf16)
+    merge_kernel<__bf16><<<grid, 256, 0, s>>>(w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
+                                              pb.Hp, pb.B, pb.k, (__bf16 *)out, lse);
+  else
+    merge_kernel<float><<<grid, 256, 0, s>>>(w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
+                                             pb.Hp, pb.B, pb.k, (float *)out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace moba

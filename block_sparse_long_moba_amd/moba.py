@@ -1,0 +1,223 @@
+"""Thin ctypes binding of libmoba.so (include/moba.h): argument marshalling only.
+
+Every step of the forward pass runs in the HIP library; this module only turns
+torch tensors (device memory) and the current HIP stream into the C ABI's
+pointers and sizes, and raises on a non-success status. There is no fallback:
+if the library is missing, loading fails with an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoba.so")
+
+DTYPE_FP32, DTYPE_BF16 = 0, 1
+STATUS = {0: "MOBA_SUCCESS", 1: "MOBA_ERROR_INVALID_VALUE", 2: "MOBA_ERROR_UNSUPPORTED",
+          3: "MOBA_ERROR_WORKSPACE_TOO_SMALL", 4: "MOBA_ERROR_HIP"}
+
+# Every entry point include/moba.h declares.
+EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_workspace_size",
+           "moba_seqtable", "moba_meanpool", "moba_gate", "moba_dispatch", "moba_attn_fwd",
+           "moba_attn_fwd_diag", "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd", "moba_dense_causal_workspace_size",
+           "moba_dense_causal_fwd"]
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS.get(status, status), message))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("total_tokens", ctypes.c_int64), ("num_seqs", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("num_blocks_bound", ctypes.c_int64), ("padded_tokens", ctypes.c_int64),
+                ("kv_heads_per_pass", ctypes.c_int32), ("q_heads_per_pass", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("table_offset", ctypes.c_size_t), ("kbar_offset", ctypes.c_size_t),
+                ("vt_offset", ctypes.c_size_t), ("idx_offset", ctypes.c_size_t),
+                ("bins_offset", ctypes.c_size_t), ("items_offset", ctypes.c_size_t),
+                ("part_o_offset", ctypes.c_size_t), ("part_lse_offset", ctypes.c_size_t),
+                ("total_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoba.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError("libmoba.so not built: run __graft_entry__.build() or "
+                          "python -m block_sparse_long_moba_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I32, I64, F, Z = (ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.c_int32,
+                                ctypes.c_int64, ctypes.c_float, ctypes.c_size_t)
+        LP = ctypes.POINTER(Layout)
+        sig = {
+            "moba_status_string": ([I32], ctypes.c_char_p),
+            "moba_last_error": ([], ctypes.c_char_p),
+            "moba_plan": ([S, I32, I32, I32, LP], I32),
+            "moba_fwd_workspace_size": ([S, I32, I32, I32], Z),
+            "moba_seqtable": ([P, S, I32, LP, P, P], I32),
+            "moba_meanpool": ([P, S, I32, LP, P, P], I32),
+            "moba_gate": ([P, S, I32, I32, LP, P, I32, P], I32),
+            "moba_dispatch": ([S, I32, I32, LP, P, I32, P], I32),
+            "moba_attn_fwd": ([P, P, P, S, I32, I32, F, LP, P, I32, P], I32),
+            "moba_attn_fwd_diag": ([P, P, P, S, I32, I32, F, LP, P, I32, P], I32),
+            "moba_attn_fwd_hist": ([P, P, S, I32, I32, F, LP, P, I32, P], I32),
+            "moba_merge": ([S, I32, I32, LP, P, I32, P, P, P], I32),
+            "moba_fwd_ex": ([P, P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
+            "moba_fwd": ([P, P, P, P, S, I32, I32, P, P, P], I32),
+            "moba_dense_causal_workspace_size": ([S], Z),
+            "moba_dense_causal_fwd": ([P, P, P, P, S, F, P, P, P, Z, P], I32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise MobaError(status, lib().moba_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_shape(total_tokens, num_seqs, num_q_heads, num_kv_heads, head_dim=128, dtype="bf16",
+               max_seqlen=0) -> Shape:
+    dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}[dtype] if isinstance(dtype, str) else int(dtype)
+    return Shape(int(total_tokens), int(num_seqs), int(max_seqlen), int(num_q_heads),
+                 int(num_kv_heads), int(head_dim), dt)
+
+
+def shape_of(q, k, cu_seqlens, max_seqlen=0) -> Shape:
+    import torch
+    T, Hq, d = q.shape
+    dt = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}[q.dtype]
+    return Shape(T, cu_seqlens.numel() - 1, int(max_seqlen), Hq, k.shape[1], d, dt)
+
+
+def moba_plan(shape: Shape, block_size: int, topk: int, kv_heads_per_pass: int = 0) -> Layout:
+    lay = Layout()
+    _check(lib().moba_plan(ctypes.byref(shape), block_size, topk, kv_heads_per_pass,
+                           ctypes.byref(lay)))
+    return lay
+
+
+def moba_fwd_workspace_size(shape: Shape, block_size: int, topk: int,
+                            kv_heads_per_pass: int = 0) -> int:
+    return lib().moba_fwd_workspace_size(ctypes.byref(shape), block_size, topk, kv_heads_per_pass)
+
+
+def moba_seqtable(cu_seqlens, shape, block_size, layout, workspace, stream=None):
+    _check(lib().moba_seqtable(_ptr(cu_seqlens), ctypes.byref(shape), block_size,
+                               ctypes.byref(layout), _ptr(workspace), _stream(stream)))
+
+
+def moba_meanpool(k, shape, block_size, layout, workspace, stream=None):
+    _check(lib().moba_meanpool(_ptr(k), ctypes.byref(shape), block_size, ctypes.byref(layout),
+                               _ptr(workspace), _stream(stream)))
+
+
+def moba_gate(q, shape, block_size, topk, layout, workspace, kv_head_begin=0, stream=None):
+    _check(lib().moba_gate(_ptr(q), ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
+                           _ptr(workspace), kv_head_begin, _stream(stream)))
+
+
+def moba_dispatch(shape, block_size, topk, layout, workspace, kv_head_begin=0, stream=None):
+    _check(lib().moba_dispatch(ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
+                               _ptr(workspace), kv_head_begin, _stream(stream)))
+
+
+def moba_attn_fwd(q, k, v, shape, block_size, topk, layout, workspace, kv_head_begin=0,
+                  softmax_scale=0.0, stream=None):
+    _check(lib().moba_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(shape), block_size, topk,
+                               softmax_scale, ctypes.byref(layout), _ptr(workspace),
+                               kv_head_begin, _stream(stream)))
+
+
+def moba_attn_fwd_diag(q, k, v, shape, block_size, topk, layout, workspace, kv_head_begin=0,
+                       softmax_scale=0.0, stream=None):
+    _check(lib().moba_attn_fwd_diag(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(shape), block_size,
+                                    topk, softmax_scale, ctypes.byref(layout), _ptr(workspace),
+                                    kv_head_begin, _stream(stream)))
+
+
+def moba_attn_fwd_hist(q, k, shape, block_size, topk, layout, workspace, kv_head_begin=0,
+                       softmax_scale=0.0, stream=None):
+    _check(lib().moba_attn_fwd_hist(_ptr(q), _ptr(k), ctypes.byref(shape), block_size, topk,
+                                    softmax_scale, ctypes.byref(layout), _ptr(workspace),
+                                    kv_head_begin, _stream(stream)))
+
+
+def moba_merge(shape, block_size, topk, layout, workspace, out, lse=None, kv_head_begin=0,
+               stream=None):
+    _check(lib().moba_merge(ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
+                            _ptr(workspace), kv_head_begin, _ptr(out), _ptr(lse),
+                            _stream(stream)))
+
+
+def _outputs(q, out, lse, want_lse=True):
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def moba_fwd(q, k, v, cu_seqlens, block_size, topk, out=None, lse=None, max_seqlen=0,
+             stream=None):
+    """MoBA forward pass; returns (out [T][Hq][d], lse [Hq][T])."""
+    out, lse = _outputs(q, out, lse)
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    _check(lib().moba_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
+                          block_size, topk, _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def moba_fwd_ex(q, k, v, cu_seqlens, block_size, topk, workspace, out=None, lse=None,
+                softmax_scale=0.0, max_seqlen=0, stream=None):
+    """MoBA forward pass with a caller-provided workspace (uint8 device tensor)."""
+    out, lse = _outputs(q, out, lse)
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    _check(lib().moba_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
+                             block_size, topk, softmax_scale, _ptr(out), _ptr(lse),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream)))
+    return out, lse
+
+
+def moba_dense_causal_workspace_size(shape: Shape) -> int:
+    return lib().moba_dense_causal_workspace_size(ctypes.byref(shape))
+
+
+def moba_dense_causal_fwd(q, k, v, cu_seqlens, out=None, lse=None, softmax_scale=0.0,
+                          workspace=None, max_seqlen=0, stream=None):
+    """Dense causal attention per sequence; returns (out, lse)."""
+    out, lse = _outputs(q, out, lse)
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moba_dense_causal_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                       ctypes.byref(sh), softmax_scale, _ptr(out), _ptr(lse),
+                                       _ptr(workspace), nbytes, _stream(stream)))
+    return out, lse

@@ -1,0 +1,240 @@
+/*
+ * moba.h -- C ABI of the MoBA (Mixture of Block Attention) forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (cited by page title and section; see the design notes for
+ * the readings taken where the pages are silent):
+ *   "MoBA: Mixture of Block Attention for Long-Context LLMs" (summary page on
+ *   paper-graph-ui.vercel.app), section 3.4:
+ *     - "Context Partitioning": every sequence is split into blocks of
+ *       block_size rows; blocks restart at each sequence boundary and the last
+ *       block of a sequence may be short;
+ *     - "Affinity Scoring": block representative = mean of the block's keys,
+ *       gate score = <q, representative> (no scaling);
+ *     - "Top-k Gating": each query head keeps its topk best blocks; the block
+ *       holding the query is always kept and counts toward topk;
+ *     - "Causality Enforcement": later blocks are never chosen (score -inf);
+ *       inside the query's own block a causal mask applies;
+ *     - "The Core MoBA Attention Equation": softmax attention over the union
+ *       of the chosen blocks;
+ *     - "Implementation: Mapping the Algorithm to Efficient GPU Kernels",
+ *       steps 1-4: pooled keys, gate, regrouping of queries by block,
+ *       per-block attention, log-sum-exp combination of the partial outputs.
+ *   The paperhub.cn review page, authors' rebuttal W1: selection is per query
+ *   head (no sharing inside a GQA group).
+ *
+ * Tensor layout ("THD", packed variable-length batch, all device memory):
+ *   q   [T][Hq][d], k and v [T][Hkv][d], out [T][Hq][d], rows contiguous, no
+ *       padding; element type given by moba_dtype_t;
+ *   lse [Hq][T] float32, natural-log log-sum-exp of the scaled logits;
+ *   cu_seqlens [S+1] int32 on the device: cu[0] = 0, non-decreasing,
+ *       cu[S] = T; sequence s owns rows [cu[s], cu[s+1]); empty sequences are
+ *       allowed.
+ *   Query head h reads kv head h / (Hq / Hkv).
+ *
+ * Ownership: the caller owns every pointer; the library never frees caller
+ * memory. Entry points that take a workspace use only that memory; moba_fwd
+ * and moba_dense_causal_fwd (with a NULL workspace) allocate stream-ordered
+ * scratch with hipMallocAsync/hipFreeAsync on the given stream.
+ *
+ * Execution: all GPU work is enqueued on `stream`; no entry point synchronises
+ * the host. Results are valid once the caller synchronises the stream. The
+ * library keeps no state between calls apart from a per-thread error message,
+ * so it may be used from several threads and streams at once (calls that
+ * share a workspace must be ordered by the caller).
+ *
+ * Errors: arguments are checked on the host before anything is launched; on
+ * an error nothing is launched, outputs are untouched, and moba_last_error()
+ * describes the problem. A failed launch returns MOBA_ERROR_HIP. Faults inside
+ * kernels surface at the caller's next synchronisation.
+ *
+ * Limits of the GPU path: head_dim == 128; block_size a positive multiple of
+ * 64; T < 2^31 and T*Hq*topk < 2^32; topk <= 33 unless topk is at least the
+ * number of blocks of the longest sequence (then every earlier block is
+ * chosen and the result is dense causal attention). Other shapes return
+ * MOBA_ERROR_UNSUPPORTED.
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moba_status {
+  MOBA_SUCCESS = 0,
+  MOBA_ERROR_INVALID_VALUE = 1,      /* bad pointer, size or layout */
+  MOBA_ERROR_UNSUPPORTED = 2,        /* valid but outside the GPU path's limits */
+  MOBA_ERROR_WORKSPACE_TOO_SMALL = 3,
+  MOBA_ERROR_HIP = 4                 /* a HIP runtime call or launch failed */
+} moba_status_t;
+
+typedef enum moba_dtype {
+  MOBA_DTYPE_FP32 = 0,
+  MOBA_DTYPE_BF16 = 1
+} moba_dtype_t;
+
+/* Shape of one call. */
+typedef struct moba_shape {
+  int64_t total_tokens;   /* T, rows of q/k/v/out */
+  int32_t num_seqs;       /* S, cu_seqlens holds S+1 entries */
+  int32_t max_seqlen;     /* host-known upper bound on any sequence length, 0 = unknown (T) */
+  int32_t num_q_heads;    /* Hq */
+  int32_t num_kv_heads;   /* Hkv, divides Hq */
+  int32_t head_dim;       /* d, 128 on the GPU path */
+  moba_dtype_t dtype;     /* element type of q, k, v and out */
+} moba_shape_t;
+
+/* Workspace plan: byte offsets of every intermediate inside one workspace.
+ * Work on the query heads is done in passes of kv_heads_per_pass kv heads
+ * (and their Hq/Hkv query heads each); per-pass buffers are reused. */
+typedef struct moba_layout {
+  int64_t num_blocks_bound;   /* NBb = ceil(T/block_size) + S >= number of blocks */
+  int64_t padded_tokens;      /* T rounded up to 64 (informational) */
+  int32_t kv_heads_per_pass;  /* P */
+  int32_t q_heads_per_pass;   /* Hp = P * Hq / Hkv */
+  int32_t max_blocks_per_seq; /* ceil(max_seqlen / block_size) */
+  int32_t reserved;
+  /* int32 blk_first[S+1] (first global block of each sequence), int32 copy
+   * of cu_seqlens[S+1], then (16-byte aligned) int32 blk_info[NBb][4] =
+   * {sequence, first row, rows, local block index} (sequence = -1 for
+   * indices past the last block). Written by moba_seqtable. */
+  size_t table_offset;
+  /* float32 kbar[NBb][Hkv][d]: mean-pooled keys of every block. */
+  size_t kbar_offset;
+  /* element type, vt[P][NBb][d][block_size]: for each kv head of the pass
+   * and each block, the block's value rows transposed (zero past its rows). */
+  size_t vt_offset;
+  /* int32 idx[T][Hp][topk]: chosen local block ids of the pass's query heads,
+   * ascending, -1 padded; the last valid entry is the query's own block. */
+  size_t idx_offset;
+  /* uint32 dispatch tables over bins b = p*NBb + global_block (p < P):
+   * count[P*NBb], offset[P*NBb+1], tile_offset[P*NBb+1] (128-row tiles),
+   * cursor[P*NBb], tile_bin[max_tiles] (bin of every tile), where
+   * max_tiles = ceil(T*Hp*(topk-1)/128) + P*NBb. */
+  size_t bins_offset;
+  /* uint32 items[T*Hp*(topk-1)]: per bin, the slots (t*Hp + hl)*topk + s that
+   * chose the bin's block as an earlier block (order inside a bin unspecified). */
+  size_t items_offset;
+  /* float32 part_o[T*Hp*topk][d] and part_lse[T*Hp*topk]: attention of slot
+   * (t, hl, s) over block idx[t][hl][s] alone (normalised), and its lse. */
+  size_t part_o_offset;
+  size_t part_lse_offset;
+  size_t total_bytes;
+} moba_layout_t;
+
+/* Name of a status code. */
+const char *moba_status_string(moba_status_t status);
+
+/* Message describing the last non-success status returned on this thread. */
+const char *moba_last_error(void);
+
+/* Host only. Checks the shape and fills *layout for a pass size of
+ * kv_heads_per_pass kv heads (0 = all of them, values are clamped to
+ * [1, Hkv]; the pass may be lowered further to fit the dispatch stage's LDS
+ * histogram, see layout->kv_heads_per_pass). */
+moba_status_t moba_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                        int32_t kv_heads_per_pass, moba_layout_t *layout);
+
+/* Bytes of workspace moba_fwd_ex needs for the given pass size (0 = all kv
+ * heads in one pass); 0 if the arguments are invalid. */
+size_t moba_fwd_workspace_size(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                               int32_t kv_heads_per_pass);
+
+/* ---- Stages of the forward pass (section 3.4 "Implementation", steps 1-4).
+ * Each works on a workspace laid out by moba_plan with the same shape,
+ * block_size and topk. moba_seqtable must run first on that workspace.
+ * kv_head_begin selects the pass: kv heads [kv_head_begin, kv_head_begin+P)
+ * (clipped to Hkv) and their query heads. */
+
+/* Block table from the device cu_seqlens ("Context Partitioning"). */
+moba_status_t moba_seqtable(const int32_t *cu_seqlens, const moba_shape_t *shape,
+                            int32_t block_size, const moba_layout_t *layout, void *workspace,
+                            hipStream_t stream);
+
+/* kbar = mean of each block's key rows, over the rows the block has
+ * ("Affinity Scoring"; step 1). Reads k, writes the kbar region. */
+moba_status_t moba_meanpool(const void *k, const moba_shape_t *shape, int32_t block_size,
+                            const moba_layout_t *layout, void *workspace, hipStream_t stream);
+
+/* Gate ("Affinity Scoring", "Top-k Gating", "Causality Enforcement"; step 1):
+ * for every row t and query head of the pass, scores <q, kbar_j> for the
+ * earlier blocks j of its sequence, keeps the topk-1 best (ties to the lower
+ * index), adds its own block and writes the idx region. Needs moba_meanpool. */
+moba_status_t moba_gate(const void *q, const moba_shape_t *shape, int32_t block_size,
+                        int32_t topk, const moba_layout_t *layout, void *workspace,
+                        int32_t kv_head_begin, hipStream_t stream);
+
+/* Regroup queries by chosen block (step 2): histogram, prefix sum and scatter
+ * of the earlier-block entries of idx into the bins and items regions. The
+ * query's own block is not dispatched (the diagonal attention covers it). */
+moba_status_t moba_dispatch(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                            const moba_layout_t *layout, void *workspace, int32_t kv_head_begin,
+                            hipStream_t stream);
+
+/* Block attention (step 3): transposes the pass's values into vt, then
+ * computes, for every (row, query head) slot, softmax attention over its own
+ * block with a causal mask and over each dispatched earlier block without
+ * one, writing part_o / part_lse. softmax_scale 0 means 1/sqrt(d). */
+moba_status_t moba_attn_fwd(const void *q, const void *k, const void *v,
+                            const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                            float softmax_scale, const moba_layout_t *layout, void *workspace,
+                            int32_t kv_head_begin, hipStream_t stream);
+
+/* The two halves of moba_attn_fwd, for callers that time or overlap them:
+ * _diag transposes the pass's values into vt and runs the own-block (causal)
+ * attention; _hist runs the earlier-block attention over the dispatched bins
+ * and needs vt from _diag of the same pass. */
+moba_status_t moba_attn_fwd_diag(const void *q, const void *k, const void *v,
+                                 const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                                 float softmax_scale, const moba_layout_t *layout,
+                                 void *workspace, int32_t kv_head_begin, hipStream_t stream);
+moba_status_t moba_attn_fwd_hist(const void *q, const void *k, const moba_shape_t *shape,
+                                 int32_t block_size, int32_t topk, float softmax_scale,
+                                 const moba_layout_t *layout, void *workspace,
+                                 int32_t kv_head_begin, hipStream_t stream);
+
+/* Log-sum-exp combination (step 4): out[t][h] = sum_s exp(lse_s - L) o_s with
+ * L = log sum_s exp(lse_s), over the valid slots in ascending block order;
+ * lse[h][t] = L (lse may be NULL). Writes the pass's heads of out and lse. */
+moba_status_t moba_merge(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                         const moba_layout_t *layout, void *workspace, int32_t kv_head_begin,
+                         void *out, float *lse, hipStream_t stream);
+
+/* ---- Whole forward pass. */
+
+/* All stages, in passes sized to fit workspace_bytes (at least
+ * moba_fwd_workspace_size(shape, block_size, topk, 1)). */
+moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v,
+                          const int32_t *cu_seqlens, const moba_shape_t *shape,
+                          int32_t block_size, int32_t topk, float softmax_scale, void *out,
+                          float *lse, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Same with softmax_scale = 1/sqrt(d) and stream-ordered scratch of at most
+ * MOBA_WORKSPACE_LIMIT_GIB GiB (environment, default 48) per call. */
+moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
+                       const moba_shape_t *shape, int32_t block_size, int32_t topk, void *out,
+                       float *lse, hipStream_t stream);
+
+/* ---- Dense causal attention on the same layout ("Standard Attention
+ * Baseline" with a causal mask, per sequence): the full-attention reference
+ * the pages compare MoBA against. workspace may be NULL (then scratch is
+ * allocated stream-ordered); otherwise it must hold
+ * moba_dense_causal_workspace_size(shape) bytes. */
+size_t moba_dense_causal_workspace_size(const moba_shape_t *shape);
+moba_status_t moba_dense_causal_fwd(const void *q, const void *k, const void *v,
+                                    const int32_t *cu_seqlens, const moba_shape_t *shape,
+                                    float softmax_scale, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H */

@@ -1,0 +1,125 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/moba.h declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_long_moba_amd import moba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moba.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moba_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = moba.lib()
+    declared = header_functions()
+    assert declared, "no declarations found"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(declared) == sorted(moba.EXPORTS), "binding and header disagree"
+
+
+def shape(T=4096, S=1, Hq=32, Hkv=8, d=128, dtype="bf16", max_seqlen=0):
+    return moba.make_shape(T, S, Hq, Hkv, d, dtype, max_seqlen)
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except moba.MobaError as e:
+        return e.status, str(e)
+    return 0, ""
+
+
+def test_plan_sizes_and_offsets_are_consistent():
+    sh = shape(T=1 << 20)
+    lay = moba.moba_plan(sh, 4096, 12, 1)
+    assert lay.kv_heads_per_pass == 1 and lay.q_heads_per_pass == 4
+    assert lay.num_blocks_bound == 256 + 1
+    offs = [lay.table_offset, lay.kbar_offset, lay.vt_offset, lay.idx_offset, lay.bins_offset,
+            lay.items_offset, lay.part_o_offset, lay.part_lse_offset, lay.total_bytes]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    slots = (1 << 20) * 4 * 12
+    assert lay.part_lse_offset - lay.part_o_offset >= slots * 128 * 4
+    assert lay.total_bytes == moba.moba_fwd_workspace_size(sh, 4096, 12, 1)
+    full = moba.moba_plan(sh, 4096, 12, 0)
+    assert full.kv_heads_per_pass == 8 and full.total_bytes > lay.total_bytes
+    # pass sizes are divisors of the kv head count
+    assert moba.moba_plan(sh, 4096, 12, 3).kv_heads_per_pass == 2
+    assert moba.moba_plan(sh, 4096, 12, 6).kv_heads_per_pass == 4
+
+
+@pytest.mark.parametrize("kw,B,k,expect", [
+    (dict(Hq=30, Hkv=8), 4096, 12, 1),       # Hq not a multiple of Hkv
+    (dict(d=64), 4096, 12, 2),               # head_dim other than 128
+    (dict(), 4000, 12, 2),                   # block size not a multiple of 64
+    (dict(), 0, 12, 1),                      # block size 0
+    (dict(), 4096, 0, 1),                    # topk 0
+    (dict(T=1 << 20), 64, 40, 2),            # topk-1 > 32 with more blocks than topk
+    (dict(T=-1), 4096, 12, 1),               # negative length
+    (dict(T=10, S=0), 4096, 12, 1),          # tokens without sequences
+    (dict(T=1 << 31), 4096, 12, 2),          # too many tokens
+    (dict(dtype=7), 4096, 12, 1),            # unknown dtype
+])
+def test_plan_rejects_bad_shapes(kw, B, k, expect):
+    st, msg = status_of(moba.moba_plan, shape(**kw), B, k)
+    assert st == expect, msg
+    assert msg
+
+
+def test_large_topk_is_fine_when_it_covers_every_block():
+    lay = moba.moba_plan(shape(T=4096, max_seqlen=4096), 64, 64)
+    assert lay.total_bytes > 0
+
+
+def test_entry_points_reject_null_arguments_without_a_device():
+    L = moba.lib()
+    sh = shape()
+    lay = moba.moba_plan(sh, 4096, 12)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    null = None
+    # moba_fwd: null q
+    assert L.moba_fwd(null, fake, fake, fake, ctypes.byref(sh), 4096, 12, fake, null, null) == 1
+    # moba_fwd: null cu_seqlens
+    assert L.moba_fwd(fake, fake, fake, null, ctypes.byref(sh), 4096, 12, fake, null, null) == 1
+    # moba_fwd_ex: workspace too small is reported before any launch
+    assert L.moba_fwd_ex(fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, 0.0, fake, null,
+                         fake, 16, null) == 3
+    assert b"workspace" in L.moba_last_error()
+    # negative softmax scale
+    assert L.moba_fwd_ex(fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, -1.0, fake, null,
+                         fake, 1 << 40, null) == 1
+    # stage entry points: mismatched layout
+    other = moba.moba_plan(shape(T=8192), 4096, 12)
+    assert L.moba_gate(fake, ctypes.byref(sh), 4096, 12, ctypes.byref(other), fake, 0, null) == 1
+    # kv_head_begin not aligned to the pass
+    lay1 = moba.moba_plan(sh, 4096, 12, 2)
+    assert L.moba_gate(fake, ctypes.byref(sh), 4096, 12, ctypes.byref(lay1), fake, 1, null) == 1
+    assert L.moba_merge(ctypes.byref(sh), 4096, 12, ctypes.byref(lay), fake, 0, null, null,
+                        null) == 1
+    # dense: bad scale / too small workspace
+    assert L.moba_dense_causal_fwd(fake, fake, fake, fake, ctypes.byref(sh), float("nan"), fake,
+                                   null, null, 0, null) == 1
+    assert L.moba_dense_causal_fwd(fake, fake, fake, fake, ctypes.byref(sh), 0.0, fake, null,
+                                   fake, 8, null) == 3
+
+
+def test_empty_problem_is_a_no_op():
+    L = moba.lib()
+    sh = shape(T=0, S=0)
+    assert L.moba_fwd(None, None, None, None, ctypes.byref(sh), 4096, 12, None, None, None) == 0
+    assert L.moba_dense_causal_fwd(None, None, None, None, ctypes.byref(sh), 0.0, None, None,
+                                   None, 0, None) == 0
+
+
+def test_status_strings():
+    L = moba.lib()
+    for code, name in moba.STATUS.items():
+        assert L.moba_status_string(code).decode() == name

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small shapes are checked on every row; the full-size workloads on sampled rows
+(every block's first and last row, random rows, every row of short blocks),
+with the same launch configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import check
+from block_sparse_long_moba_amd import moba, synth
+from block_sparse_long_moba_amd.tensors import to_device, to_host_f64, workspace_view
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moba.lib()  # the HIP library must be present; no fallback
+    yield
+    torch.cuda.synchronize()
+
+
+class Dev:
+    """Inputs on the device plus the workspace plan for one (B, topk, pass)."""
+
+    def __init__(self, inp, block_size, topk, kv_heads_per_pass=0):
+        import torch
+        self.inp, self.B, self.k = inp, block_size, topk
+        self.q, self.kk, self.v = (to_device(x) for x in (inp.q, inp.k, inp.v))
+        self.cu = to_device(inp.cu_seqlens)
+        self.shape = moba.shape_of(self.q, self.kk, self.cu)
+        self.lay = moba.moba_plan(self.shape, block_size, topk, kv_heads_per_pass)
+        self.ws = torch.empty(self.lay.total_bytes, dtype=torch.uint8, device="cuda")
+        self.dtype = inp.workload.dtype
+
+    def view(self, offset, count, dtype):
+        return workspace_view(self.ws, offset, count, dtype)
+
+
+def host_inputs(lengths, hq, hkv, dtype, B, k, seed):
+    return synth.custom(lengths, hq, hkv, 128, dtype, B, k, seed)
+
+
+def gpu_rows(out, lse, rows):
+    o = to_host_f64(out)[rows]
+    l = to_host_f64(lse).T[rows]
+    return o, l
+
+
+SMALL = [
+    # lengths,              Hq, Hkv, dtype,  B,   k, seed
+    ([1000],                 4,  2, "bf16", 128,  3, 11),  # ragged tail, several tiles
+    ([0, 300, 64, 1, 700],   8,  2, "bf16",  64,  4, 12),  # empty, short, one-row sequences
+    ([513, 2048],            8,  8, "fp32", 256,  4, 13),  # MHA, fp32 path
+    ([4096],                32,  8, "bf16", 512,  3, 14),  # 8B head shape, 8 blocks
+    ([2000],                 8,  1, "bf16", 128,  1, 15),  # topk 1: own block only
+    ([1500],                 4,  4, "bf16", 256, 16, 16),  # topk covers all blocks: dense
+    ([3000, 1000],          16,  2, "bf16", 192,  5, 17),  # block size 3*64, G = 8
+    ([777, 1234],            2,  1, "fp32",  64,  6, 18),  # fp32, G = 2, many small blocks
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "L%s_h%d_%d_%s_B%d_k%d" % (
+    "-".join(map(str, c[0])), c[1], c[2], c[3], c[4], c[5]))
+def test_moba_fwd_matches_oracle_on_every_row(case):
+    import torch
+    lengths, hq, hkv, dtype, B, k, seed = case
+    note("case %s" % (case,))
+    inp = host_inputs(lengths, hq, hkv, dtype, B, k, seed)
+    d = Dev(inp, B, k)
+    out, lse = moba.moba_fwd_ex(d.q, d.kk, d.v, d.cu, B, k, d.ws)
+    torch.cuda.synchronize()
+    T = inp.q.shape[0]
+    rows = np.arange(T)
+    kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+    # selection of the last pass's heads is still in the workspace (one pass here)
+    assert d.lay.kv_heads_per_pass == hkv
+    gidx = d.view(d.lay.idx_offset, T * hq * k, torch.int32).view(T, hq, k).cpu().numpy()
+    sel, ref_out, ref_lse, info = check.reference_for_rows(inp.q, inp.k, inp.v, inp.cu_seqlens,
+                                                           kbar, B, k, rows, gpu_sel_rows=gidx)
+    go, gl = gpu_rows(out, lse, rows)
+    stats = check.compare_outputs(go, gl, ref_out, ref_lse, dtype)
+    note("stats %s %s" % (stats, info))
+
+
+def test_stages_meanpool_gate_dispatch_partials():
+    """Each stage entry point against its oracle counterpart."""
+    import torch
+    lengths, hq, hkv, dtype, B, k = [1500, 2100], 8, 2, "bf16", 256, 4
+    inp = host_inputs(lengths, hq, hkv, dtype, B, k, 21)
+    d = Dev(inp, B, k, kv_heads_per_pass=1)
+    sh, lay = d.shape, d.lay
+    T = inp.q.shape[0]
+    moba.moba_seqtable(d.cu, sh, B, lay, d.ws)
+    moba.moba_meanpool(d.kk, sh, B, lay, d.ws)
+    torch.cuda.synchronize()
+    kbar_ref = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+    nb = kbar_ref.shape[0]
+    kbar = d.view(lay.kbar_offset, nb * hkv * 128, torch.float32).view(nb, hkv, 128).cpu().numpy()
+    err = np.abs(kbar - kbar_ref).max()
+    assert err <= 1e-6 * max(1.0, np.abs(kbar_ref).max()), err
+    # the fp32 mean is the rounded fp64 mean
+    np.testing.assert_array_equal(kbar, kbar_ref.astype(np.float32))
+
+    out = torch.empty_like(d.q)
+    lse = torch.empty((hq, T), dtype=torch.float32, device="cuda")
+    Hp = lay.q_heads_per_pass
+    G = hq // hkv
+    for g0 in range(0, hkv, lay.kv_heads_per_pass):
+        h0 = g0 * G
+        moba.moba_gate(d.q, sh, B, k, lay, d.ws, g0)
+        moba.moba_dispatch(sh, B, k, lay, d.ws, g0)
+        moba.moba_attn_fwd(d.q, d.kk, d.v, sh, B, k, lay, d.ws, g0)
+        moba.moba_merge(sh, B, k, lay, d.ws, out, lse, g0)
+        torch.cuda.synchronize()
+        gidx = d.view(lay.idx_offset, T * Hp * k, torch.int32).view(T, Hp, k).cpu().numpy()
+        sel, tie, scores = oracle.select(inp.q, kbar_ref, inp.cu_seqlens, B, k, want_scores=True)
+        check.check_selection(gidx, sel[:, h0:h0 + Hp], tie[:, h0:h0 + Hp],
+                              scores[:, h0:h0 + Hp], k)
+        # dispatch: every earlier-block slot lands exactly once, in its block's bin
+        NBb = lay.num_blocks_bound
+        nbins = lay.kv_heads_per_pass * NBb
+        bins = d.view(lay.bins_offset, 2 * nbins + 1, torch.int32).cpu().numpy().view(np.uint32)
+        count, off = bins[:nbins], bins[nbins:2 * nbins + 1]
+        assert np.all(np.diff(off.astype(np.int64)) == count)
+        n_items = int(off[-1])
+        items = d.view(lay.items_offset, max(n_items, 1), torch.int32).cpu().numpy().view(np.uint32)[:n_items]
+        first = oracle.block_first(inp.cu_seqlens, B)
+        seq_of = np.searchsorted(inp.cu_seqlens, np.arange(T), side="right") - 1
+        expect = []
+        for t in range(T):
+            for hl in range(Hp):
+                row = gidx[t, hl]
+                c = row[(row >= 0).sum() - 1]
+                for s_ in range(k):
+                    j = row[s_]
+                    if 0 <= j < c:
+                        expect.append(((hl // G) * NBb + first[seq_of[t]] + j, (t * Hp + hl) * k + s_))
+        expect.sort()
+        got = []
+        for b in range(nbins):
+            for it in items[off[b]:off[b + 1]]:
+                got.append((b, int(it)))
+        got.sort()
+        assert got == expect
+        # partial outputs of a sample of slots against single-block oracle attention
+        part_o = d.view(lay.part_o_offset, T * Hp * k * 128, torch.float32).view(T, Hp, k, 128)
+        part_l = d.view(lay.part_lse_offset, T * Hp * k, torch.float32).view(T, Hp, k)
+        rng = np.random.default_rng(5)
+        ts = rng.integers(0, T, 64)
+        po, pl = part_o[ts].cpu().numpy(), part_l[ts].cpu().numpy()
+        q_sub = np.ascontiguousarray(inp.q[:, h0:h0 + Hp])
+        k_sub = np.ascontiguousarray(inp.k[:, g0:g0 + Hp // G])
+        v_sub = np.ascontiguousarray(inp.v[:, g0:g0 + Hp // G])
+        for s_ in range(k):
+            one = np.full((len(ts), Hp, k), -1, np.int32)
+            one[:, :, 0] = gidx[ts, :, s_]
+            valid = one[:, :, 0] >= 0
+            one[~valid, 0] = gidx[ts, :, 0][~valid]  # placeholder, ignored below
+            ro, rl = oracle.attend(q_sub, k_sub, v_sub, inp.cu_seqlens, B, k, one, rows=ts)
+            assert np.abs(po[:, :, s_][valid] - ro[valid]).max(initial=0) < 2e-2
+            assert np.abs(pl[:, :, s_][valid] - rl[valid]).max(initial=0) < 1e-3
+    # staged run == one-call run, bit for bit
+    out2, lse2 = moba.moba_fwd_ex(d.q, d.kk, d.v, d.cu, B, k, d.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_pass_size_and_determinism():
+    import torch
+    inp = host_inputs([3000, 1100], 16, 4, "bf16", 256, 4, 31)
+    d_all = Dev(inp, 256, 4)
+    d_one = Dev(inp, 256, 4, kv_heads_per_pass=1)
+    a = moba.moba_fwd_ex(d_all.q, d_all.kk, d_all.v, d_all.cu, 256, 4, d_all.ws)
+    b = moba.moba_fwd_ex(d_one.q, d_one.kk, d_one.v, d_one.cu, 256, 4, d_one.ws)
+    c = moba.moba_fwd_ex(d_all.q, d_all.kk, d_all.v, d_all.cu, 256, 4, d_all.ws)
+    e = moba.moba_fwd(d_all.q, d_all.kk, d_all.v, d_all.cu, 256, 4)
+    torch.cuda.synchronize()
+    for x in (b, c, e):
+        assert torch.equal(a[0], x[0]) and torch.equal(a[1], x[1])
+
+
+@pytest.mark.parametrize("case", [
+    ([1000, 300], 8, 2, "bf16", 21), ([513], 4, 4, "fp32", 22), ([0, 2049, 64], 8, 1, "bf16", 23)])
+def test_dense_causal_matches_oracle(case):
+    import torch
+    lengths, hq, hkv, dtype, seed = case
+    inp = host_inputs(lengths, hq, hkv, dtype, 64, 1, seed)
+    q, k, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    out, lse = moba.moba_dense_causal_fwd(q, k, v, cu)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.dense_causal(inp.q, inp.k, inp.v, inp.cu_seqlens)
+    rows = np.arange(inp.q.shape[0])
+    go, gl = gpu_rows(out, lse, rows)
+    check.compare_outputs(go, gl, ref_out, ref_lse, dtype)
+
+
+def test_moba_with_topk_covering_all_blocks_equals_dense_kernel():
+    import torch
+    inp = host_inputs([2048, 1000], 8, 2, "bf16", 256, 8, 41)
+    q, k, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    a_out, a_lse = moba.moba_fwd(q, k, v, cu, 256, 8)
+    b_out, b_lse = moba.moba_dense_causal_fwd(q, k, v, cu)
+    torch.cuda.synchronize()
+    assert (a_out.float() - b_out.float()).abs().max().item() < 2e-2
+    assert (a_lse - b_lse).abs().max().item() < 1e-3
+
+
+# --------------------------------------------------------------- full size
+
+def staged_run(d, rows, heads_cb=None):
+    """The bench's launch sequence (moba_fwd_ex's stage order) through the
+    stage entry points, collecting the selection of `rows` after each gate."""
+    import torch
+    sh, lay, B, k = d.shape, d.lay, d.B, d.k
+    T, Hq = d.q.shape[0], d.q.shape[1]
+    out = torch.empty_like(d.q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    moba.moba_seqtable(d.cu, sh, B, lay, d.ws)
+    moba.moba_meanpool(d.kk, sh, B, lay, d.ws)
+    Hp, P = lay.q_heads_per_pass, lay.kv_heads_per_pass
+    sel = np.zeros((len(rows), Hq, k), np.int32)
+    rows_t = torch.from_numpy(rows).cuda()
+    for g0 in range(0, sh.num_kv_heads, P):
+        moba.moba_gate(d.q, sh, B, k, lay, d.ws, g0)
+        idx = d.view(lay.idx_offset, T * Hp * k, torch.int32).view(T, Hp, k)
+        h0 = g0 * Hq // sh.num_kv_heads
+        sel[:, h0:h0 + Hp] = idx.index_select(0, rows_t).cpu().numpy()
+        moba.moba_dispatch(sh, B, k, lay, d.ws, g0)
+        moba.moba_attn_fwd(d.q, d.kk, d.v, sh, B, k, lay, d.ws, g0)
+        moba.moba_merge(sh, B, k, lay, d.ws, out, lse, g0)
+    torch.cuda.synchronize()
+    return out, lse, sel
+
+
+FULL = list(synth.WORKLOADS)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_sampled_rows(name):
+    import torch
+    w = synth.WORKLOADS[name]
+    note("workload %s: generating inputs" % name)
+    inp = synth.generate(w)
+    T = w.total_tokens
+    # the benchmark's pass size: the largest that fits 48 GiB of workspace
+    P = w.num_kv_heads
+    while P > 1 and moba.moba_fwd_workspace_size(moba.make_shape(
+            T, len(w.lengths), w.num_q_heads, w.num_kv_heads, 128, w.dtype), w.block_size,
+            w.topk, P) > (48 << 30):
+        P //= 2
+    d = Dev(inp, w.block_size, w.topk, kv_heads_per_pass=P)
+    per_block = 64 if T <= 4096 else (6 if T >= (1 << 20) else 8)
+    rows = (np.arange(T) if T <= 4096 else
+            check.sample_rows(w.cu_seqlens(), w.block_size, per_block, w.seed))
+    note("workload %s: GPU run, pass of %d kv heads, %d sampled rows" % (name, P, len(rows)))
+    out, lse, gsel = staged_run(d, rows)
+    # one-call path, same launch configuration: identical bits
+    out2, lse2 = moba.moba_fwd_ex(d.q, d.kk, d.v, d.cu, w.block_size, w.topk, d.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # pooled keys of every block
+    kbar_ref = oracle.meanpool(inp.k, inp.cu_seqlens, w.block_size)
+    nb = kbar_ref.shape[0]
+    kbar = d.view(d.lay.kbar_offset, nb * w.num_kv_heads * 128, torch.float32).view(
+        nb, w.num_kv_heads, 128).cpu().numpy()
+    np.testing.assert_array_equal(kbar, kbar_ref.astype(np.float32))
+    note("workload %s: oracle on sampled rows" % name)
+    go, gl = gpu_rows(out, lse, rows)
+    sel, ref_out, ref_lse, info = check.reference_for_rows(
+        inp.q, inp.k, inp.v, inp.cu_seqlens, kbar_ref, w.block_size, w.topk, rows,
+        gpu_sel_rows=gsel)
+    stats = check.compare_outputs(go, gl, ref_out, ref_lse, w.dtype)
+    note("workload %s: %s %s" % (name, stats, info))
