@@ -83,16 +83,28 @@ def compare_outputs(gpu_out, gpu_lse, ref_out, ref_lse, dtype):
     return stats
 
 
-def reference_for_rows(q, k, v, cu, kbar, block_size, topk, rows, gpu_sel_rows=None, scale=None):
-    """Oracle selection (with near-tie flags and scores) and outputs for `rows`.
-    If the GPU's selection for those rows is given, near-tie rows where it
-    differs are recomputed over the GPU's selection."""
+def reference_for_rows(q, k, v, cu, kbar, block_size, topk, rows, gpu_sel_rows=None, scale=None,
+                       out_rows=None):
+    """Oracle selection (with near-tie flags and scores) for `rows`, and oracle
+    outputs for `out_rows` (a subset of `rows`; default all of them). If the
+    GPU's selection for `rows` is given it is checked, and near-tie rows where
+    it differs get their reference output over the GPU's selection.
+    Returns (sel, out, lse, info, out_index) with out_index the positions of
+    the output rows inside `rows`."""
+    rows = np.asarray(rows, dtype=np.int64)
     sel, tie, scores = select(q, kbar, cu, block_size, topk, rows=rows, want_scores=True)
-    info = dict(near_ties=int(tie.sum()), differing=0)
+    info = dict(rows_checked=int(len(rows)), near_ties=int(tie.sum()), differing=0)
     use = sel
     if gpu_sel_rows is not None:
         differs, _ = check_selection(gpu_sel_rows, sel, tie, scores, topk)
         info["differing"] = int(differs.sum())
         use = np.where(differs[..., None], gpu_sel_rows, sel)
-    out, lse = attend(q, k, v, cu, block_size, topk, use, scale=scale, rows=rows)
-    return sel, out, lse, info
+    if out_rows is None:
+        out_index = np.arange(len(rows))
+    else:
+        out_index = np.searchsorted(rows, np.asarray(out_rows, dtype=np.int64))
+        assert np.all(rows[out_index] == out_rows), "out_rows must be a subset of rows"
+    out, lse = attend(q, k, v, cu, block_size, topk, np.ascontiguousarray(use[out_index]),
+                      scale=scale, rows=rows[out_index])
+    info["output_rows"] = int(len(out_index))
+    return sel, out, lse, info, out_index

@@ -87,8 +87,8 @@ def test_moba_fwd_matches_oracle_on_every_row(case):
     # selection of the last pass's heads is still in the workspace (one pass here)
     assert d.lay.kv_heads_per_pass == hkv
     gidx = d.view(d.lay.idx_offset, T * hq * k, torch.int32).view(T, hq, k).cpu().numpy()
-    sel, ref_out, ref_lse, info = check.reference_for_rows(inp.q, inp.k, inp.v, inp.cu_seqlens,
-                                                           kbar, B, k, rows, gpu_sel_rows=gidx)
+    sel, ref_out, ref_lse, info, _ = check.reference_for_rows(
+        inp.q, inp.k, inp.v, inp.cu_seqlens, kbar, B, k, rows, gpu_sel_rows=gidx)
     go, gl = gpu_rows(out, lse, rows)
     stats = check.compare_outputs(go, gl, ref_out, ref_lse, dtype)
     note("stats %s %s" % (stats, info))
@@ -110,8 +110,8 @@ def test_stages_meanpool_gate_dispatch_partials():
     kbar = d.view(lay.kbar_offset, nb * hkv * 128, torch.float32).view(nb, hkv, 128).cpu().numpy()
     err = np.abs(kbar - kbar_ref).max()
     assert err <= 1e-6 * max(1.0, np.abs(kbar_ref).max()), err
-    # the fp32 mean is the rounded fp64 mean
-    np.testing.assert_array_equal(kbar, kbar_ref.astype(np.float32))
+    # the fp32 mean is the fp64 mean rounded once (up to fp64 summation order)
+    assert np.all(np.abs(kbar - kbar_ref) <= 2.0 ** -23 * np.abs(kbar_ref) + 1e-12)
 
     out = torch.empty_like(d.q)
     lse = torch.empty((hq, T), dtype=torch.float32, device="cuda")
@@ -244,7 +244,7 @@ def staged_run(d, rows, heads_cb=None):
     return out, lse, sel
 
 
-FULL = list(synth.WORKLOADS)
+FULL = sorted(synth.WORKLOADS, key=lambda n: synth.WORKLOADS[n].total_tokens)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -261,10 +261,19 @@ def test_full_workload_sampled_rows(name):
             w.topk, P) > (48 << 30):
         P //= 2
     d = Dev(inp, w.block_size, w.topk, kv_heads_per_pass=P)
-    per_block = 64 if T <= 4096 else (6 if T >= (1 << 20) else 8)
-    rows = (np.arange(T) if T <= 4096 else
-            check.sample_rows(w.cu_seqlens(), w.block_size, per_block, w.seed))
-    note("workload %s: GPU run, pass of %d kv heads, %d sampled rows" % (name, P, len(rows)))
+    if T <= 4096:
+        rows = out_rows = np.arange(T)
+    else:
+        # selection on the first/last and 6 random rows of every block (all rows
+        # of short blocks); outputs on a random subset plus each sequence's
+        # first and last row
+        rows = check.sample_rows(w.cu_seqlens(), w.block_size, 8, w.seed)
+        rng = np.random.default_rng(w.seed + 2000)
+        n_out = 96 if T >= (1 << 20) else 160
+        ends = np.concatenate([w.cu_seqlens()[:-1], w.cu_seqlens()[1:] - 1])
+        out_rows = np.unique(np.concatenate([rng.choice(rows, n_out, replace=False), ends]))
+    note("workload %s: GPU run, pass of %d kv heads, %d/%d sampled rows" % (
+        name, P, len(rows), len(out_rows)))
     out, lse, gsel = staged_run(d, rows)
     # one-call path, same launch configuration: identical bits
     out2, lse2 = moba.moba_fwd_ex(d.q, d.kk, d.v, d.cu, w.block_size, w.topk, d.ws)
@@ -275,11 +284,11 @@ def test_full_workload_sampled_rows(name):
     nb = kbar_ref.shape[0]
     kbar = d.view(d.lay.kbar_offset, nb * w.num_kv_heads * 128, torch.float32).view(
         nb, w.num_kv_heads, 128).cpu().numpy()
-    np.testing.assert_array_equal(kbar, kbar_ref.astype(np.float32))
+    assert np.all(np.abs(kbar - kbar_ref) <= 2.0 ** -23 * np.abs(kbar_ref) + 1e-12)
     note("workload %s: oracle on sampled rows" % name)
-    go, gl = gpu_rows(out, lse, rows)
-    sel, ref_out, ref_lse, info = check.reference_for_rows(
+    sel, ref_out, ref_lse, info, oi = check.reference_for_rows(
         inp.q, inp.k, inp.v, inp.cu_seqlens, kbar_ref, w.block_size, w.topk, rows,
-        gpu_sel_rows=gsel)
+        gpu_sel_rows=gsel, out_rows=out_rows)
+    go, gl = gpu_rows(out, lse, out_rows)
     stats = check.compare_outputs(go, gl, ref_out, ref_lse, w.dtype)
     note("workload %s: %s %s" % (name, stats, info))
