@@ -19,6 +19,8 @@
 // the V^T operand is a contiguous 16-byte LDS read.
 #include <math.h>
 
+#include <type_traits>
+
 #include "moba_internal.h"
 
 namespace moba {
@@ -110,8 +112,10 @@ struct PolF32 {
 };
 
 // Global -> register -> LDS staging of one key tile (64 K rows) and one V^T
-// tile (d rows x 64 keys), 16-byte vectors.
-template <class Pol> struct Stage {
+// tile (d rows x 64 keys), 16-byte vectors. Per-thread offsets are computed
+// once; each tile only moves a uniform base pointer. CHECK guards K rows past
+// the end of the tensor (own-block and dense tiles can run past it).
+template <class Pol, bool CHECK> struct Stage {
   using T = typename Pol::T;
   static constexpr int N = 16 / sizeof(T);
   static constexpr int KVPR = kHeadDim / N;                // vectors per K row
@@ -119,20 +123,28 @@ template <class Pol> struct Stage {
   static constexpr int KV = kKeyTile * KVPR / 256;
   static constexpr int VV = kHeadDim * VVPR / 256;
   uint4 kr[KV], vr[VV];
-  __device__ void load(const T *kbase, int64_t kstride, int64_t row0, int64_t rows_total,
-                       const T *vtile, int64_t vstride) {
+  uint32_t koff[KV], voff[VV];
+  __device__ void init(uint32_t kstride, uint32_t vstride) {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
       const int c = threadIdx.x + 256 * i;
-      const int64_t row = row0 + c / KVPR;
-      kr[i] = row < rows_total ? *(const uint4 *)(kbase + row * kstride + (c % KVPR) * N)
-                               : make_uint4(0, 0, 0, 0);
+      koff[i] = (uint32_t)(c / KVPR) * kstride + (c % KVPR) * N;
     }
 #pragma unroll
     for (int i = 0; i < VV; ++i) {
       const int c = threadIdx.x + 256 * i;
-      vr[i] = *(const uint4 *)(vtile + (int64_t)(c / VVPR) * vstride + (c % VVPR) * N);
+      voff[i] = (uint32_t)(c / VVPR) * vstride + (c % VVPR) * N;
     }
+  }
+  // krows: tile rows that exist in the tensor (only read when CHECK)
+  __device__ void load(const T *ktile, int krows, const T *vtile) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int row = (threadIdx.x + 256 * i) / KVPR;
+      kr[i] = (!CHECK || row < krows) ? *(const uint4 *)(ktile + koff[i]) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VV; ++i) vr[i] = *(const uint4 *)(vtile + voff[i]);
   }
   __device__ void store(T *Ks, T *Vs) const {
 #pragma unroll
@@ -147,6 +159,11 @@ template <class Pol> struct Stage {
     }
   }
 };
+
+// The reference max moves only when a tile's max exceeds it by more than this
+// (log2 units), so probabilities stay <= 2^8 and the rescale of the output
+// accumulators is rare. The result is exact: l uses the same reference.
+constexpr float kRescaleSlack = 8.0f;
 
 enum { MODE_HIST = 0, MODE_DIAG = 1, MODE_DENSE = 2 };
 
@@ -181,11 +198,286 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, float a, f
   *(bf16x4 *)p = v;
 }
 
+// Causal mask of one 64-key tile (own block / dense): key > query -> -inf.
+template <class Pol>
+__device__ __forceinline__ void mask_tile(float (&sv)[2][16], int kt, int qpos, int hh) {
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (kt * kKeyTile + Pol::key_of(st, i, hh) > qpos) sv[st][i] = -INFINITY;
+}
+
+// Online softmax, first half: tile max, lazy move of the reference max (rare
+// rescale of O and l). Returns -m (finite) for the exponent of this tile.
+__device__ __forceinline__ float softmax_rescale(const float (&sv)[2][16], float c2, float &m,
+                                                 float &l, floatx16 (&o)[4]) {
+  float mt = sv[0][0];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sv[st][i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;  // the scale is positive: max commutes with it
+  const bool moved = mt > m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(moved)) {
+    const float alpha = moved ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+    m = moved ? mt : m;
+    l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+  }
+  return m == -INFINITY ? 0.f : -m;  // finite even if nothing was visible yet
+}
+
+// Online-softmax update for one tile of raw scores (q.k, unscaled): leaves the
+// probabilities exp2(c2*s - m) in sv and adds them to l (fp32 path).
+__device__ __forceinline__ void softmax_step(float (&sv)[2][16], float c2, float &m, float &l,
+                                             floatx16 (&o)[4]) {
+  const float nm = softmax_rescale(sv, c2, m, l, o);
+  float rs = 0.f;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sv[st][i] = __builtin_amdgcn_exp2f(fmaf(sv[st][i], c2, nm));
+      rs += sv[st][i];
+    }
+  l += rs;
+}
+
+// ---- bf16 tile loop: direct global->LDS loads, swizzled LDS, QK of the next
+// tile issued before the softmax of the current one.
+//
+// LDS (64 KiB): K buffers 0/1 at 0 / 16 KiB (64 rows x 16 chunks of 16 B),
+// V^T buffers 0/1 at 32 / 48 KiB (128 rows x 8 chunks). Chunk c of K row r is
+// stored at position c ^ (r & 15), chunk c of V^T row r at c ^ ((r >> 1) & 7):
+// the 16 lanes that read one chunk column of 16 consecutive rows then hit 16
+// different 16-byte bank groups. A direct load writes 16 B per lane at
+// LDS base + 16 * lane, so each lane fetches the global chunk that belongs at
+// its fixed LDS position.
+struct Direct {
+  static constexpr int KBUF = 16384, VBUF = 16384;
+  static constexpr int K0 = 0, K1 = KBUF, V0 = 2 * KBUF, V1 = 2 * KBUF + VBUF;
+  static constexpr int BYTES = 2 * KBUF + 2 * VBUF;
+};
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+__device__ __forceinline__ void direct_load16(const void *g, char *lds_region) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_region, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_loads_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+template <int MODE>
+__device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, uint32_t kstride,
+                                             int64_t rows_after, const __bf16 *vt0, int64_t vstep,
+                                             uint32_t vstride, int nkt, const PolBf16::Q &qr,
+                                             int qfirst, int qpos, float c2, floatx16 (&o)[4],
+                                             float &m, float &l) {
+  constexpr bool CAUSAL = MODE != MODE_HIST;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  // direct-load sources: wave w fills K rows 16w..16w+15 and V^T rows 32w..32w+31
+  int krow[4];
+  uint32_t kcol[4], vso[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int region = wave * 4 + j;
+    krow[j] = region * 4 + (lane >> 4);
+    kcol[j] = (uint32_t)(((lane & 15) ^ (krow[j] & 15)) * 8);
+    const int vrow = region * 8 + (lane >> 3);
+    vso[j] = (uint32_t)vrow * vstride + (uint32_t)(((lane & 7) ^ ((vrow >> 1) & 7)) * 8);
+  }
+  // LDS read offsets (bytes) of this lane's MFMA A operands
+  const int pr = PolBf16::perm(n);
+  uint32_t krd[8], vrd[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) krd[kk] = pr * 256 + (((2 * kk + hh) ^ (pr & 15)) * 16);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vrd[c] = n * 128 + (((2 * c + hh) ^ ((n >> 1) & 7)) * 16);
+
+  auto issue_k = [&](int kt, int buf) {
+    const int64_t r0 = (int64_t)kt * kKeyTile;
+    const __bf16 *base = ktile0 + r0 * kstride;
+    const int valid_rows = CAUSAL ? (int)min<int64_t>(rows_after - r0, kKeyTile) : kKeyTile;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // rows past the end of the tensor re-read the last row: those keys lie
+      // beyond every query of the tile and are masked
+      const int row = CAUSAL ? min(krow[j], valid_rows - 1) : krow[j];
+      direct_load16(base + (uint32_t)row * kstride + kcol[j], lds + buf + (wave * 4 + j) * 1024);
+    }
+  };
+  auto issue_v = [&](int kt, int buf) {
+    const __bf16 *base = vt0 + kt * vstep;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) direct_load16(base + vso[j], lds + buf + (wave * 4 + j) * 1024);
+  };
+  auto qk = [&](floatx16 (&acc)[2], int kbuf) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[st][i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 av = *(const bf16x8 *)(lds + kbuf + st * 8192 + krd[kk]);
+        acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qr.v[kk], acc[st], 0, 0, 0);
+      }
+    }
+  };
+  // exp2 of one tile's scores, chunk by chunk straight into the P V product;
+  // the row sum adds the fp32 probabilities (lse keeps fp32 accuracy).
+  auto exp_pv = [&](const floatx16 (&sc)[2], float nm, int vbuf) {
+    float rs = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pj = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * c + j], c2, nm));
+          rs += pj;
+          b[j] = (__bf16)pj;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 av = *(const bf16x8 *)(lds + vbuf + dt * 4096 + vrd[2 * st + c]);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, o[dt], 0, 0, 0);
+        }
+      }
+    l += rs;
+  };
+  // One tile: tile kt's raw scores are in cur; with HAS_NEXT the next tile's
+  // scores are computed into nxt in the same scheduling region, interleaved
+  // with this tile's exponentials.
+  auto body = [&](auto has_next, int kt, floatx16 (&cur)[2], floatx16 (&nxt)[2], int kb_cur,
+                  int kb_nxt, int vb_cur, int vb_nxt) {
+    constexpr bool HAS_NEXT = decltype(has_next)::value;
+    if (HAS_NEXT) issue_v(kt + 1, vb_nxt);
+    if (kt + 2 < nkt) issue_k(kt + 2, kb_cur);
+    if (CAUSAL && kt * kKeyTile + kKeyTile - 1 > qfirst) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt * kKeyTile + PolBf16::key_of(st, i, hh) > qpos) cur[st][i] = -INFINITY;
+    }
+    float sv[2][16];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[st][i] = cur[st][i];
+    const float nm = softmax_rescale(sv, c2, m, l, o);
+    // ---- branch-free region: next QK + this tile's exp and P V
+    if (HAS_NEXT) qk(nxt, kb_nxt);
+    exp_pv(cur, nm, vb_cur);
+    // schedule: LDS operand reads run 4 MFMAs ahead; the exp pipeline fills
+    // the issue slots between the MFMAs
+    constexpr int kAhead = 4;
+    if (HAS_NEXT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // K reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK of the next tile)
+        if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (exp pipeline)
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // V^T reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (P V)
+      if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+    wait_loads_and_sync();
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  issue_k(0, Direct::K0);
+  if (nkt > 1) issue_k(1, Direct::K1);
+  issue_v(0, Direct::V0);
+  wait_loads_and_sync();
+  floatx16 sa[2], sb[2];
+  qk(sa, Direct::K0);
+  __syncthreads();  // every wave has read K buffer 0 before tile 2 refills it
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    body(T_{}, kt, sa, sb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+    body(T_{}, kt + 1, sb, sa, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
+  }
+  if (kt + 1 < nkt) {
+    body(T_{}, kt, sa, sb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+    body(F_{}, kt + 1, sb, sa, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
+  } else {
+    body(F_{}, kt, sa, sb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+  }
+}
+
+// ---- generic tile loop (fp32 path): register-staged loads into padded LDS.
+template <class Pol, int MODE>
+__device__ __forceinline__ void tiles_staged(typename Pol::T *lds, const typename Pol::T *ktile,
+                                             uint32_t kstride, int64_t rows_after,
+                                             const typename Pol::T *vt0, int64_t vstep,
+                                             uint32_t vstride, int nkt, const typename Pol::Q &qr,
+                                             int qfirst, int qpos, float c2, floatx16 (&o)[4],
+                                             float &m, float &l) {
+  using T = typename Pol::T;
+  constexpr int KS = kKeyTile * Pol::KP, VS = kHeadDim * Pol::VP;
+  constexpr bool CHECK = MODE != MODE_HIST;  // earlier blocks are always whole and in range
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31, hh = lane >> 5;
+  Stage<Pol, CHECK> stage;
+  stage.init(kstride, vstride);
+  stage.load(ktile, (int)min<int64_t>(rows_after, kKeyTile), vt0);
+  stage.store(lds, lds + KS);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const T *Ks = lds + (kt & 1) * (KS + VS);
+    const T *Vs = Ks + KS;
+    if (kt + 1 < nkt) {
+      const int64_t r0 = (int64_t)(kt + 1) * kKeyTile;
+      stage.load(ktile + r0 * kstride, (int)min<int64_t>(rows_after - r0, kKeyTile),
+                 vt0 + (kt + 1) * vstep);
+    }
+    float sv[2][16];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      floatx16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      Pol::qk(acc, Ks, st, qr, n, hh);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[st][i] = acc[i];
+    }
+    if (MODE != MODE_HIST && kt * kKeyTile + kKeyTile - 1 > qfirst) mask_tile<Pol>(sv, kt, qpos, hh);
+    softmax_step(sv, c2, m, l, o);
+    Pol::pv(o, Vs, sv, n, hh);
+    if (kt + 1 < nkt) {
+      T *Kn = lds + ((kt + 1) & 1) * (KS + VS);
+      stage.store(Kn, Kn + KS);
+    }
+    __syncthreads();
+  }
+}
+
+template <class Pol> struct LdsBytes {
+  static constexpr int value = 2 * (kKeyTile * Pol::KP + kHeadDim * Pol::VP) * (int)sizeof(typename Pol::T);
+};
+template <> struct LdsBytes<PolBf16> { static constexpr int value = Direct::BYTES; };
+
 template <class Pol, int MODE>
 __global__ __launch_bounds__(256, Pol::kOcc) void attn_kernel(const AttnArgs a) {
   using T = typename Pol::T;
-  constexpr int KS = kKeyTile * Pol::KP, VS = kHeadDim * Pol::VP;
-  __shared__ __attribute__((aligned(16))) T lds[2 * (KS + VS)];
+  __shared__ __attribute__((aligned(1024))) char lds[LdsBytes<Pol>::value];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int r = wave * 32 + n;  // this lane's query row inside the tile
@@ -274,67 +566,14 @@ __global__ __launch_bounds__(256, Pol::kOcc) void attn_kernel(const AttnArgs a) 
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  Stage<Pol> stage;
-  stage.load(kbase, kstride, kbeg, a.T, vt0, vstride);
-  stage.store(lds, lds + KS);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const T *Ks = lds + (kt & 1) * (KS + VS);
-    const T *Vs = Ks + KS;
-    if (kt + 1 < nkt)
-      stage.load(kbase, kstride, kbeg + (int64_t)(kt + 1) * kKeyTile, a.T, vt0 + (kt + 1) * vstep,
-                 vstride);
-
-    float sv[2][16];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      floatx16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      Pol::qk(acc, Ks, st, qr, n, hh);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv[st][i] = acc[i] * a.scale_log2;
-    }
-    if (MODE != MODE_HIST && kt * kKeyTile + kKeyTile - 1 > qfirst) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kt * kKeyTile + Pol::key_of(st, i, hh) > qpos) sv[st][i] = -INFINITY;
-    }
-    float mt = sv[0][0];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sv[st][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;  // no row here is fully masked; stay finite
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
-    m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-    float rs = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[st][i] = __builtin_amdgcn_exp2f(sv[st][i] - mref);
-        rs += sv[st][i];
-      }
-    l += rs;
-    Pol::pv(o, Vs, sv, n, hh);
-
-    if (kt + 1 < nkt) {
-      T *Kn = lds + ((kt + 1) & 1) * (KS + VS);
-      stage.store(Kn, Kn + KS);
-    }
-    __syncthreads();
-  }
+  const T *ktile = kbase + kbeg * kstride;
+  const int64_t rows_after = a.T - kbeg;  // K rows from kbeg to the end of the tensor
+  if constexpr (std::is_same<Pol, PolBf16>::value)
+    tiles_direct<MODE>(lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride,
+                       nkt, qr, qfirst, qpos, a.scale_log2, o, m, l);
+  else
+    tiles_staged<Pol, MODE>((T *)lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep,
+                            (uint32_t)vstride, nkt, qr, qfirst, qpos, a.scale_log2, o, m, l);
 
   const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.f / lt;
