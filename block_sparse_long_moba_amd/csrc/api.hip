@@ -113,7 +113,7 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   const int64_t NBb = ceil_div(T, B) + S;
   const int64_t nbins = (int64_t)P * NBb;
   const int64_t hist_items = T * Hp * (k - 1);
-  const int64_t max_tiles = ceil_div(hist_items, kRowTile) + nbins;
+  const int64_t max_tiles = ceil_div(hist_items, kRowTile) + nbins;  // bound for any tile size
   const int64_t slots = T * Hp * k;
 
   *L = moba_layout_t{};
@@ -152,6 +152,7 @@ Problem make_problem(const moba_shape_t *sh, int32_t B, int32_t k, float scale,
   pb.P = L->kv_heads_per_pass;
   pb.Hp = L->q_heads_per_pass;
   pb.maxblk = L->max_blocks_per_seq;
+  pb.rows = attn_rows(pb.bf16);
   return pb;
 }
 
@@ -174,7 +175,7 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.items = (uint32_t *)(b + L->items_offset);
   w.part_o = (float *)(b + L->part_o_offset);
   w.part_lse = (float *)(b + L->part_lse_offset);
-  w.max_tiles = ceil_div(pb.T * pb.Hp * (pb.k - 1), kRowTile) + nbins;
+  w.max_tiles = ceil_div(pb.T * pb.Hp * (pb.k - 1), pb.rows) + nbins;
   return w;
 }
 

@@ -37,9 +37,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // accumulator i of lane l is C[8*(i/4) + 4*(l/32) + i%4][l%32].
 struct PolBf16 {
   using T = __bf16;
+  static constexpr int kRows = kRowsBf16;        // query rows per workgroup
+  static constexpr int kThreads = 2 * kRows;     // waves of 32 rows
+  static constexpr int kOcc = 2;                 // workgroups per CU
   static constexpr int KP = kHeadDim + 8;  // LDS pitch of a key row (272 B)
   static constexpr int VP = kKeyTile + 8;  // LDS pitch of a V^T row (144 B)
-  static constexpr int kOcc = 2;
   struct Q { bf16x8 v[kHeadDim / 16]; };
   // K row fed to M-row m: swapping bits 2 and 3 makes accumulator i of lane
   // half hh hold key 16*(i/8) + 8*hh + i%8 of the 32-key sub-tile.
@@ -80,9 +82,11 @@ struct PolBf16 {
 // fp32 inputs: v_mfma_f32_32x32x2f32 (lane l holds A[l%32][l/32], B[l/32][l%32]).
 struct PolF32 {
   using T = float;
+  static constexpr int kRows = kRowsF32;         // query rows per workgroup
+  static constexpr int kThreads = 2 * kRows;     // waves of 32 rows
+  static constexpr int kOcc = 1;
   static constexpr int KP = kHeadDim + 4;  // 528 B
   static constexpr int VP = kKeyTile + 4;  // 272 B
-  static constexpr int kOcc = 1;
   struct Q { float v[kHeadDim / 2]; };
   // accumulator i of lane half hh holds key 2*i + hh of the 32-key sub-tile
   __device__ static int perm(int m) { return 8 * (m >> 3) + 2 * (m & 3) + ((m >> 2) & 1); }
@@ -120,19 +124,20 @@ template <class Pol, bool CHECK> struct Stage {
   static constexpr int N = 16 / sizeof(T);
   static constexpr int KVPR = kHeadDim / N;                // vectors per K row
   static constexpr int VVPR = kKeyTile / N;                // vectors per V^T row
-  static constexpr int KV = kKeyTile * KVPR / 256;
-  static constexpr int VV = kHeadDim * VVPR / 256;
+  static constexpr int NT = Pol::kThreads;
+  static constexpr int KV = kKeyTile * KVPR / NT;
+  static constexpr int VV = kHeadDim * VVPR / NT;
   uint4 kr[KV], vr[VV];
   uint32_t koff[KV], voff[VV];
   __device__ void init(uint32_t kstride, uint32_t vstride) {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       koff[i] = (uint32_t)(c / KVPR) * kstride + (c % KVPR) * N;
     }
 #pragma unroll
     for (int i = 0; i < VV; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       voff[i] = (uint32_t)(c / VVPR) * vstride + (c % VVPR) * N;
     }
   }
@@ -140,7 +145,7 @@ template <class Pol, bool CHECK> struct Stage {
   __device__ void load(const T *ktile, int krows, const T *vtile) {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int row = (threadIdx.x + 256 * i) / KVPR;
+      const int row = (threadIdx.x + NT * i) / KVPR;
       kr[i] = (!CHECK || row < krows) ? *(const uint4 *)(ktile + koff[i]) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -149,12 +154,12 @@ template <class Pol, bool CHECK> struct Stage {
   __device__ void store(T *Ks, T *Vs) const {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       *(uint4 *)(Ks + (c / KVPR) * Pol::KP + (c % KVPR) * N) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < VV; ++i) {
-      const int c = threadIdx.x + 256 * i;
+      const int c = threadIdx.x + NT * i;
       *(uint4 *)(Vs + (c / VVPR) * Pol::VP + (c % VVPR) * N) = vr[i];
     }
   }
@@ -208,16 +213,20 @@ __device__ __forceinline__ void mask_tile(float (&sv)[2][16], int kt, int qpos, 
       if (kt * kKeyTile + Pol::key_of(st, i, hh) > qpos) sv[st][i] = -INFINITY;
 }
 
-// Online softmax, first half: tile max, lazy move of the reference max (rare
-// rescale of O and l). Returns -m (finite) for the exponent of this tile.
-__device__ __forceinline__ float softmax_rescale(const float (&sv)[2][16], float c2, float &m,
-                                                 float &l, floatx16 (&o)[4]) {
+// Scaled max of one tile of raw scores (the scale is positive, so it commutes
+// with the max); both lane halves of a query get the same value.
+__device__ __forceinline__ float tile_max(const float (&sv)[2][16], float c2) {
   float mt = sv[0][0];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sv[st][i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;  // the scale is positive: max commutes with it
+  return fmaxf(mt, __shfl_xor(mt, 32)) * c2;
+}
+
+// Lazy move of the reference max given a tile's scaled max mt (rare rescale
+// of O and l). Returns -m (finite) for the exponent of this tile.
+__device__ __forceinline__ float move_max(float mt, float &m, float &l, floatx16 (&o)[4]) {
   const bool moved = mt > m + kRescaleSlack;
   if (__builtin_amdgcn_ballot_w64(moved)) {
     const float alpha = moved ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
@@ -229,6 +238,12 @@ __device__ __forceinline__ float softmax_rescale(const float (&sv)[2][16], float
       for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
   }
   return m == -INFINITY ? 0.f : -m;  // finite even if nothing was visible yet
+}
+
+// Online softmax, first half: tile max, lazy move of the reference max.
+__device__ __forceinline__ float softmax_rescale(const float (&sv)[2][16], float c2, float &m,
+                                                 float &l, floatx16 (&o)[4]) {
+  return move_max(tile_max(sv, c2), m, l, o);
 }
 
 // Online-softmax update for one tile of raw scores (q.k, unscaled): leaves the
@@ -354,48 +369,49 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
       }
     l += rs;
   };
-  // One tile: tile kt's raw scores are in cur; with HAS_NEXT the next tile's
-  // scores are computed into nxt in the same scheduling region, interleaved
-  // with this tile's exponentials.
-  auto body = [&](auto has_next, int kt, floatx16 (&cur)[2], floatx16 (&nxt)[2], int kb_cur,
-                  int kb_nxt, int vb_cur, int vb_nxt) {
-    constexpr bool HAS_NEXT = decltype(has_next)::value;
-    if (HAS_NEXT) issue_v(kt + 1, vb_nxt);
-    if (kt + 2 < nkt) issue_k(kt + 2, kb_cur);
+  auto mask = [&](floatx16 (&sc)[2], int kt) {
     if (CAUSAL && kt * kKeyTile + kKeyTile - 1 > qfirst) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (kt * kKeyTile + PolBf16::key_of(st, i, hh) > qpos) cur[st][i] = -INFINITY;
+          if (kt * kKeyTile + PolBf16::key_of(st, i, hh) > qpos) sc[st][i] = -INFINITY;
     }
+  };
+  auto smax = [&](const floatx16 (&sc)[2]) {
     float sv[2][16];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[st][i] = cur[st][i];
-    const float nm = softmax_rescale(sv, c2, m, l, o);
-    // ---- branch-free region: next QK + this tile's exp and P V
-    if (HAS_NEXT) qk(nxt, kb_nxt);
-    exp_pv(cur, nm, vb_cur);
-    // schedule: LDS operand reads run 4 MFMAs ahead; the exp pipeline fills
-    // the issue slots between the MFMAs
-    constexpr int kAhead = 4;
+      for (int i = 0; i < 16; ++i) sv[st][i] = sc[st][i];
+    return tile_max(sv, c2);
+  };
+  // One tile: tile kt's masked raw scores are in cur and their scaled max in
+  // mt_cur. With HAS_NEXT the next tile's scores (masked) and max are
+  // produced in the same branch-free region as this tile's exp and P V.
+  auto body = [&](auto has_next, int kt, floatx16 (&cur)[2], floatx16 (&nxt)[2], float mt_cur,
+                  float &mt_nxt, int kb_cur, int kb_nxt, int vb_cur, int vb_nxt) {
+    constexpr bool HAS_NEXT = decltype(has_next)::value;
+    if (HAS_NEXT) issue_v(kt + 1, vb_nxt);
+    if (kt + 2 < nkt) issue_k(kt + 2, kb_cur);
+    const float nm = move_max(mt_cur, m, l, o);
+    // ---- branch-free region
     if (HAS_NEXT) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // K reads
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (QK of the next tile)
-        if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (exp pipeline)
-      }
+      qk(nxt, kb_nxt);
+      mask(nxt, kt + 1);
+      mt_nxt = smax(nxt);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // V^T reads
+    exp_pv(cur, nm, vb_cur);
+    // schedule: LDS operand reads run 4 MFMAs ahead; the VALU work is spread
+    // evenly between all MFMAs of the region
+    constexpr int kAhead = 4;
+    constexpr int nmfma = HAS_NEXT ? 32 : 16;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (P V)
-      if (i + kAhead < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    for (int i = 0; i < nmfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + kAhead < nmfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, HAS_NEXT ? 4 : 6, 0);
     }
     wait_loads_and_sync();
   };
@@ -408,17 +424,19 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   wait_loads_and_sync();
   floatx16 sa[2], sb[2];
   qk(sa, Direct::K0);
+  mask(sa, 0);
+  float ma = smax(sa), mb = 0.f;
   __syncthreads();  // every wave has read K buffer 0 before tile 2 refills it
   int kt = 0;
   for (; kt + 2 < nkt; kt += 2) {
-    body(T_{}, kt, sa, sb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
-    body(T_{}, kt + 1, sb, sa, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
+    body(T_{}, kt, sa, sb, ma, mb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+    body(T_{}, kt + 1, sb, sa, mb, ma, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
   }
   if (kt + 1 < nkt) {
-    body(T_{}, kt, sa, sb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
-    body(F_{}, kt + 1, sb, sa, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
+    body(T_{}, kt, sa, sb, ma, mb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+    body(F_{}, kt + 1, sb, sa, mb, ma, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
   } else {
-    body(F_{}, kt, sa, sb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+    body(F_{}, kt, sa, sb, ma, mb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
   }
 }
 
@@ -475,7 +493,8 @@ template <class Pol> struct LdsBytes {
 template <> struct LdsBytes<PolBf16> { static constexpr int value = Direct::BYTES; };
 
 template <class Pol, int MODE>
-__global__ __launch_bounds__(256, Pol::kOcc) void attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const AttnArgs a) {
+  constexpr int ROWS = Pol::kRows;
   using T = typename Pol::T;
   __shared__ __attribute__((aligned(1024))) char lds[LdsBytes<Pol>::value];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -501,8 +520,8 @@ __global__ __launch_bounds__(256, Pol::kOcc) void attn_kernel(const AttnArgs a) 
     const int p = (int)(bin / a.NBb);
     const int64_t gb = bin % a.NBb;
     const int4 bi = a.info[gb];
-    const uint32_t r0 = a.bin_off[bin] + (tile - a.tile_off[bin]) * kRowTile;
-    nrows = (int)min((uint32_t)kRowTile, a.bin_off[bin + 1] - r0);
+    const uint32_t r0 = a.bin_off[bin] + (tile - a.tile_off[bin]) * ROWS;
+    nrows = (int)min((uint32_t)ROWS, a.bin_off[bin + 1] - r0);
     slot = a.items[r0 + (r < nrows ? r : 0)];
     const int64_t th = slot / a.topk;
     t = th / a.Hp;
@@ -514,19 +533,19 @@ __global__ __launch_bounds__(256, Pol::kOcc) void attn_kernel(const AttnArgs a) 
     vstep = kKeyTile;
     vstride = a.B;
   } else if (MODE == MODE_DIAG) {
-    const int nq = (a.B + kRowTile - 1) / kRowTile;
+    const int nq = (a.B + ROWS - 1) / ROWS;
     const int qt = nq - 1 - (int)(blockIdx.x / a.NBb);  // most keys first
     const int64_t gb = blockIdx.x % a.NBb;
     const int4 bi = a.info[gb];
-    if (bi.x < 0 || qt * kRowTile >= bi.z) return;
+    if (bi.x < 0 || qt * ROWS >= bi.z) return;
     const int hl = blockIdx.y;
     hq = a.h0 + hl;
     g = hq / a.G;
-    nrows = min(kRowTile, bi.z - qt * kRowTile);
-    qfirst = qt * kRowTile;
+    nrows = min(ROWS, bi.z - qt * ROWS);
+    qfirst = qt * ROWS;
     qpos = qfirst + r;
     t = bi.y + qfirst + (r < nrows ? r : 0);
-    const int kend = min(bi.z, qfirst + kRowTile);
+    const int kend = min(bi.z, qfirst + ROWS);
     nkt = (kend + kKeyTile - 1) / kKeyTile;
     kbeg = bi.y;
     const int nsel = min(a.topk, bi.w + 1);  // own block is the last chosen slot
@@ -538,14 +557,14 @@ __global__ __launch_bounds__(256, Pol::kOcc) void attn_kernel(const AttnArgs a) 
     const int qt = a.nqt - 1 - (int)(blockIdx.x / a.S);
     const int s = blockIdx.x % a.S;
     const int L = a.cu[s + 1] - a.cu[s];
-    if (qt * kRowTile >= L) return;
+    if (qt * ROWS >= L) return;
     hq = blockIdx.y;
     g = hq / a.G;
-    nrows = min(kRowTile, L - qt * kRowTile);
-    qfirst = qt * kRowTile;
+    nrows = min(ROWS, L - qt * ROWS);
+    qfirst = qt * ROWS;
     qpos = qfirst + r;
     t = a.cu[s] + qfirst + (r < nrows ? r : 0);
-    const int kend = min(L, qfirst + kRowTile);
+    const int kend = min(L, qfirst + ROWS);
     nkt = (kend + kKeyTile - 1) / kKeyTile;
     kbeg = a.cu[s];
     vt0 = (const T *)a.vt + ((int64_t)g * a.NBb64 + a.blk_first64[s]) * kHeadDim * kKeyTile;
@@ -617,9 +636,9 @@ template <int MODE>
 hipError_t launch_mode(bool bf16, dim3 grid, const AttnArgs &a, hipStream_t s) {
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   if (bf16)
-    attn_kernel<PolBf16, MODE><<<grid, 256, 0, s>>>(a);
+    attn_kernel<PolBf16, MODE><<<grid, PolBf16::kThreads, 0, s>>>(a);
   else
-    attn_kernel<PolF32, MODE><<<grid, 256, 0, s>>>(a);
+    attn_kernel<PolF32, MODE><<<grid, PolF32::kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -628,7 +647,7 @@ hipError_t launch_mode(bool bf16, dim3 grid, const AttnArgs &a, hipStream_t s) {
 hipError_t launch_attn_diag(const Problem &pb, const Work &w, const void *q, const void *k, int g0,
                             hipStream_t s) {
   const AttnArgs a = base_args(pb, w, q, k, g0);
-  const int nq = (pb.B + kRowTile - 1) / kRowTile;
+  const int nq = (pb.B + pb.rows - 1) / pb.rows;
   return launch_mode<MODE_DIAG>(pb.bf16, dim3((unsigned)(pb.NBb * nq), (unsigned)pb.Hp), a, s);
 }
 
@@ -649,7 +668,8 @@ hipError_t launch_dense(const void *q, const void *k, const void *vt, const int3
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.scale_log2 = scale * kLog2e;
   a.cu = cu; a.blk_first64 = blk_first64; a.S = S;
-  a.nqt = (maxlen + kRowTile - 1) / kRowTile;
+  const int rows = attn_rows(bf16);
+  a.nqt = (maxlen + rows - 1) / rows;
   a.NBb64 = NBb64;
   a.out = out; a.lse = lse;
   return launch_mode<MODE_DENSE>(bf16 != 0, dim3((unsigned)((int64_t)S * a.nqt), (unsigned)Hq),

@@ -105,10 +105,10 @@ __device__ uint32_t scan1024(uint32_t x, uint32_t *wsum) {
   return r;
 }
 
-// Exclusive scans of the bin counts (item offsets) and of their 128-row tile
-// counts; resets the scatter cursors.
+// Exclusive scans of the bin counts (item offsets) and of their tile counts
+// (tiles of `rows` query rows); resets the scatter cursors.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const uint32_t *__restrict__ count,
-                                                             int64_t nbins,
+                                                             int64_t nbins, uint32_t rows,
                                                              uint32_t *__restrict__ off,
                                                              uint32_t *__restrict__ tile_off,
                                                              uint32_t *__restrict__ cursor) {
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const uint32_t *__r
   for (int64_t base = 0; base < nbins; base += 1024) {
     const int64_t b = base + threadIdx.x;
     const uint32_t n = b < nbins ? count[b] : 0u;
-    const uint32_t nt = (n + kRowTile - 1) / kRowTile;
+    const uint32_t nt = (n + rows - 1) / rows;
     const uint32_t in = scan1024(n, wsum) + carry[0];
     const uint32_t it = scan1024(nt, wsum) + carry[1];
     if (b < nbins) {
@@ -161,7 +161,8 @@ hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s) {
   dispatch_kernel<false><<<grid, 256, 0, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k,
                                               w.bin_count, w.bin_off, w.cursor, w.items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dispatch_scan_kernel<<<1, 1024, 0, s>>>(w.bin_count, nbins, w.bin_off, w.tile_off, w.cursor);
+  dispatch_scan_kernel<<<1, 1024, 0, s>>>(w.bin_count, nbins, (uint32_t)pb.rows, w.bin_off,
+                                          w.tile_off, w.cursor);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   tile_bin_kernel<<<dim3((unsigned)((w.max_tiles + 255) / 256)), 256, 0, s>>>(
       w.tile_off, nbins, w.max_tiles, w.tile_bin);

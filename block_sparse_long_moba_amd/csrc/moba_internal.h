@@ -10,7 +10,10 @@ namespace moba {
 
 constexpr int kHeadDim = 128;       // head dimension of the GPU path
 constexpr int kKeyTile = 64;        // keys per LDS tile in the attention kernels
-constexpr int kRowTile = 128;       // query rows per attention workgroup (4 waves x 32)
+constexpr int kRowTile = 128;       // smallest query-row tile of the attention kernels
+constexpr int kRowsBf16 = 128;      // bf16 attention workgroup: 4 waves x 32 rows
+constexpr int kRowsF32 = 128;       // fp32 attention workgroup: 4 waves x 32 rows
+inline int attn_rows(int bf16) { return bf16 ? kRowsBf16 : kRowsF32; }
 constexpr int kGateTokens = 64;     // tokens per gate workgroup (one wave per query head)
 constexpr int kDispatchTokens = 64; // tokens per dispatch workgroup
 constexpr int kMaxHistPick = 32;    // largest topk-1 kept in registers by the gate
@@ -28,6 +31,7 @@ struct Problem {
   int64_t NBb;      // upper bound on the number of blocks
   int P, Hp;        // kv heads and query heads per pass
   int maxblk;       // ceil(maxlen / B)
+  int rows;         // query rows per attention workgroup (and per dispatch tile)
 };
 
 // Device buffers carved out of a workspace (see moba_layout_t).
