@@ -32,6 +32,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+__device__ __forceinline__ int64_t min_i64(int64_t a, int64_t b) { return a < b ? a : b; }
+
 // bf16 inputs: v_mfma_f32_32x32x16_bf16 (A: 32x16, B: 16x32, fp32 accumulate).
 // Lane l holds A[m = l%32][k = 8*(l/32) .. +7] and B[k = 8*(l/32) .. +7][n = l%32];
 // accumulator i of lane l is C[8*(i/4) + 4*(l/32) + i%4][l%32].
@@ -279,9 +281,17 @@ struct Direct {
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+// Word 3 of a raw buffer descriptor on gfx9-family parts (gfx950 included).
+constexpr int kBufferWord3 = 0x00020000;
 
-__device__ __forceinline__ void direct_load16(const void *g, char *lds_region) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_region, 16, 0, 0);
+// Raw buffer descriptor from wave-uniform values (kept in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, int64_t bytes) {
+  const uint64_t v = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)min_i64(bytes, 0x7fffffff));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           kBufferWord3);
 }
 
 __device__ __forceinline__ void wait_loads_and_sync() {
@@ -296,19 +306,24 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
                                              int qfirst, int qpos, float c2, floatx16 (&o)[4],
                                              float &m, float &l) {
   constexpr bool CAUSAL = MODE != MODE_HIST;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int n = lane & 31, hh = lane >> 5;
-  // direct-load sources: wave w fills K rows 16w..16w+15 and V^T rows 32w..32w+31
+  // direct-load sources (byte offsets from the tile base): wave w fills K rows
+  // 16w..16w+15 and V^T rows 32w..32w+31; its LDS regions start at
+  // buffer + 4 KiB * w (a wave-uniform address, so M0 is set by scalar code)
   int krow[4];
-  uint32_t kcol[4], vso[4];
+  uint32_t kcolb[4], kso[4], vso[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int region = wave * 4 + j;
     krow[j] = region * 4 + (lane >> 4);
-    kcol[j] = (uint32_t)(((lane & 15) ^ (krow[j] & 15)) * 8);
+    kcolb[j] = (uint32_t)(((lane & 15) ^ (krow[j] & 15)) * 16);
+    kso[j] = (uint32_t)krow[j] * kstride * 2u + kcolb[j];
     const int vrow = region * 8 + (lane >> 3);
-    vso[j] = (uint32_t)vrow * vstride + (uint32_t)(((lane & 7) ^ ((vrow >> 1) & 7)) * 8);
+    vso[j] = (uint32_t)vrow * vstride * 2u + (uint32_t)(((lane & 7) ^ ((vrow >> 1) & 7)) * 16);
   }
+  char *const lds_w = lds + wave * 4096;
   // LDS read offsets (bytes) of this lane's MFMA A operands
   const int pr = PolBf16::perm(n);
   uint32_t krd[8], vrd[4];
@@ -317,22 +332,26 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
 #pragma unroll
   for (int c = 0; c < 4; ++c) vrd[c] = n * 128 + (((2 * c + hh) ^ ((n >> 1) & 7)) * 16);
 
+  // Buffer descriptors over this workgroup's keys and values: loads take a
+  // constant per-lane offset plus a scalar per-tile offset, and offsets past
+  // num_records read zeros (K rows past the end of the tensor; those keys lie
+  // beyond every query of the tile and are masked anyway).
+  const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(ktile0, rows_after * kstride * 2);
+  const __amdgpu_buffer_rsrc_t vrs =
+      uniform_rsrc(vt0, (int64_t)(nkt - 1) * vstep * 2 + (int64_t)kHeadDim * vstride * 2);
   auto issue_k = [&](int kt, int buf) {
-    const int64_t r0 = (int64_t)kt * kKeyTile;
-    const __bf16 *base = ktile0 + r0 * kstride;
-    const int valid_rows = CAUSAL ? (int)min<int64_t>(rows_after - r0, kKeyTile) : kKeyTile;
+    const uint32_t soff = (uint32_t)kt * kKeyTile * kstride * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // rows past the end of the tensor re-read the last row: those keys lie
-      // beyond every query of the tile and are masked
-      const int row = CAUSAL ? min(krow[j], valid_rows - 1) : krow[j];
-      direct_load16(base + (uint32_t)row * kstride + kcol[j], lds + buf + (wave * 4 + j) * 1024);
-    }
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(lds_w + buf + j * 1024), 16, kso[j],
+                                               soff, 0, 0);
   };
   auto issue_v = [&](int kt, int buf) {
-    const __bf16 *base = vt0 + kt * vstep;
+    const uint32_t soff = (uint32_t)(kt * vstep) * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) direct_load16(base + vso[j], lds + buf + (wave * 4 + j) * 1024);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(lds_w + buf + j * 1024), 16, vso[j],
+                                               soff, 0, 0);
   };
   auto qk = [&](floatx16 (&acc)[2], int kbuf) {
 #pragma unroll
@@ -455,7 +474,7 @@ __device__ __forceinline__ void tiles_staged(typename Pol::T *lds, const typenam
   const int n = lane & 31, hh = lane >> 5;
   Stage<Pol, CHECK> stage;
   stage.init(kstride, vstride);
-  stage.load(ktile, (int)min<int64_t>(rows_after, kKeyTile), vt0);
+  stage.load(ktile, (int)min_i64(rows_after, kKeyTile), vt0);
   stage.store(lds, lds + KS);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
@@ -463,7 +482,7 @@ __device__ __forceinline__ void tiles_staged(typename Pol::T *lds, const typenam
     const T *Vs = Ks + KS;
     if (kt + 1 < nkt) {
       const int64_t r0 = (int64_t)(kt + 1) * kKeyTile;
-      stage.load(ktile + r0 * kstride, (int)min<int64_t>(rows_after - r0, kKeyTile),
+      stage.load(ktile + r0 * kstride, (int)min_i64(rows_after - r0, kKeyTile),
                  vt0 + (kt + 1) * vstep);
     }
     float sv[2][16];
