@@ -124,7 +124,7 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   L->max_blocks_per_seq = (int32_t)maxblk;
   size_t off = 0;
   L->table_offset = off;     off = align_up(off + table_bytes(S, NBb));
-  L->kbar_offset = off;      off = align_up(off + sizeof(float) * (size_t)NBb * Hkv * kHeadDim);
+  L->kbar_offset = off;      off = align_up(off + (sizeof(float) + 4) * (size_t)NBb * Hkv * kHeadDim);
   L->vt_offset = off;        off = align_up(off + es * (size_t)P * NBb * kHeadDim * B);
   L->idx_offset = off;       off = align_up(off + sizeof(int32_t) * (size_t)slots);
   L->bins_offset = off;      off = align_up(off + sizeof(uint32_t) * (size_t)(4 * nbins + 2 + max_tiles));
@@ -163,6 +163,7 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.cu = (int32_t *)(b + L->table_offset + cu_copy_offset(pb.S));
   w.blk_info = (int4 *)(b + L->table_offset + info_offset(pb.S));
   w.kbar = (float *)(b + L->kbar_offset);
+  w.kbar_split = (__bf16 *)(w.kbar + (size_t)pb.NBb * pb.Hkv * kHeadDim);
   w.vt = b + L->vt_offset;
   w.idx = (int32_t *)(b + L->idx_offset);
   const int64_t nbins = (int64_t)pb.P * pb.NBb;

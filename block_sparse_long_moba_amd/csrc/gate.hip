@@ -133,6 +133,175 @@ __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ q,
   }
 }
 
+// ---- Matrix-core gate (bf16 inputs, GQA groups of a multiple of 4 heads).
+//
+// Scores S^T = Kbar Q^T run on the MFMA with Kbar split into bf16 hi + lo
+// parts (q is exact in bf16; the two products carry ~16 mantissa bits of
+// Kbar, so a score is within ~1e-5 relative of the fp32 dot product). Each
+// lane then holds 16 block scores of one query row per 32-block tile.
+// Top-k: every score becomes an order-preserving 32-bit key whose low
+// idx_bits hold (2^idx_bits - 1 - j), so a larger key means a higher score and,
+// for equal scores, a lower block index. Dropping the low score bits can only
+// reorder scores that agree to better than 2^-(23 - idx_bits) relative. A key
+// enters the lane's descending list with one v_med3_u32 per slot (all slots
+// computed from the old list); the two half-lists of a row (lanes n and n+32)
+// are merged at the end.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGateChunk = 64;                // candidate blocks per LDS chunk
+constexpr int kGatePitch = 2 * kHeadDim + 8;  // bf16 per LDS row: hi | lo | pad (528 B)
+constexpr int kGateRows = 64;                 // tokens per workgroup (2 halves x 32)
+
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+template <int KMAX>
+__device__ __forceinline__ void key_insert(uint32_t (&ts)[KMAX], uint32_t x) {
+  uint32_t nt[KMAX];
+  nt[0] = max(ts[0], x);
+#pragma unroll
+  for (int i = 1; i < KMAX; ++i) nt[i] = med3_u32(ts[i - 1], ts[i], x);
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) ts[i] = nt[i];
+}
+
+__device__ __forceinline__ uint32_t score_key(float s, uint32_t keep, uint32_t low) {
+  const uint32_t u = __float_as_uint(s + 0.0f);  // -0 becomes +0
+  const uint32_t ordered = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return (ordered & keep) | low;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(512) void gate_mfma_kernel(const __bf16 *__restrict__ q,
+                                                        const __bf16 *__restrict__ kbar_split,
+                                                        const int4 *__restrict__ info, int Hq,
+                                                        int Hkv, int G, int h0, int Hp, int k,
+                                                        int idx_bits, int32_t *__restrict__ idx) {
+  const int64_t gb = blockIdx.x;
+  const int4 bi = info[gb];
+  if (bi.x < 0 || (int)blockIdx.y * kGateRows >= bi.z) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n = lane & 31, hh = lane >> 5;
+  const int hl = blockIdx.z * 4 + (wave & 3);
+  const int h = h0 + hl;
+  const int g = (h0 + blockIdx.z * 4) / G;  // the 4 heads share one kv head
+  const int c = bi.w;
+  const int64_t first = gb - c;
+  const int pick = k - 1;
+  const int r = blockIdx.y * kGateRows + (wave >> 2) * 32 + n;
+  const bool active = r < bi.z;
+  const int64_t t = bi.y + (active ? r : 0);
+  int32_t *dst = idx + (t * Hp + hl) * k;
+
+  if (pick >= c) {  // every earlier block fits: nothing to rank
+    if (active && hh == 0) {
+      for (int j = 0; j < c; ++j) dst[j] = j;
+      dst[c] = c;
+      for (int j = c + 1; j < k; ++j) dst[j] = -1;
+    }
+    return;
+  }
+
+  bf16x8 qv[kHeadDim / 16];
+  const __bf16 *qrow = q + (t * Hq + h) * kHeadDim + 8 * hh;
+#pragma unroll
+  for (int kk = 0; kk < kHeadDim / 16; ++kk) qv[kk] = *(const bf16x8 *)(qrow + 16 * kk);
+
+  __shared__ __attribute__((aligned(16))) __bf16 kl[kGateChunk * kGatePitch];
+  uint32_t ts[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) ts[i] = 0u;
+  const uint32_t maxi = (1u << idx_bits) - 1u, keep = ~maxi;
+  const __bf16 *ksrc = kbar_split + (first * Hkv + g) * 2 * kHeadDim;
+  const int64_t krow_stride = (int64_t)Hkv * 2 * kHeadDim;
+
+  for (int j0 = 0; j0 < c; j0 += kGateChunk) {
+    __syncthreads();  // the previous chunk has been consumed
+    for (int x = threadIdx.x; x < kGateChunk * 32; x += 512) {
+      const int row = x >> 5, col = x & 31;  // 32 16-byte pieces per row: hi then lo
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j0 + row < c) v = *(const uint4 *)(ksrc + (j0 + row) * krow_stride + col * 8);
+      *(uint4 *)(kl + row * kGatePitch + col * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (j0 + 32 * st >= c) break;
+      floatx16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      const __bf16 *ar = kl + (32 * st + n) * kGatePitch + 8 * hh;
+#pragma unroll
+      for (int kk = 0; kk < kHeadDim / 16; ++kk) {
+        const bf16x8 ahi = *(const bf16x8 *)(ar + 16 * kk);
+        const bf16x8 alo = *(const bf16x8 *)(ar + kHeadDim + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qv[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qv[kk], acc, 0, 0, 0);
+      }
+      const int jb = j0 + 32 * st + 4 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = jb + 8 * (i >> 2) + (i & 3);  // accumulator i holds block j
+        key_insert<KMAX>(ts, j < c ? score_key(acc[i], keep, maxi - (uint32_t)j) : 0u);
+      }
+    }
+  }
+  // merge the two half-lists of the row (lanes n and n + 32)
+  uint32_t other[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) other[i] = __shfl_xor(ts[i], 32);
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) key_insert<KMAX>(ts, other[i]);
+  // chosen indices in ascending order (entries past `pick` become sentinels)
+  int sel[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) sel[i] = i < pick ? (int)(maxi - (ts[i] & maxi)) : INT_MAX;
+#pragma unroll
+  for (int pass = 0; pass < KMAX; ++pass)
+#pragma unroll
+    for (int i = pass & 1; i + 1 < KMAX; i += 2) {
+      const int a = sel[i], b = sel[i + 1];
+      sel[i] = min(a, b);
+      sel[i + 1] = max(a, b);
+    }
+  if (active && hh == 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (i < pick) dst[i] = sel[i];
+    dst[pick] = c;
+  }
+}
+
+// Bits needed for a local block index (at least 1).
+int index_bits(int maxblk) {
+  int b = 1;
+  while ((1 << b) < maxblk) ++b;
+  return b;
+}
+
+hipError_t launch_gate_mfma(const Problem &pb, const Work &w, const __bf16 *q, int g0,
+                            hipStream_t s, int bits) {
+  dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kGateRows - 1) / kGateRows), (unsigned)(pb.Hp / 4));
+  const int h0 = g0 * pb.G;
+  const int pick = pb.k - 1;
+#define MOBA_GATE_MFMA(KM)                                                                       \
+  gate_mfma_kernel<KM><<<grid, 512, 0, s>>>(q, w.kbar_split, w.blk_info, pb.Hq, pb.Hkv, pb.G, h0, \
+                                            pb.Hp, pb.k, bits, w.idx)
+  if (pick <= 4) MOBA_GATE_MFMA(4);
+  else if (pick <= 8) MOBA_GATE_MFMA(8);
+  else if (pick <= 12) MOBA_GATE_MFMA(12);
+  else if (pick <= 16) MOBA_GATE_MFMA(16);
+  else if (pick <= 24) MOBA_GATE_MFMA(24);
+  else if (pick <= kMaxHistPick) MOBA_GATE_MFMA(kMaxHistPick);
+  else MOBA_GATE_MFMA(4);  // only with the select-all path
+#undef MOBA_GATE_MFMA
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_gate_t(const Problem &pb, const Work &w, const T *q, int g0, hipStream_t s) {
   dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kGateTokens - 1) / kGateTokens),
@@ -160,6 +329,11 @@ hipError_t launch_gate_t(const Problem &pb, const Work &w, const T *q, int g0, h
 }  // namespace
 
 hipError_t launch_gate(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s) {
+  // matrix-core gate: bf16, groups of a multiple of 4 heads, at most 4096
+  // blocks per sequence (12 index bits keep 20 score bits in the keys)
+  const int bits = index_bits(pb.maxblk);
+  if (pb.bf16 && pb.G % 4 == 0 && bits <= 12)
+    return launch_gate_mfma(pb, w, (const __bf16 *)q, g0, s, bits);
   return pb.bf16 ? launch_gate_t<__bf16>(pb, w, (const __bf16 *)q, g0, s)
                  : launch_gate_t<float>(pb, w, (const float *)q, g0, s);
 }

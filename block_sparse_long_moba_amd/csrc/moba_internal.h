@@ -40,6 +40,7 @@ struct Work {
   int32_t *cu;          // [S+1] copy of cu_seqlens
   int4 *blk_info;       // [NBb] {seq, first row, rows, local block}
   float *kbar;          // [NBb][Hkv][d]
+  __bf16 *kbar_split;   // [NBb][Hkv][2][d]: bf16 hi and lo parts, kbar ~= hi + lo
   void *vt;             // [P][NBb][d][B]
   int32_t *idx;         // [T][Hp][k]
   uint32_t *bin_count;  // [P*NBb]

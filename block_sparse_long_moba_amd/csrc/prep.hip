@@ -111,10 +111,13 @@ template <> struct Vec16<float> {
 // 3.4 of the MoBA summary page; step 1 of its implementation). One workgroup
 // per (block, kv head): 16 row groups x 16 column threads, fp64 accumulation so
 // the stored fp32 mean is the correctly rounded block mean up to one rounding.
+// Also writes the bf16 split hi = bf16(mean), lo = bf16(mean - hi) that the
+// gate's matrix-core scores use (two bf16 products recover ~16 mantissa bits).
 template <typename T>
 __global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
                                                        const int4 *__restrict__ info, int Hkv,
-                                                       float *__restrict__ kbar) {
+                                                       float *__restrict__ kbar,
+                                                       __bf16 *__restrict__ kbar_split) {
   constexpr int N = Vec16<T>::N;        // elements per 16-byte load
   constexpr int COLS = kHeadDim / N;    // threads per row: 16 (bf16) or 32 (fp32)
   constexpr int RG = 256 / COLS;        // row groups
@@ -151,7 +154,13 @@ __global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < RG; ++i) s += red[i][threadIdx.x];
-    kbar[((int64_t)gb * Hkv + g) * kHeadDim + threadIdx.x] = (float)(s / (double)bi.z);
+    const float mean = (float)(s / (double)bi.z);
+    kbar[((int64_t)gb * Hkv + g) * kHeadDim + threadIdx.x] = mean;
+    const __bf16 hi = (__bf16)mean;
+    const __bf16 lo = (__bf16)(mean - (float)hi);
+    __bf16 *sp = kbar_split + ((int64_t)gb * Hkv + g) * 2 * kHeadDim + threadIdx.x;
+    sp[0] = hi;
+    sp[kHeadDim] = lo;
   }
 }
 
@@ -273,9 +282,11 @@ hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t NBb, int32_t
 hipError_t launch_meanpool(const Problem &pb, const Work &w, const void *k, hipStream_t s) {
   dim3 grid((unsigned)pb.NBb, (unsigned)pb.Hkv);
   if (pb.bf16)
-    meanpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, w.blk_info, pb.Hkv, w.kbar);
+    meanpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, w.blk_info, pb.Hkv, w.kbar,
+                                                  w.kbar_split);
   else
-    meanpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kbar);
+    meanpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kbar,
+                                                 w.kbar_split);
   return hipGetLastError();
 }
 

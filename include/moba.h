@@ -105,7 +105,8 @@ typedef struct moba_layout {
    * {sequence, first row, rows, local block index} (sequence = -1 for
    * indices past the last block). Written by moba_seqtable. */
   size_t table_offset;
-  /* float32 kbar[NBb][Hkv][d]: mean-pooled keys of every block. */
+  /* float32 kbar[NBb][Hkv][d]: mean-pooled keys of every block, followed by
+   * bf16 kbar_split[NBb][Hkv][2][d]: hi = bf16(kbar), lo = bf16(kbar - hi). */
   size_t kbar_offset;
   /* element type, vt[P][NBb][d][block_size]: for each kv head of the pass
    * and each block, the block's value rows transposed (zero past its rows). */
