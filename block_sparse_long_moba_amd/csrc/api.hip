@@ -129,7 +129,7 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   L->idx_offset = off;       off = align_up(off + sizeof(int32_t) * (size_t)slots);
   L->bins_offset = off;      off = align_up(off + sizeof(uint32_t) * (size_t)(4 * nbins + 2 + max_tiles));
   L->items_offset = off;     off = align_up(off + sizeof(uint32_t) * (size_t)std::max<int64_t>(1, hist_items));
-  L->part_o_offset = off;    off = align_up(off + sizeof(float) * (size_t)slots * kHeadDim);
+  L->part_o_offset = off;    off = align_up(off + es * (size_t)slots * kHeadDim);
   L->part_lse_offset = off;  off = align_up(off + sizeof(float) * (size_t)slots);
   L->total_bytes = off;
   return MOBA_SUCCESS;
@@ -174,7 +174,7 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.cursor = bins + 3 * nbins + 2;
   w.tile_bin = bins + 4 * nbins + 2;
   w.items = (uint32_t *)(b + L->items_offset);
-  w.part_o = (float *)(b + L->part_o_offset);
+  w.part_o = b + L->part_o_offset;
   w.part_lse = (float *)(b + L->part_lse_offset);
   w.max_tiles = ceil_div(pb.T * pb.Hp * (pb.k - 1), pb.rows) + nbins;
   return w;

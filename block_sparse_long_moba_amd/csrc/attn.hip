@@ -186,7 +186,8 @@ struct AttnArgs {
   const uint32_t *tile_off, *tile_bin, *bin_off, *items;
   int64_t nbins;
   // partial outputs (MoBA) or final outputs (dense)
-  float *part_o, *part_lse;
+  void *part_o;
+  float *part_lse;
   const int32_t *cu, *blk_first64;
   int S, nqt;
   int64_t NBb64;
@@ -618,13 +619,13 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   const float lse = (m + __log2f(lt)) * kLn2;
   if (!valid) return;
   if (MODE != MODE_DENSE) {
-    float *dst = a.part_o + slot * kHeadDim + 4 * hh;
+    T *dst = (T *)a.part_o + slot * kHeadDim + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int aa = 0; aa < 4; ++aa)
-        store4<float>(dst + 32 * dt + 8 * aa, o[dt][4 * aa] * inv, o[dt][4 * aa + 1] * inv,
-                      o[dt][4 * aa + 2] * inv, o[dt][4 * aa + 3] * inv);
+        store4<T>(dst + 32 * dt + 8 * aa, o[dt][4 * aa] * inv, o[dt][4 * aa + 1] * inv,
+                  o[dt][4 * aa + 2] * inv, o[dt][4 * aa + 3] * inv);
     if (hh == 0) a.part_lse[slot] = lse;
   } else {
     T *dst = (T *)a.out + (t * a.Hq + hq) * kHeadDim + 4 * hh;

@@ -49,7 +49,7 @@ struct Work {
   uint32_t *cursor;     // [P*NBb]
   uint32_t *tile_bin;   // [max tiles]
   uint32_t *items;      // [T*Hp*(k-1)]
-  float *part_o;        // [T*Hp*k][d]
+  void *part_o;         // [T*Hp*k][d], element type of the inputs
   float *part_lse;      // [T*Hp*k]
   int64_t max_tiles;
 };

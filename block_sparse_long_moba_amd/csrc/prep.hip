@@ -230,8 +230,17 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, float4 v) 
 // implementation in section 3.4 of the MoBA summary page: rescale each part by
 // its normaliser). Slots are combined in ascending block order.
 // 32 threads per (row, head), 4 head-dim elements each.
+template <typename TO> __device__ __forceinline__ float4 load4(const TO *p);
+template <> __device__ __forceinline__ float4 load4<float>(const float *p) { return *(const float4 *)p; }
+template <> __device__ __forceinline__ float4 load4<__bf16>(const __bf16 *p) {
+  const uint2 u = *(const uint2 *)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// Partial outputs are stored in the element type of the inputs.
 template <typename TO>
-__global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ part_o,
+__global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
                                                     const int32_t *__restrict__ cu, int S,
                                                     int64_t T_, int Hq, int h0, int Hp, int B,
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ pa
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i = 0; i < nsel; ++i) {
     const float wgt = expf(pl[i] - L);
-    const float4 o = *(const float4 *)(part_o + (row * k + i) * kHeadDim + lane * 4);
+    const float4 o = load4<TO>(part_o + (row * k + i) * kHeadDim + lane * 4);
     acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
   }
   store4<TO>(out + (t * Hq + h0 + hl) * kHeadDim + lane * 4, acc);
@@ -310,10 +319,10 @@ hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, flo
   dim3 grid((unsigned)((rows + 7) / 8));
   const int h0 = g0 * pb.G;
   if (pb.bf16)
-    merge_kernel<__bf16><<<grid, 256, 0, s>>>(w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
+    merge_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
                                               pb.Hp, pb.B, pb.k, (__bf16 *)out, lse);
   else
-    merge_kernel<float><<<grid, 256, 0, s>>>(w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
+    merge_kernel<float><<<grid, 256, 0, s>>>((const float *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
                                              pb.Hp, pb.B, pb.k, (float *)out, lse);
   return hipGetLastError();
 }

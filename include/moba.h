@@ -122,8 +122,9 @@ typedef struct moba_layout {
   /* uint32 items[T*Hp*(topk-1)]: per bin, the slots (t*Hp + hl)*topk + s that
    * chose the bin's block as an earlier block (order inside a bin unspecified). */
   size_t items_offset;
-  /* float32 part_o[T*Hp*topk][d] and part_lse[T*Hp*topk]: attention of slot
-   * (t, hl, s) over block idx[t][hl][s] alone (normalised), and its lse. */
+  /* part_o[T*Hp*topk][d] (element type of the inputs) and float32
+   * part_lse[T*Hp*topk]: attention of slot (t, hl, s) over block idx[t][hl][s]
+   * alone (normalised), and its lse. */
   size_t part_o_offset;
   size_t part_lse_offset;
   size_t total_bytes;

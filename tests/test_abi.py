@@ -47,7 +47,7 @@ def test_plan_sizes_and_offsets_are_consistent():
             lay.items_offset, lay.part_o_offset, lay.part_lse_offset, lay.total_bytes]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     slots = (1 << 20) * 4 * 12
-    assert lay.part_lse_offset - lay.part_o_offset >= slots * 128 * 4
+    assert lay.part_lse_offset - lay.part_o_offset >= slots * 128 * 2  # bf16 partials
     assert lay.total_bytes == moba.moba_fwd_workspace_size(sh, 4096, 12, 1)
     full = moba.moba_plan(sh, 4096, 12, 0)
     assert full.kv_heads_per_pass == 8 and full.total_bytes > lay.total_bytes
