@@ -7,6 +7,8 @@
 namespace moba {
 namespace {
 
+constexpr float kLog2eF = 1.4426950408889634f;
+
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, uint32_t value, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = value;
@@ -217,28 +219,12 @@ __device__ __forceinline__ int seq_of_row(const int32_t *cu, int S, int64_t t) {
   return lo;
 }
 
-template <typename TO> __device__ __forceinline__ void store4(TO *p, float4 v);
-template <> __device__ __forceinline__ void store4<float>(float *p, float4 v) { *(float4 *)p = v; }
-template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, float4 v) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 b;
-  b[0] = (__bf16)v.x; b[1] = (__bf16)v.y; b[2] = (__bf16)v.z; b[3] = (__bf16)v.w;
-  *(bf16x4 *)p = b;
-}
 
 // Log-sum-exp combination of the per-block partial outputs (step 4 of the
 // implementation in section 3.4 of the MoBA summary page: rescale each part by
 // its normaliser). Slots are combined in ascending block order.
-// 32 threads per (row, head), 4 head-dim elements each.
-template <typename TO> __device__ __forceinline__ float4 load4(const TO *p);
-template <> __device__ __forceinline__ float4 load4<float>(const float *p) { return *(const float4 *)p; }
-template <> __device__ __forceinline__ float4 load4<__bf16>(const __bf16 *p) {
-  const uint2 u = *(const uint2 *)p;
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-
-// Partial outputs are stored in the element type of the inputs.
+// One row (token, head) per group of LANES threads, 16 bytes of the row each;
+// slot loads are issued four at a time so several are in flight per thread.
 template <typename TO>
 __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
@@ -246,9 +232,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
                                                     int64_t T_, int Hq, int h0, int Hp, int B,
                                                     int k, TO *__restrict__ out,
                                                     float *__restrict__ lse_out) {
-  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  constexpr int N = 16 / sizeof(TO);       // elements per thread
+  constexpr int LANES = kHeadDim / N;      // threads per row: 16 (bf16) or 32 (fp32)
+  constexpr int ROWS = 256 / LANES;
+  const int64_t row = (int64_t)blockIdx.x * ROWS + threadIdx.x / LANES;
   if (row >= T_ * Hp) return;
-  const int lane = threadIdx.x & 31;
+  const int lane = threadIdx.x % LANES;
   const int64_t t = row / Hp;
   const int hl = (int)(row % Hp);
   const int s = seq_of_row(cu, S, t);
@@ -258,15 +247,31 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
   float m = -INFINITY;
   for (int i = 0; i < nsel; ++i) m = fmaxf(m, pl[i]);
   float sum = 0.f;
-  for (int i = 0; i < nsel; ++i) sum += expf(pl[i] - m);
+  for (int i = 0; i < nsel; ++i) sum += __builtin_amdgcn_exp2f((pl[i] - m) * kLog2eF);
   const float L = m + logf(sum);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = 0; i < nsel; ++i) {
-    const float wgt = expf(pl[i] - L);
-    const float4 o = load4<TO>(part_o + (row * k + i) * kHeadDim + lane * 4);
-    acc.x += wgt * o.x; acc.y += wgt * o.y; acc.z += wgt * o.z; acc.w += wgt * o.w;
+  float acc[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) acc[j] = 0.f;
+  const TO *po = part_o + row * k * kHeadDim + lane * N;
+  for (int i0 = 0; i0 < nsel; i0 += 4) {
+    uint4 raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      raw[u] = i0 + u < nsel ? *(const uint4 *)(po + (int64_t)(i0 + u) * kHeadDim)
+                             : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u >= nsel) break;
+      const float wgt = __builtin_amdgcn_exp2f((pl[i0 + u] - L) * kLog2eF);
+      const TO *v = (const TO *)&raw[u];
+#pragma unroll
+      for (int j = 0; j < N; ++j) acc[j] += wgt * (float)v[j];
+    }
   }
-  store4<TO>(out + (t * Hq + h0 + hl) * kHeadDim + lane * 4, acc);
+  TO res[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) res[j] = (TO)acc[j];
+  *(uint4 *)(out + (t * Hq + h0 + hl) * kHeadDim + lane * N) = *(const uint4 *)res;
   if (lane == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = L;
 }
 
@@ -316,7 +321,8 @@ hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, flo
   const int32_t *cu = w.cu;
   const int64_t rows = pb.T * pb.Hp;
   if (rows == 0) return hipSuccess;
-  dim3 grid((unsigned)((rows + 7) / 8));
+  const int rows_per_wg = pb.bf16 ? 16 : 8;
+  dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
   const int h0 = g0 * pb.G;
   if (pb.bf16)
     merge_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
