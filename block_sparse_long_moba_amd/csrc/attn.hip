@@ -41,7 +41,7 @@ struct PolBf16 {
   using T = __bf16;
   static constexpr int kRows = kRowsBf16;        // query rows per workgroup
   static constexpr int kThreads = 2 * kRows;     // waves of 32 rows
-  static constexpr int kOcc = 2;                 // workgroups per CU
+  static constexpr int kOcc = 1;                 // workgroups per CU (64 KiB LDS, 8 waves)
   static constexpr int KP = kHeadDim + 8;  // LDS pitch of a key row (272 B)
   static constexpr int VP = kKeyTile + 8;  // LDS pitch of a V^T row (144 B)
   struct Q { bf16x8 v[kHeadDim / 16]; };
@@ -300,7 +300,7 @@ __device__ __forceinline__ void wait_loads_and_sync() {
   __syncthreads();
 }
 
-template <int MODE>
+template <int MODE, int NW>
 __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, uint32_t kstride,
                                              int64_t rows_after, const __bf16 *vt0, int64_t vstep,
                                              uint32_t vstride, int nkt, const PolBf16::Q &qr,
@@ -310,21 +310,21 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int n = lane & 31, hh = lane >> 5;
-  // direct-load sources (byte offsets from the tile base): wave w fills K rows
-  // 16w..16w+15 and V^T rows 32w..32w+31; its LDS regions start at
-  // buffer + 4 KiB * w (a wave-uniform address, so M0 is set by scalar code)
-  int krow[4];
-  uint32_t kcolb[4], kso[4], vso[4];
+  // direct-load sources (byte offsets from the tile base): each tile is 16
+  // regions of 1 KiB (K: 4 rows, V^T: 8 rows per region); wave w fills regions
+  // w*LPW .. w*LPW+LPW-1 of both, at buffer + LPW KiB * w (a wave-uniform
+  // address, so M0 is set by scalar code)
+  constexpr int LPW = 16 / NW;  // loads per wave per tile and tensor
+  uint32_t kso[LPW], vso[LPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int region = wave * 4 + j;
-    krow[j] = region * 4 + (lane >> 4);
-    kcolb[j] = (uint32_t)(((lane & 15) ^ (krow[j] & 15)) * 16);
-    kso[j] = (uint32_t)krow[j] * kstride * 2u + kcolb[j];
+  for (int j = 0; j < LPW; ++j) {
+    const int region = wave * LPW + j;
+    const int krow = region * 4 + (lane >> 4);
+    kso[j] = (uint32_t)krow * kstride * 2u + (uint32_t)(((lane & 15) ^ (krow & 15)) * 16);
     const int vrow = region * 8 + (lane >> 3);
     vso[j] = (uint32_t)vrow * vstride * 2u + (uint32_t)(((lane & 7) ^ ((vrow >> 1) & 7)) * 16);
   }
-  char *const lds_w = lds + wave * 4096;
+  char *const lds_w = lds + wave * LPW * 1024;
   // LDS read offsets (bytes) of this lane's MFMA A operands
   const int pr = PolBf16::perm(n);
   uint32_t krd[8], vrd[4];
@@ -343,14 +343,14 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   auto issue_k = [&](int kt, int buf) {
     const uint32_t soff = (uint32_t)kt * kKeyTile * kstride * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < LPW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(lds_w + buf + j * 1024), 16, kso[j],
                                                soff, 0, 0);
   };
   auto issue_v = [&](int kt, int buf) {
     const uint32_t soff = (uint32_t)(kt * vstep) * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < LPW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(lds_w + buf + j * 1024), 16, vso[j],
                                                soff, 0, 0);
   };
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   const T *ktile = kbase + kbeg * kstride;
   const int64_t rows_after = a.T - kbeg;  // K rows from kbeg to the end of the tensor
   if constexpr (std::is_same<Pol, PolBf16>::value)
-    tiles_direct<MODE>(lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride,
+    tiles_direct<MODE, Pol::kThreads / 64>(lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride,
                        nkt, qr, qfirst, qpos, a.scale_log2, o, m, l);
   else
     tiles_staged<Pol, MODE>((T *)lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep,

@@ -11,7 +11,7 @@ namespace moba {
 constexpr int kHeadDim = 128;       // head dimension of the GPU path
 constexpr int kKeyTile = 64;        // keys per LDS tile in the attention kernels
 constexpr int kRowTile = 128;       // smallest query-row tile of the attention kernels
-constexpr int kRowsBf16 = 128;      // bf16 attention workgroup: 4 waves x 32 rows
+constexpr int kRowsBf16 = 256;      // bf16 attention workgroup: 8 waves x 32 rows
 constexpr int kRowsF32 = 128;       // fp32 attention workgroup: 4 waves x 32 rows
 inline int attn_rows(int bf16) { return bf16 ? kRowsBf16 : kRowsF32; }
 constexpr int kGateTokens = 64;     // tokens per gate workgroup (one wave per query head)
