@@ -114,6 +114,11 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   const int64_t nbins = (int64_t)P * NBb;
   const int64_t hist_items = T * Hp * (k - 1);
   const int64_t max_tiles = ceil_div(hist_items, kRowTile) + nbins;  // bound for any tile size
+  // own-block attention launches one workgroup per (query head, block, row tile)
+  if ((int64_t)Hp * NBb * ceil_div(B, kRowTile) >= (int64_t(1) << 31))
+    return fail(MOBA_ERROR_UNSUPPORTED,
+                "too many own-block tiles per pass (num_q_heads * blocks * block_size / %d)",
+                kRowTile);
   const int64_t slots = T * Hp * k;
 
   *L = moba_layout_t{};

@@ -41,7 +41,9 @@ struct PolBf16 {
   using T = __bf16;
   static constexpr int kRows = kRowsBf16;        // query rows per workgroup
   static constexpr int kThreads = 2 * kRows;     // waves of 32 rows
-  static constexpr int kOcc = 1;                 // workgroups per CU (64 KiB LDS, 8 waves)
+  static constexpr int kOcc = 1;                 // workgroups per CU (8 waves)
+  static constexpr int kStages = 2;              // K and V^T tile buffers in LDS (4 spills VGPRs)
+  static constexpr int kLoadAhead = 1;           // tiles between a load's issue and its use
   static constexpr int KP = kHeadDim + 8;  // LDS pitch of a key row (272 B)
   static constexpr int VP = kKeyTile + 8;  // LDS pitch of a V^T row (144 B)
   struct Q { bf16x8 v[kHeadDim / 16]; };
@@ -268,17 +270,17 @@ __device__ __forceinline__ void softmax_step(float (&sv)[2][16], float c2, float
 // ---- bf16 tile loop: direct global->LDS loads, swizzled LDS, QK of the next
 // tile issued before the softmax of the current one.
 //
-// LDS (64 KiB): K buffers 0/1 at 0 / 16 KiB (64 rows x 16 chunks of 16 B),
-// V^T buffers 0/1 at 32 / 48 KiB (128 rows x 8 chunks). Chunk c of K row r is
-// stored at position c ^ (r & 15), chunk c of V^T row r at c ^ ((r >> 1) & 7):
-// the 16 lanes that read one chunk column of 16 consecutive rows then hit 16
-// different 16-byte bank groups. A direct load writes 16 B per lane at
-// LDS base + 16 * lane, so each lane fetches the global chunk that belongs at
-// its fixed LDS position.
-struct Direct {
-  static constexpr int KBUF = 16384, VBUF = 16384;
-  static constexpr int K0 = 0, K1 = KBUF, V0 = 2 * KBUF, V1 = 2 * KBUF + VBUF;
-  static constexpr int BYTES = 2 * KBUF + 2 * VBUF;
+// LDS: NS K buffers (64 rows x 16 chunks of 16 B) then NS V^T buffers (128
+// rows x 8 chunks), 16 KiB each. Chunk c of K row r is stored at position
+// c ^ (r & 15), chunk c of V^T row r at c ^ ((r >> 1) & 7): the 16 lanes that
+// read one chunk column of 16 consecutive rows then hit 16 different 16-byte
+// bank groups. A direct load writes 16 B per lane at LDS base + 16 * lane, so
+// each lane fetches the global chunk that belongs at its fixed LDS position.
+template <int NS> struct Direct {
+  static constexpr int BUF = 16384;
+  static constexpr int K(int i) { return i * BUF; }
+  static constexpr int V(int i) { return (NS + i) * BUF; }
+  static constexpr int BYTES = 2 * NS * BUF;
 };
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
@@ -300,7 +302,28 @@ __device__ __forceinline__ void wait_loads_and_sync() {
   __syncthreads();
 }
 
-template <int MODE, int NW>
+// Wait until at most N vector memory loads of this wave are outstanding.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Same with N = c * PER for a wave-uniform c in [0, MAXC].
+template <int PER, int MAXC> __device__ __forceinline__ void wait_vm_groups(int c) {
+  if constexpr (MAXC == 0) {
+    wait_vm<0>();
+  } else {
+    if (c >= MAXC) wait_vm<MAXC * PER>();
+    else wait_vm_groups<PER, MAXC - 1>(c);
+  }
+}
+
+// Tile pipeline: key tile kt lives in K buffer kt % NS and V^T buffer
+// kt % NS. Body kt computes the scores of tile kt + 1 and the exp and P V of
+// tile kt, and issues the loads of V^T tile kt + A and K tile kt + A + 1; at
+// its end each wave waits for its loads that the next body reads (V^T tile
+// kt + 1, K tile kt + 2), then the workgroup synchronises. A buffer is
+// refilled only after the barrier that ends the last body reading it, which
+// needs NS >= A + 1.
+template <int MODE, int NW, int NS, int A>
 __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, uint32_t kstride,
                                              int64_t rows_after, const __bf16 *vt0, int64_t vstep,
                                              uint32_t vstride, int nkt, const PolBf16::Q &qr,
@@ -406,22 +429,28 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
       for (int i = 0; i < 16; ++i) sv[st][i] = sc[st][i];
     return tile_max(sv, c2);
   };
+  static_assert((NS == 2 || NS == 4) && NS >= A + 1 && A >= 1, "pipeline shape");
+  using D = Direct<NS>;
+  // Loads issued by body j (j < 0: the prologue's share of the pipeline).
+  auto loads_of = [&](int j) { return (j + A < nkt ? 1 : 0) + (j + A + 1 < nkt ? 1 : 0); };
   // One tile: tile kt's masked raw scores are in cur and their scaled max in
   // mt_cur. With HAS_NEXT the next tile's scores (masked) and max are
   // produced in the same branch-free region as this tile's exp and P V.
-  auto body = [&](auto has_next, int kt, floatx16 (&cur)[2], floatx16 (&nxt)[2], float mt_cur,
-                  float &mt_nxt, int kb_cur, int kb_nxt, int vb_cur, int vb_nxt) {
+  // PH = kt % NS selects the buffers at compile time.
+  auto body = [&](auto has_next, auto phase, int kt, floatx16 (&cur)[2], floatx16 (&nxt)[2],
+                  float mt_cur, float &mt_nxt) {
     constexpr bool HAS_NEXT = decltype(has_next)::value;
-    if (HAS_NEXT) issue_v(kt + 1, vb_nxt);
-    if (kt + 2 < nkt) issue_k(kt + 2, kb_cur);
+    constexpr int PH = decltype(phase)::value;
+    if (kt + A < nkt) issue_v(kt + A, D::V((PH + A) % NS));
+    if (kt + A + 1 < nkt) issue_k(kt + A + 1, D::K((PH + A + 1) % NS));
     const float nm = move_max(mt_cur, m, l, o);
     // ---- branch-free region
     if (HAS_NEXT) {
-      qk(nxt, kb_nxt);
+      qk(nxt, D::K((PH + 1) % NS));
       mask(nxt, kt + 1);
       mt_nxt = smax(nxt);
     }
-    exp_pv(cur, nm, vb_cur);
+    exp_pv(cur, nm, D::V(PH));
     // schedule: LDS operand reads run 4 MFMAs ahead; the VALU work is spread
     // evenly between all MFMAs of the region
     constexpr int kAhead = 4;
@@ -433,30 +462,70 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
       if (i + kAhead < nmfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, HAS_NEXT ? 4 : 6, 0);
     }
-    wait_loads_and_sync();
+    // loads issued by bodies kt + 2 - A .. kt may stay in flight
+    int later = 0;
+#pragma unroll
+    for (int j = 2 - A; j <= 0; ++j) later += loads_of(kt + j);
+    wait_vm_groups<LPW, 2 * (A - 1)>(later);
+    __syncthreads();
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  using std::integral_constant;
 
-  issue_k(0, Direct::K0);
-  if (nkt > 1) issue_k(1, Direct::K1);
-  issue_v(0, Direct::V0);
+  issue_k(0, D::K(0));
+  if (nkt > 1) issue_k(1, D::K(1));
+  issue_v(0, D::V(0));
   wait_loads_and_sync();
+  // the prologue's share: V^T tiles 1 .. A-1 and K tiles 2 .. A
+#pragma unroll
+  for (int i = 1; i < A; ++i) {
+    if (i < nkt) issue_v(i, D::V(i % NS));
+    if (i + 1 < nkt) issue_k(i + 1, D::K((i + 1) % NS));
+  }
   floatx16 sa[2], sb[2];
-  qk(sa, Direct::K0);
+  qk(sa, D::K(0));
   mask(sa, 0);
   float ma = smax(sa), mb = 0.f;
-  __syncthreads();  // every wave has read K buffer 0 before tile 2 refills it
+  // body 0 refills K buffer 0 when A + 1 == NS: every wave must have read it
+  if ((A + 1) % NS == 0) __syncthreads();
+  // even bodies hold the current tile's scores in sa, odd ones in sb
+  auto run = [&](auto has_next, auto phase, int kt) {
+    constexpr int PH = decltype(phase)::value;
+    if constexpr (PH % 2 == 0) body(has_next, phase, kt, sa, sb, ma, mb);
+    else body(has_next, phase, kt, sb, sa, mb, ma);
+  };
   int kt = 0;
-  for (; kt + 2 < nkt; kt += 2) {
-    body(T_{}, kt, sa, sb, ma, mb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
-    body(T_{}, kt + 1, sb, sa, mb, ma, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
+  for (; kt + NS < nkt; kt += NS) {
+    run(T_{}, integral_constant<int, 0>{}, kt);
+    run(T_{}, integral_constant<int, 1>{}, kt + 1);
+    if constexpr (NS > 2) {
+      run(T_{}, integral_constant<int, 2>{}, kt + 2);
+      run(T_{}, integral_constant<int, 3>{}, kt + 3);
+    }
   }
-  if (kt + 1 < nkt) {
-    body(T_{}, kt, sa, sb, ma, mb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
-    body(F_{}, kt + 1, sb, sa, mb, ma, Direct::K1, Direct::K0, Direct::V1, Direct::V0);
+  // 1 .. NS tiles left, kt % NS == 0
+  const int left = nkt - kt;
+  if constexpr (NS > 2) {
+    if (left == 4) {
+      run(T_{}, integral_constant<int, 0>{}, kt);
+      run(T_{}, integral_constant<int, 1>{}, kt + 1);
+      run(T_{}, integral_constant<int, 2>{}, kt + 2);
+      run(F_{}, integral_constant<int, 3>{}, kt + 3);
+      return;
+    }
+    if (left == 3) {
+      run(T_{}, integral_constant<int, 0>{}, kt);
+      run(T_{}, integral_constant<int, 1>{}, kt + 1);
+      run(F_{}, integral_constant<int, 2>{}, kt + 2);
+      return;
+    }
+  }
+  if (left == 2) {
+    run(T_{}, integral_constant<int, 0>{}, kt);
+    run(F_{}, integral_constant<int, 1>{}, kt + 1);
   } else {
-    body(F_{}, kt, sa, sb, ma, mb, Direct::K0, Direct::K1, Direct::V0, Direct::V1);
+    run(F_{}, integral_constant<int, 0>{}, kt);
   }
 }
 
@@ -510,7 +579,7 @@ __device__ __forceinline__ void tiles_staged(typename Pol::T *lds, const typenam
 template <class Pol> struct LdsBytes {
   static constexpr int value = 2 * (kKeyTile * Pol::KP + kHeadDim * Pol::VP) * (int)sizeof(typename Pol::T);
 };
-template <> struct LdsBytes<PolBf16> { static constexpr int value = Direct::BYTES; };
+template <> struct LdsBytes<PolBf16> { static constexpr int value = Direct<PolBf16::kStages>::BYTES; };
 
 template <class Pol, int MODE>
 __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const AttnArgs a) {
@@ -553,12 +622,24 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     vstep = kKeyTile;
     vstride = a.B;
   } else if (MODE == MODE_DIAG) {
+    // Work item w runs over (kv head of the pass, block, query tile with the
+    // most keys first, query head of the group). Workgroup i runs on XCD
+    // i % 8 and every XCD takes a contiguous run of w, so the tiles that read
+    // one block's keys and values run together and share that XCD's L2.
     const int nq = (a.B + ROWS - 1) / ROWS;
-    const int qt = nq - 1 - (int)(blockIdx.x / a.NBb);  // most keys first
-    const int64_t gb = blockIdx.x % a.NBb;
+    const uint32_t total = (uint32_t)(a.Hp * a.NBb * nq);
+    const uint32_t per = (total + 7) >> 3;
+    const uint32_t jj = blockIdx.x >> 3;
+    if (jj >= per) return;
+    const uint32_t wi = (blockIdx.x & 7) * per + jj;
+    if (wi >= total) return;
+    uint32_t rest = wi / (uint32_t)a.G;
+    const int qt = nq - 1 - (int)(rest % (uint32_t)nq);
+    rest /= (uint32_t)nq;
+    const int64_t gb = rest % (uint32_t)a.NBb;
+    const int hl = (int)(rest / (uint32_t)a.NBb) * a.G + (int)(wi % (uint32_t)a.G);
     const int4 bi = a.info[gb];
     if (bi.x < 0 || qt * ROWS >= bi.z) return;
-    const int hl = blockIdx.y;
     hq = a.h0 + hl;
     g = hq / a.G;
     nrows = min(ROWS, bi.z - qt * ROWS);
@@ -608,7 +689,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   const T *ktile = kbase + kbeg * kstride;
   const int64_t rows_after = a.T - kbeg;  // K rows from kbeg to the end of the tensor
   if constexpr (std::is_same<Pol, PolBf16>::value)
-    tiles_direct<MODE, Pol::kThreads / 64>(lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride,
+    tiles_direct<MODE, Pol::kThreads / 64, Pol::kStages, Pol::kLoadAhead>(lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride,
                        nkt, qr, qfirst, qpos, a.scale_log2, o, m, l);
   else
     tiles_staged<Pol, MODE>((T *)lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep,
@@ -667,8 +748,9 @@ hipError_t launch_mode(bool bf16, dim3 grid, const AttnArgs &a, hipStream_t s) {
 hipError_t launch_attn_diag(const Problem &pb, const Work &w, const void *q, const void *k, int g0,
                             hipStream_t s) {
   const AttnArgs a = base_args(pb, w, q, k, g0);
-  const int nq = (pb.B + pb.rows - 1) / pb.rows;
-  return launch_mode<MODE_DIAG>(pb.bf16, dim3((unsigned)(pb.NBb * nq), (unsigned)pb.Hp), a, s);
+  const int64_t nq = (pb.B + pb.rows - 1) / pb.rows;
+  const int64_t grid = (pb.Hp * pb.NBb * nq + 7) / 8 * 8;
+  return launch_mode<MODE_DIAG>(pb.bf16, dim3((unsigned)grid), a, s);
 }
 
 hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, const void *k, int g0,
