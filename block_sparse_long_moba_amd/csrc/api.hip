@@ -87,6 +87,16 @@ size_t cu_copy_offset(int S) { return sizeof(int32_t) * (S + 1); }
 size_t info_offset(int S) { return (2 * sizeof(int32_t) * (S + 1) + 15) / 16 * 16; }
 size_t table_bytes(int S, int64_t NBb) { return info_offset(S) + 16 * (size_t)NBb; }
 
+// Bins region: count[nbins], offset[nbins+1], tile_offset[nbins+1],
+// cursor[nbins], work counters[kWorkCounters] (uint32), then (16-byte
+// aligned) int4 tile records.
+size_t tile_rec_offset(int64_t nbins) {
+  return (sizeof(uint32_t) * (size_t)(4 * nbins + 2 + kWorkCounters) + 15) / 16 * 16;
+}
+size_t bins_bytes(int64_t nbins, int64_t max_tiles) {
+  return tile_rec_offset(nbins) + 16 * (size_t)max_tiles;
+}
+
 int largest_divisor_at_most(int n, int cap) {
   for (int d = std::min(n, cap); d >= 1; --d)
     if (n % d == 0) return d;
@@ -132,7 +142,7 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   L->kbar_offset = off;      off = align_up(off + (sizeof(float) + 4) * (size_t)NBb * Hkv * kHeadDim);
   L->vt_offset = off;        off = align_up(off + es * (size_t)P * NBb * kHeadDim * B);
   L->idx_offset = off;       off = align_up(off + sizeof(int32_t) * (size_t)slots);
-  L->bins_offset = off;      off = align_up(off + sizeof(uint32_t) * (size_t)(4 * nbins + 2 + max_tiles));
+  L->bins_offset = off;      off = align_up(off + bins_bytes(nbins, max_tiles));
   L->items_offset = off;     off = align_up(off + sizeof(uint32_t) * (size_t)std::max<int64_t>(1, hist_items));
   L->part_o_offset = off;    off = align_up(off + es * (size_t)slots * kHeadDim);
   L->part_lse_offset = off;  off = align_up(off + sizeof(float) * (size_t)slots);
@@ -177,7 +187,8 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.bin_off = bins + nbins;
   w.tile_off = bins + 2 * nbins + 1;
   w.cursor = bins + 3 * nbins + 2;
-  w.tile_bin = bins + 4 * nbins + 2;
+  w.work = bins + 4 * nbins + 2;
+  w.tile_rec = (int4 *)((char *)bins + tile_rec_offset(nbins));
   w.items = (uint32_t *)(b + L->items_offset);
   w.part_o = b + L->part_o_offset;
   w.part_lse = (float *)(b + L->part_lse_offset);

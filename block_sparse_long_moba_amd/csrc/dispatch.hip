@@ -137,10 +137,13 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const uint32_t *__r
   }
 }
 
-// tile_bin[i] = bin owning attention tile i (largest b with tile_off[b] <= i).
-__global__ __launch_bounds__(256) void tile_bin_kernel(const uint32_t *__restrict__ tile_off,
+// Record of attention tile i: {first item, rows, bin, first token of the
+// bin's block}, for the bin b owning the tile (largest b with tile_off[b] <= i).
+__global__ __launch_bounds__(256) void tile_rec_kernel(const uint32_t *__restrict__ tile_off,
+                                                       const uint32_t *__restrict__ bin_off,
+                                                       const int4 *__restrict__ info, int64_t NBb,
                                                        int64_t nbins, int64_t max_tiles,
-                                                       uint32_t *__restrict__ tile_bin) {
+                                                       uint32_t rows, int4 *__restrict__ tile_rec) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= max_tiles || i >= tile_off[nbins]) return;
   int64_t lo = 0, hi = nbins - 1;
@@ -148,7 +151,9 @@ __global__ __launch_bounds__(256) void tile_bin_kernel(const uint32_t *__restric
     const int64_t mid = (lo + hi + 1) >> 1;
     if (tile_off[mid] <= i) lo = mid; else hi = mid - 1;
   }
-  tile_bin[i] = (uint32_t)lo;
+  const uint32_t r0 = bin_off[lo] + (uint32_t)(i - tile_off[lo]) * rows;
+  const uint32_t n = min(rows, bin_off[lo + 1] - r0);
+  tile_rec[i] = make_int4((int)r0, (int)n, (int)lo, info[lo % NBb].y);
 }
 
 }  // namespace
@@ -164,8 +169,9 @@ hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s) {
   dispatch_scan_kernel<<<1, 1024, 0, s>>>(w.bin_count, nbins, (uint32_t)pb.rows, w.bin_off,
                                           w.tile_off, w.cursor);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  tile_bin_kernel<<<dim3((unsigned)((w.max_tiles + 255) / 256)), 256, 0, s>>>(
-      w.tile_off, nbins, w.max_tiles, w.tile_bin);
+  tile_rec_kernel<<<dim3((unsigned)((w.max_tiles + 255) / 256)), 256, 0, s>>>(
+      w.tile_off, w.bin_off, w.blk_info, pb.NBb, nbins, w.max_tiles, (uint32_t)pb.rows,
+      w.tile_rec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dispatch_kernel<true><<<grid, 256, 0, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k,
                                              w.bin_count, w.bin_off, w.cursor, w.items);

@@ -17,6 +17,7 @@ inline int attn_rows(int bf16) { return bf16 ? kRowsBf16 : kRowsF32; }
 constexpr int kGateTokens = 64;     // tokens per gate workgroup (one wave per query head)
 constexpr int kDispatchTokens = 64; // tokens per dispatch workgroup
 constexpr int kMaxHistPick = 32;    // largest topk-1 kept in registers by the gate
+constexpr int kWorkCounters = 8;    // one per XCD
 constexpr int kLdsBins = 16384;     // LDS histogram bins of the dispatch stage (64 KiB)
 
 // Everything a launcher needs to know about one call.
@@ -47,7 +48,8 @@ struct Work {
   uint32_t *bin_off;    // [P*NBb + 1]
   uint32_t *tile_off;   // [P*NBb + 1]
   uint32_t *cursor;     // [P*NBb]
-  uint32_t *tile_bin;   // [max tiles]
+  uint32_t *work;       // [kWorkCounters] tile counters of the persistent attention (per XCD)
+  int4 *tile_rec;       // [max tiles] {first item, rows, bin, first token of the block}
   uint32_t *items;      // [T*Hp*(k-1)]
   void *part_o;         // [T*Hp*k][d], element type of the inputs
   float *part_lse;      // [T*Hp*k]

@@ -114,10 +114,13 @@ typedef struct moba_layout {
   /* int32 idx[T][Hp][topk]: chosen local block ids of the pass's query heads,
    * ascending, -1 padded; the last valid entry is the query's own block. */
   size_t idx_offset;
-  /* uint32 dispatch tables over bins b = p*NBb + global_block (p < P):
-   * count[P*NBb], offset[P*NBb+1], tile_offset[P*NBb+1] (128-row tiles),
-   * cursor[P*NBb], tile_bin[max_tiles] (bin of every tile), where
-   * max_tiles = ceil(T*Hp*(topk-1)/128) + P*NBb. */
+  /* dispatch tables over bins b = p*NBb + global_block (p < P), uint32:
+   * count[P*NBb], offset[P*NBb+1], tile_offset[P*NBb+1] (tiles of the
+   * attention kernel's query rows: 256 for bf16, 128 for float32),
+   * cursor[P*NBb], 8 tile counters of the earlier-block attention; then,
+   * 16-byte aligned, int32x4 tile records
+   * [max_tiles] = {first item, rows, bin, first token of the bin's block},
+   * where max_tiles = ceil(T*Hp*(topk-1)/128) + P*NBb bounds the tile count. */
   size_t bins_offset;
   /* uint32 items[T*Hp*(topk-1)]: per bin, the slots (t*Hp + hl)*topk + s that
    * chose the bin's block as an earlier block (order inside a bin unspecified). */
