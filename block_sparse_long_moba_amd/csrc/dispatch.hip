@@ -6,9 +6,10 @@
 // handled separately (causal, contiguous) and is not dispatched.
 //
 // Bins are (kv head of the pass p, global block gb) -> p*NBb + gb. Three
-// passes: per-workgroup LDS histograms added into global counts, one exclusive
-// scan (items and 128-row tiles), and a scatter that reserves a range per
-// (workgroup, bin) and fills it from LDS cursors. Item order inside a bin is
+// passes: per-workgroup LDS histograms added into global counts, one
+// exclusive scan (items, and tiles of the attention kernel's query rows), and
+// a scatter that reserves a range per (workgroup, bin) and fills it from LDS
+// cursors; a record per tile follows the scan. Item order inside a bin is
 // unspecified; every consumer treats a bin's items independently.
 #include "moba_internal.h"
 
