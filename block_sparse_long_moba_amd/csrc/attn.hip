@@ -410,7 +410,8 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
     }
   };
   // exp2 of one tile's scores, chunk by chunk straight into the P V product;
-  // the row sum adds the fp32 probabilities (lse keeps fp32 accuracy).
+  // the row sum adds the fp32 probabilities (lse keeps fp32 accuracy), as a
+  // tree per chunk of 8.
   auto exp_pv = [&](const floatx16 (&sc)[2], float nm, int vbuf) {
     float rs = 0.f;
 #pragma unroll
@@ -418,12 +419,13 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 b;
+        float pj[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float pj = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * c + j], c2, nm));
-          rs += pj;
-          b[j] = (__bf16)pj;
+          pj[j] = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * c + j], c2, nm));
+          b[j] = (__bf16)pj[j];
         }
+        rs += ((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7]));
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const bf16x8 av = *(const bf16x8 *)(lds + vbuf + dt * 4096 + vrd[2 * st + c]);
@@ -431,6 +433,9 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
         }
       }
     l += rs;
+    // l is next needed in the next body; keep its sum in this body, among
+    // the MFMAs (it would otherwise be sunk past the workgroup barrier)
+    asm volatile("" : "+v"(l));
   };
   auto mask = [&](floatx16 (&sc)[2], int kt) {
     if (CAUSAL && kt * kKeyTile + kKeyTile - 1 > qfirst) {
