@@ -203,8 +203,14 @@ def main():
     nb = sum(-(-L // B) for L in w.lengths)
     mp_bytes = T * Hkv * HEAD_DIM * es + nb * Hkv * HEAD_DIM * 4
     gate_bytes = T * Hq * HEAD_DIM * es + T * Hq * k * 4
+    # dispatch: idx read by the count and the scatter pass, items written
+    n_hist = sum(hist_rows)
+    disp_bytes = 2 * T * Hq * k * 4 + n_hist * 4
+    # merge: every valid slot's partial (row and lse) read, out and lse written
+    merge_bytes = (n_hist + T * Hq) * (HEAD_DIM * es + 4) + T * Hq * (HEAD_DIM * es + 4)
     hbm = {}
-    for name, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes)):
+    for name, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes), ("dispatch", disp_bytes),
+                         ("merge", merge_bytes)):
         sm = stages[name][0]
         hbm[name] = {"ms": round(sm, 4), "GB/s": round(nbytes / (sm * 1e-3) / 1e9, 1),
                      "frac": round(nbytes / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}

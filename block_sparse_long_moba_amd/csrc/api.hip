@@ -139,7 +139,7 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   L->max_blocks_per_seq = (int32_t)maxblk;
   size_t off = 0;
   L->table_offset = off;     off = align_up(off + table_bytes(S, NBb));
-  L->kbar_offset = off;      off = align_up(off + (sizeof(float) + 4) * (size_t)NBb * Hkv * kHeadDim);
+  L->kbar_offset = off;      off = align_up(off + 3 * (sizeof(float) + 4) * (size_t)NBb * Hkv * kHeadDim);
   L->vt_offset = off;        off = align_up(off + es * (size_t)P * NBb * kHeadDim * B);
   L->idx_offset = off;       off = align_up(off + sizeof(int32_t) * (size_t)slots);
   L->bins_offset = off;      off = align_up(off + bins_bytes(nbins, max_tiles));
@@ -178,7 +178,12 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.cu = (int32_t *)(b + L->table_offset + cu_copy_offset(pb.S));
   w.blk_info = (int4 *)(b + L->table_offset + info_offset(pb.S));
   w.kbar = (float *)(b + L->kbar_offset);
-  w.kbar_split = (__bf16 *)(w.kbar + (size_t)pb.NBb * pb.Hkv * kHeadDim);
+  const size_t nkb = (size_t)pb.NBb * pb.Hkv * kHeadDim;
+  w.kbar_split = (__bf16 *)(w.kbar + nkb);
+  w.kmax = (float *)(w.kbar_split + 2 * nkb);
+  w.kmax_split = (__bf16 *)(w.kmax + nkb);
+  w.kmin = (float *)(w.kmax_split + 2 * nkb);
+  w.kmin_split = (__bf16 *)(w.kmin + nkb);
   w.vt = b + L->vt_offset;
   w.idx = (int32_t *)(b + L->idx_offset);
   const int64_t nbins = (int64_t)pb.P * pb.NBb;
@@ -217,8 +222,14 @@ moba_status_t check_pass(const moba_shape_t *sh, const moba_layout_t *L, int32_t
 }
 
 moba_status_t run_pass(const Problem &pb, const Work &w, const void *q, const void *k,
-                       const void *v, int g0, void *out, float *lse, hipStream_t s) {
-  MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
+                       const void *v, int g0, void *out, float *lse, hipStream_t s,
+                       const moba_gate_t &gate) {
+  if (gate.kind == MOBA_GATE_WINDOW)
+    MOBA_HIP(launch_gate_window(pb, w, gate.n_sink, s), "gate_window");
+  else if (gate.kind == MOBA_GATE_POOLED)
+    MOBA_HIP(launch_gate_pooled(pb, w, q, g0, gate.extra_max, gate.extra_min, s), "gate_pooled");
+  else
+    MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
   MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
   MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
            "vtrans");
@@ -226,6 +237,28 @@ moba_status_t run_pass(const Problem &pb, const Work &w, const void *q, const vo
   MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
   MOBA_HIP(launch_merge(pb, w, g0, out, lse, s), "merge");
   return MOBA_SUCCESS;
+}
+
+moba_status_t check_gate(const moba_gate_t *g, int32_t topk) {
+  if (!g) return fail(MOBA_ERROR_INVALID_VALUE, "gate is NULL");
+  switch (g->kind) {
+    case MOBA_GATE_MEAN: return MOBA_SUCCESS;
+    case MOBA_GATE_WINDOW:
+      if (g->n_sink < 0 || g->n_sink >= topk)
+        return fail(MOBA_ERROR_INVALID_VALUE, "n_sink %d must lie in [0, topk)", g->n_sink);
+      return MOBA_SUCCESS;
+    case MOBA_GATE_POOLED:
+      if (g->extra_max < 0 || g->extra_min < 0)
+        return fail(MOBA_ERROR_INVALID_VALUE, "extra_max / extra_min must be >= 0");
+      if (g->extra_max > kMaxExtraPick || g->extra_min > kMaxExtraPick)
+        return fail(MOBA_ERROR_UNSUPPORTED, "extra_max / extra_min: at most %d", kMaxExtraPick);
+      if (topk - g->extra_max - g->extra_min < 1)
+        return fail(MOBA_ERROR_INVALID_VALUE,
+                    "topk %d must exceed extra_max + extra_min (%d); the own block needs a slot",
+                    topk, g->extra_max + g->extra_min);
+      return MOBA_SUCCESS;
+  }
+  return fail(MOBA_ERROR_INVALID_VALUE, "unknown gate kind %d", (int)g->kind);
 }
 
 moba_status_t check_io(const void *q, const void *k, const void *v, const int32_t *cu,
@@ -341,6 +374,50 @@ moba_status_t moba_gate(const void *q, const moba_shape_t *sh, int32_t B, int32_
   return MOBA_SUCCESS;
 }
 
+moba_status_t moba_minmaxpool(const void *k, const moba_shape_t *sh, int32_t B,
+                              const moba_layout_t *L, void *ws, hipStream_t s) {
+  moba_status_t st = check_table_stage(sh, B, L, ws);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if (!k) return fail(MOBA_ERROR_INVALID_VALUE, "k is NULL");
+  Problem pb = make_problem(sh, B, 1, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_minmaxpool(pb, w, k, s), "minmaxpool");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_gate_window(const moba_shape_t *sh, int32_t B, int32_t k, int32_t n_sink,
+                               const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  const moba_gate_t gate{MOBA_GATE_WINDOW, n_sink, 0, 0};
+  if ((st = check_gate(&gate, k)) != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  Problem pb = make_problem(sh, B, k, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_gate_window(pb, w, n_sink, s), "gate_window");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_gate_pooled(const void *q, const moba_shape_t *sh, int32_t B, int32_t k,
+                               int32_t extra_max, int32_t extra_min, const moba_layout_t *L,
+                               void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  const moba_gate_t gate{MOBA_GATE_POOLED, 0, extra_max, extra_min};
+  if ((st = check_gate(&gate, k)) != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q) return fail(MOBA_ERROR_INVALID_VALUE, "q is NULL");
+  Problem pb = make_problem(sh, B, k, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_gate_pooled(pb, w, q, g0, extra_max, extra_min, s), "gate_pooled");
+  return MOBA_SUCCESS;
+}
+
 moba_status_t moba_dispatch(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L,
                             void *ws, int32_t g0, hipStream_t s) {
   moba_layout_t f;
@@ -421,11 +498,13 @@ moba_status_t moba_merge(const moba_shape_t *sh, int32_t B, int32_t k, const mob
   return MOBA_SUCCESS;
 }
 
-moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int32_t *cu,
-                          const moba_shape_t *sh, int32_t B, int32_t topk, float scale,
-                          void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v, const int32_t *cu,
+                             const moba_shape_t *sh, int32_t B, int32_t topk,
+                             const moba_gate_t *gate, float scale, void *out, float *lse,
+                             void *ws, size_t ws_bytes, hipStream_t s) {
   moba_status_t st = check_moba_args(sh, B, topk);
   if (st != MOBA_SUCCESS) return st;
+  if ((st = check_gate(gate, topk)) != MOBA_SUCCESS) return st;
   if ((st = check_io(q, k, v, cu, out, sh)) != MOBA_SUCCESS) return st;
   if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
   moba_layout_t L;
@@ -442,10 +521,18 @@ moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int
   Problem pb = make_problem(sh, B, topk, scale, &L);
   Work w = carve(pb, &L, ws);
   MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
-  MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
+  if (gate->kind != MOBA_GATE_WINDOW) MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
+  if (gate->kind == MOBA_GATE_POOLED) MOBA_HIP(launch_minmaxpool(pb, w, k, s), "minmaxpool");
   for (int g0 = 0; g0 < pb.Hkv; g0 += pb.P)
-    if ((st = run_pass(pb, w, q, k, v, g0, out, lse, s)) != MOBA_SUCCESS) return st;
+    if ((st = run_pass(pb, w, q, k, v, g0, out, lse, s, *gate)) != MOBA_SUCCESS) return st;
   return MOBA_SUCCESS;
+}
+
+moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int32_t *cu,
+                          const moba_shape_t *sh, int32_t B, int32_t topk, float scale,
+                          void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+  const moba_gate_t mean{MOBA_GATE_MEAN, 0, 0, 0};
+  return moba_fwd_gated(q, k, v, cu, sh, B, topk, &mean, scale, out, lse, ws, ws_bytes, s);
 }
 
 moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_t *cu,

@@ -328,6 +328,112 @@ hipError_t launch_gate_t(const Problem &pb, const Work &w, const T *q, int g0, h
 
 }  // namespace
 
+// ---- Fixed gates (MoBA summary page, section 3.4 "Context Partitioning": a
+// sliding window is a gate that always picks the most recent blocks, an
+// attention sink one that picks the initial and the recent blocks). Slots of
+// (row, query head): the n_sink initial blocks and the k - n_sink most recent
+// blocks up to the own block, ascending; rows with at most k blocks so far
+// take all of them. Every head gets the same selection.
+__global__ __launch_bounds__(256) void gate_window_kernel(const int32_t *__restrict__ cu, int S,
+                                                          int64_t T, int B, int Hp, int k,
+                                                          int n_sink, int32_t *__restrict__ idx) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (t, hl)
+  if (row >= T * Hp) return;
+  const int64_t t = row / Hp;
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int c = (int)((t - cu[lo]) / B);
+  const int w = k - n_sink;
+  int32_t *dst = idx + row * k;
+  int n = 0;
+  for (int j = 0; j <= c && n < k; ++j)
+    if (j < n_sink || j > c - w) dst[n++] = j;
+  for (; n < k; ++n) dst[n] = -1;
+}
+
+// ---- Pooled-key gate (MoBA review page, authors' rebuttals on mean pooling
+// and on QUEST): on top of the mean-pooled top-k, the best blocks by
+// max-pooled and by min-pooled keys are selected too. The three rankings run
+// through the ordinary gate kernels (same scores, order and tie rule) into
+// scratch lists; this kernel forms their union per (row, query head) in the
+// k slots: earlier blocks ascending, -1 for slots left empty by coinciding
+// picks (their partial lse is set to -inf so the merge skips them), the own
+// block at position min(k, c + 1) - 1, then -1.
+__global__ __launch_bounds__(256) void gate_union_kernel(
+    const int32_t *__restrict__ lm, int km, const int32_t *__restrict__ lx, int kx,
+    const int32_t *__restrict__ ln, int kn, const int32_t *__restrict__ cu, int S, int64_t T,
+    int B, int Hp, int k, int32_t *__restrict__ idx, float *__restrict__ part_lse) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= T * Hp) return;
+  const int64_t t = row / Hp;
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int c = (int)((t - cu[lo]) / B);
+  const int32_t *a = lm + row * km, *b = lx + row * kx, *d = ln + row * kn;
+  int ia = 0, ib = 0, id = 0;
+  const int nsel = min(k, c + 1);
+  int32_t *dst = idx + row * k;
+  float *pl = part_lse + row * k;
+  int n = 0;
+  // three ascending lists of earlier blocks (each ends at its own-block entry
+  // or a -1): merge without duplicates
+  for (;;) {
+    const int va = ia < km && a[ia] >= 0 && a[ia] < c ? a[ia] : INT_MAX;
+    const int vb = ib < kx && b[ib] >= 0 && b[ib] < c ? b[ib] : INT_MAX;
+    const int vd = id < kn && d[id] >= 0 && d[id] < c ? d[id] : INT_MAX;
+    const int v = min(va, min(vb, vd));
+    if (v == INT_MAX || n >= nsel - 1) break;
+    dst[n++] = v;
+    ia += va == v; ib += vb == v; id += vd == v;
+  }
+  for (; n < nsel - 1; ++n) { dst[n] = -1; pl[n] = -INFINITY; }
+  dst[n++] = c;
+  for (; n < k; ++n) dst[n] = -1;
+}
+
+hipError_t launch_gate_window(const Problem &pb, const Work &w, int n_sink, hipStream_t s) {
+  const int64_t rows = pb.T * pb.Hp;
+  if (rows == 0) return hipSuccess;
+  gate_window_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(
+      w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, n_sink, w.idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, int g0,
+                              int extra_max, int extra_min, hipStream_t s) {
+  const int64_t rows = pb.T * pb.Hp;
+  if (rows == 0) return hipSuccess;
+  // scratch lists in the partial-output region (unused until the attention);
+  // a ranking with nothing to pick gets no list (length 0)
+  const int pm = pb.k - extra_max - extra_min - 1;
+  const int km = pm > 0 ? pm + 1 : 0, kx = extra_max > 0 ? extra_max + 1 : 0,
+            kn = extra_min > 0 ? extra_min + 1 : 0;
+  int32_t *lm = (int32_t *)w.part_o, *lx = lm + rows * km, *ln = lx + rows * kx;
+  struct Ranking { float *f; __bf16 *split; int32_t *list; int k; };
+  const Ranking rk[3] = {{w.kbar, w.kbar_split, lm, km}, {w.kmax, w.kmax_split, lx, kx},
+                         {w.kmin, w.kmin_split, ln, kn}};
+  for (const Ranking &r : rk) {
+    if (r.k == 0) continue;
+    Problem p2 = pb;
+    p2.k = r.k;
+    Work w2 = w;
+    w2.kbar = r.f;
+    w2.kbar_split = r.split;
+    w2.idx = r.list;
+    hipError_t e = launch_gate(p2, w2, q, g0, s);
+    if (e != hipSuccess) return e;
+  }
+  gate_union_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(
+      lm, km, lx, kx, ln, kn, w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, w.idx, w.part_lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s) {
   // matrix-core gate: bf16, groups of a multiple of 4 heads, at most 4096
   // blocks per sequence (12 index bits keep 20 score bits in the keys)

@@ -18,6 +18,7 @@ constexpr int kGateTokens = 64;     // tokens per gate workgroup (one wave per q
 constexpr int kDispatchTokens = 64; // tokens per dispatch workgroup
 constexpr int kMaxHistPick = 32;    // largest topk-1 kept in registers by the gate
 constexpr int kWorkCounters = 8;    // one per XCD
+constexpr int kMaxExtraPick = 16;   // pooled gate: extra blocks per max / min ranking
 constexpr int kLdsBins = 16384;     // LDS histogram bins of the dispatch stage (64 KiB)
 
 // Everything a launcher needs to know about one call.
@@ -42,6 +43,8 @@ struct Work {
   int4 *blk_info;       // [NBb] {seq, first row, rows, local block}
   float *kbar;          // [NBb][Hkv][d]
   __bf16 *kbar_split;   // [NBb][Hkv][2][d]: bf16 hi and lo parts, kbar ~= hi + lo
+  float *kmax, *kmin;   // [NBb][Hkv][d] max- and min-pooled keys
+  __bf16 *kmax_split, *kmin_split;  // [NBb][Hkv][2][d] their bf16 hi and lo parts
   void *vt;             // [P][NBb][d][B]
   int32_t *idx;         // [T][Hp][k]
   uint32_t *bin_count;  // [P*NBb]
@@ -61,7 +64,11 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s
 hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t NBb, int32_t *blk_first,
                            int32_t *cu_copy, int4 *blk_info, hipStream_t s);
 hipError_t launch_meanpool(const Problem &pb, const Work &w, const void *k, hipStream_t s);
+hipError_t launch_minmaxpool(const Problem &pb, const Work &w, const void *k, hipStream_t s);
 hipError_t launch_gate(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s);
+hipError_t launch_gate_window(const Problem &pb, const Work &w, int n_sink, hipStream_t s);
+hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, int g0,
+                              int extra_max, int extra_min, hipStream_t s);
 hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s);
 hipError_t launch_vtrans(const void *v, int bf16, int64_t T, int Hkv, int g0, int P,
                          int64_t NBb, int B, const int4 *blk_info, void *vt, hipStream_t s);

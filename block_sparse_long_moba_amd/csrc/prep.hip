@@ -166,6 +166,55 @@ __global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
   }
 }
 
+// kmax / kmin[gb][g][:] = elementwise max / min of the block's key rows, the
+// block representations of the extra picks by max and min pooling (MoBA
+// review page, authors' rebuttals on mean pooling and on QUEST). Same
+// workgroup shape as the mean; max and min are exact, and the bf16 hi / lo
+// splits serve the matrix-core gate as for the mean.
+template <typename T>
+__global__ __launch_bounds__(256) void minmaxpool_kernel(const T *__restrict__ k,
+                                                         const int4 *__restrict__ info, int Hkv,
+                                                         float *__restrict__ kmax,
+                                                         float *__restrict__ kmin,
+                                                         __bf16 *__restrict__ kmax_split,
+                                                         __bf16 *__restrict__ kmin_split) {
+  constexpr int N = Vec16<T>::N;
+  constexpr int COLS = kHeadDim / N;
+  constexpr int RG = 256 / COLS;
+  const int gb = blockIdx.x, g = blockIdx.y;
+  const int4 bi = info[gb];
+  if (bi.x < 0) return;
+  const int col = threadIdx.x % COLS, rg = threadIdx.x / COLS;
+  float mx[N], mn[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) { mx[i] = -INFINITY; mn[i] = INFINITY; }
+  const int64_t stride = (int64_t)Hkv * kHeadDim;
+  const T *base = k + ((int64_t)bi.y * Hkv + g) * kHeadDim + col * N;
+  for (int r = rg; r < bi.z; r += RG) {
+    float f[N];
+    Vec16<T>::load(base + (int64_t)r * stride, f);
+#pragma unroll
+    for (int i = 0; i < N; ++i) { mx[i] = fmaxf(mx[i], f[i]); mn[i] = fminf(mn[i], f[i]); }
+  }
+  __shared__ float red[2][RG][kHeadDim];
+#pragma unroll
+  for (int i = 0; i < N; ++i) { red[0][rg][col * N + i] = mx[i]; red[1][rg][col * N + i] = mn[i]; }
+  __syncthreads();
+  if (threadIdx.x < 2 * kHeadDim) {
+    const int which = threadIdx.x / kHeadDim, e = threadIdx.x % kHeadDim;
+    float v = red[which][0][e];
+#pragma unroll
+    for (int i = 1; i < RG; ++i) v = which ? fminf(v, red[1][i][e]) : fmaxf(v, red[0][i][e]);
+    const int64_t o = ((int64_t)gb * Hkv + g) * kHeadDim;
+    (which ? kmin : kmax)[o + e] = v;
+    const __bf16 hi = (__bf16)v;
+    const __bf16 lo = (__bf16)(v - (float)hi);
+    __bf16 *sp = (which ? kmin_split : kmax_split) + 2 * o + e;
+    sp[0] = hi;
+    sp[kHeadDim] = lo;
+  }
+}
+
 // vt[p][gb][e][j] = v[first row of gb + j][g0 + p][e], zero past the block's
 // rows: each block's values transposed so the attention kernels can feed them
 // to the matrix cores with keys along the contraction. One 64-key tile per
@@ -243,11 +292,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
   const int s = seq_of_row(cu, S, t);
   const int c = (int)((t - cu[s]) / B);
   const int nsel = min(k, c + 1);
+  // a slot whose lse is -inf holds no block (a gate that picked fewer blocks
+  // than it had slots) and is skipped
   const float *pl = part_lse + row * k;
   float m = -INFINITY;
   for (int i = 0; i < nsel; ++i) m = fmaxf(m, pl[i]);
   float sum = 0.f;
-  for (int i = 0; i < nsel; ++i) sum += __builtin_amdgcn_exp2f((pl[i] - m) * kLog2eF);
+  for (int i = 0; i < nsel; ++i)
+    if (pl[i] > -INFINITY) sum += __builtin_amdgcn_exp2f((pl[i] - m) * kLog2eF);
   const float L = m + logf(sum);
   float acc[N];
 #pragma unroll
@@ -258,10 +310,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       raw[u] = i0 + u < nsel ? *(const uint4 *)(po + (int64_t)(i0 + u) * kHeadDim)
-                             : make_uint4(0, 0, 0, 0);
+                             : make_uint4(0, 0, 0, 0);  // in bounds; an empty slot's bytes are ignored
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (i0 + u >= nsel) break;
+      if (!(pl[i0 + u] > -INFINITY)) continue;
       const float wgt = __builtin_amdgcn_exp2f((pl[i0 + u] - L) * kLog2eF);
       const TO *v = (const TO *)&raw[u];
 #pragma unroll
@@ -301,6 +354,17 @@ hipError_t launch_meanpool(const Problem &pb, const Work &w, const void *k, hipS
   else
     meanpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kbar,
                                                  w.kbar_split);
+  return hipGetLastError();
+}
+
+hipError_t launch_minmaxpool(const Problem &pb, const Work &w, const void *k, hipStream_t s) {
+  dim3 grid((unsigned)pb.NBb, (unsigned)pb.Hkv);
+  if (pb.bf16)
+    minmaxpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, w.blk_info, pb.Hkv, w.kmax,
+                                                    w.kmin, w.kmax_split, w.kmin_split);
+  else
+    minmaxpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kmax,
+                                                   w.kmin, w.kmax_split, w.kmin_split);
   return hipGetLastError();
 }
 

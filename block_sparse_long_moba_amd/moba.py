@@ -19,9 +19,12 @@ STATUS = {0: "MOBA_SUCCESS", 1: "MOBA_ERROR_INVALID_VALUE", 2: "MOBA_ERROR_UNSUP
 
 # Every entry point include/moba.h declares.
 EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_workspace_size",
-           "moba_seqtable", "moba_meanpool", "moba_gate", "moba_dispatch", "moba_attn_fwd",
-           "moba_attn_fwd_diag", "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd", "moba_dense_causal_workspace_size",
-           "moba_dense_causal_fwd"]
+           "moba_seqtable", "moba_meanpool", "moba_gate", "moba_minmaxpool", "moba_gate_window",
+           "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
+           "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
+           "moba_dense_causal_workspace_size", "moba_dense_causal_fwd"]
+
+GATE_MEAN, GATE_WINDOW, GATE_POOLED = 0, 1, 2
 
 
 class MobaError(RuntimeError):
@@ -35,6 +38,23 @@ class Shape(ctypes.Structure):
                 ("max_seqlen", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32)]
+
+
+class Gate(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("extra_max", ctypes.c_int32), ("extra_min", ctypes.c_int32)]
+
+
+def gate_mean() -> Gate:
+    return Gate(GATE_MEAN, 0, 0, 0)
+
+
+def gate_window(n_sink=0) -> Gate:
+    return Gate(GATE_WINDOW, int(n_sink), 0, 0)
+
+
+def gate_pooled(extra_max=1, extra_min=1) -> Gate:
+    return Gate(GATE_POOLED, 0, int(extra_max), int(extra_min))
 
 
 class Layout(ctypes.Structure):
@@ -70,12 +90,17 @@ def lib():
             "moba_seqtable": ([P, S, I32, LP, P, P], I32),
             "moba_meanpool": ([P, S, I32, LP, P, P], I32),
             "moba_gate": ([P, S, I32, I32, LP, P, I32, P], I32),
+            "moba_minmaxpool": ([P, S, I32, LP, P, P], I32),
+            "moba_gate_window": ([S, I32, I32, I32, LP, P, I32, P], I32),
+            "moba_gate_pooled": ([P, S, I32, I32, I32, I32, LP, P, I32, P], I32),
             "moba_dispatch": ([S, I32, I32, LP, P, I32, P], I32),
             "moba_attn_fwd": ([P, P, P, S, I32, I32, F, LP, P, I32, P], I32),
             "moba_attn_fwd_diag": ([P, P, P, S, I32, I32, F, LP, P, I32, P], I32),
             "moba_attn_fwd_hist": ([P, P, S, I32, I32, F, LP, P, I32, P], I32),
             "moba_merge": ([S, I32, I32, LP, P, I32, P, P, P], I32),
             "moba_fwd_ex": ([P, P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
+            "moba_fwd_gated": ([P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, Z,
+                                P], I32),
             "moba_fwd": ([P, P, P, P, S, I32, I32, P, P, P], I32),
             "moba_dense_causal_workspace_size": ([S], Z),
             "moba_dense_causal_fwd": ([P, P, P, P, S, F, P, P, P, Z, P], I32),
@@ -143,6 +168,25 @@ def moba_gate(q, shape, block_size, topk, layout, workspace, kv_head_begin=0, st
                            _ptr(workspace), kv_head_begin, _stream(stream)))
 
 
+def moba_minmaxpool(k, shape, block_size, layout, workspace, stream=None):
+    _check(lib().moba_minmaxpool(_ptr(k), ctypes.byref(shape), block_size, ctypes.byref(layout),
+                                 _ptr(workspace), _stream(stream)))
+
+
+def moba_gate_window(shape, block_size, topk, n_sink, layout, workspace, kv_head_begin=0,
+                     stream=None):
+    _check(lib().moba_gate_window(ctypes.byref(shape), block_size, topk, n_sink,
+                                  ctypes.byref(layout), _ptr(workspace), kv_head_begin,
+                                  _stream(stream)))
+
+
+def moba_gate_pooled(q, shape, block_size, topk, extra_max, extra_min, layout, workspace,
+                     kv_head_begin=0, stream=None):
+    _check(lib().moba_gate_pooled(_ptr(q), ctypes.byref(shape), block_size, topk, extra_max,
+                                  extra_min, ctypes.byref(layout), _ptr(workspace),
+                                  kv_head_begin, _stream(stream)))
+
+
 def moba_dispatch(shape, block_size, topk, layout, workspace, kv_head_begin=0, stream=None):
     _check(lib().moba_dispatch(ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
                                _ptr(workspace), kv_head_begin, _stream(stream)))
@@ -204,6 +248,18 @@ def moba_fwd_ex(q, k, v, cu_seqlens, block_size, topk, workspace, out=None, lse=
                              block_size, topk, softmax_scale, _ptr(out), _ptr(lse),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream)))
+    return out, lse
+
+
+def moba_fwd_gated(q, k, v, cu_seqlens, block_size, topk, gate, workspace, out=None, lse=None,
+                   softmax_scale=0.0, max_seqlen=0, stream=None):
+    """Forward pass with a gate variant (Gate) and a caller-provided workspace."""
+    out, lse = _outputs(q, out, lse)
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    _check(lib().moba_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
+                                block_size, topk, ctypes.byref(gate), softmax_scale, _ptr(out),
+                                _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

@@ -93,6 +93,31 @@ typedef struct moba_shape {
 /* Workspace plan: byte offsets of every intermediate inside one workspace.
  * Work on the query heads is done in passes of kv_heads_per_pass kv heads
  * (and their Hq/Hkv query heads each); per-pass buffers are reused. */
+/* Gate variants (moba_fwd_gated). Every gate keeps the query's own block and
+ * never selects a later block; all three share the attention and merge. */
+typedef enum {
+  /* top-k by the mean-pooled keys (section 3.4, "Affinity Scoring" and
+   * "Top-k Gating"): moba_gate */
+  MOBA_GATE_MEAN = 0,
+  /* fixed: the n_sink initial blocks and the topk - n_sink most recent ones
+   * (section 3.4, "Context Partitioning": sliding window, attention sink):
+   * moba_gate_window */
+  MOBA_GATE_WINDOW = 1,
+  /* the mean gate's topk - extra_max - extra_min - 1 earlier blocks plus the
+   * extra_max best by max-pooled and the extra_min best by min-pooled keys
+   * (review page, authors' rebuttals on mean pooling and on QUEST), as a
+   * union: moba_gate_pooled */
+  MOBA_GATE_POOLED = 2
+} moba_gate_kind_t;
+
+typedef struct moba_gate {
+  moba_gate_kind_t kind;
+  int32_t n_sink;     /* WINDOW: initial blocks always kept, 0 <= n_sink < topk */
+  int32_t extra_max;  /* POOLED: extra blocks by max-pooled keys, 0..16 */
+  int32_t extra_min;  /* POOLED: extra blocks by min-pooled keys, 0..16;
+                       * extra_max + extra_min < topk */
+} moba_gate_t;
+
 typedef struct moba_layout {
   int64_t num_blocks_bound;   /* NBb = ceil(T/block_size) + S >= number of blocks */
   int64_t padded_tokens;      /* T rounded up to 64 (informational) */
@@ -106,13 +131,17 @@ typedef struct moba_layout {
    * indices past the last block). Written by moba_seqtable. */
   size_t table_offset;
   /* float32 kbar[NBb][Hkv][d]: mean-pooled keys of every block, followed by
-   * bf16 kbar_split[NBb][Hkv][2][d]: hi = bf16(kbar), lo = bf16(kbar - hi). */
+   * bf16 kbar_split[NBb][Hkv][2][d]: hi = bf16(kbar), lo = bf16(kbar - hi);
+   * then the same pair for the max-pooled keys (kmax, kmax_split) and for the
+   * min-pooled keys (kmin, kmin_split). */
   size_t kbar_offset;
   /* element type, vt[P][NBb][d][block_size]: for each kv head of the pass
    * and each block, the block's value rows transposed (zero past its rows). */
   size_t vt_offset;
   /* int32 idx[T][Hp][topk]: chosen local block ids of the pass's query heads,
-   * ascending, -1 padded; the last valid entry is the query's own block. */
+   * ascending, unused entries -1; the query's own block c is always at
+   * position min(topk, c + 1) - 1 (the mean and window gates fill every
+   * position before it; the pooled gate may leave some -1 there). */
   size_t idx_offset;
   /* dispatch tables over bins b = p*NBb + global_block (p < P), uint32:
    * count[P*NBb], offset[P*NBb+1], tile_offset[P*NBb+1] (tiles of the
@@ -175,6 +204,31 @@ moba_status_t moba_gate(const void *q, const moba_shape_t *shape, int32_t block_
                         int32_t topk, const moba_layout_t *layout, void *workspace,
                         int32_t kv_head_begin, hipStream_t stream);
 
+/* kmax / kmin = elementwise max / min of each block's key rows (the block
+ * representations of the pooled gate). Reads k, writes their parts of the
+ * kbar region. */
+moba_status_t moba_minmaxpool(const void *k, const moba_shape_t *shape, int32_t block_size,
+                              const moba_layout_t *layout, void *workspace, hipStream_t stream);
+
+/* Fixed gate (MOBA_GATE_WINDOW): writes the idx region with, for every row
+ * and query head of the pass, the n_sink initial blocks and the
+ * topk - n_sink most recent blocks up to its own (all blocks so far when
+ * there are at most topk). Reads only the block table; 0 <= n_sink < topk. */
+moba_status_t moba_gate_window(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                               int32_t n_sink, const moba_layout_t *layout, void *workspace,
+                               int32_t kv_head_begin, hipStream_t stream);
+
+/* Pooled-key gate (MOBA_GATE_POOLED): the union of the mean gate's
+ * topk - extra_max - extra_min - 1 earlier blocks, the extra_max best by
+ * <q, kmax_j> and the extra_min best by <q, kmin_j> (same tie rule), plus the
+ * own block, in the idx layout above; slots left empty are -1 and their
+ * part_lse entries are set to -inf so that the merge skips them. Uses the
+ * part_o region as scratch; needs moba_meanpool and moba_minmaxpool. */
+moba_status_t moba_gate_pooled(const void *q, const moba_shape_t *shape, int32_t block_size,
+                               int32_t topk, int32_t extra_max, int32_t extra_min,
+                               const moba_layout_t *layout, void *workspace,
+                               int32_t kv_head_begin, hipStream_t stream);
+
 /* Regroup queries by chosen block (step 2): histogram, prefix sum and scatter
  * of the earlier-block entries of idx into the bins and items regions. The
  * query's own block is not dispatched (the diagonal attention covers it). */
@@ -205,8 +259,10 @@ moba_status_t moba_attn_fwd_hist(const void *q, const void *k, const moba_shape_
                                  int32_t kv_head_begin, hipStream_t stream);
 
 /* Log-sum-exp combination (step 4): out[t][h] = sum_s exp(lse_s - L) o_s with
- * L = log sum_s exp(lse_s), over the valid slots in ascending block order;
- * lse[h][t] = L (lse may be NULL). Writes the pass's heads of out and lse. */
+ * L = log sum_s exp(lse_s), over the slots before and at the own block's
+ * position in ascending block order (slots whose lse is -inf hold no block
+ * and are skipped); lse[h][t] = L (lse may be NULL). Writes the pass's heads
+ * of out and lse. */
 moba_status_t moba_merge(const moba_shape_t *shape, int32_t block_size, int32_t topk,
                          const moba_layout_t *layout, void *workspace, int32_t kv_head_begin,
                          void *out, float *lse, hipStream_t stream);
@@ -221,7 +277,15 @@ moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v,
                           float *lse, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* Same with softmax_scale = 1/sqrt(d) and stream-ordered scratch of at most
+/* The same with a gate variant (gate must be non-NULL; MOBA_GATE_MEAN is
+ * moba_fwd_ex). topk is the number of slots per (row, head). */
+moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v,
+                             const int32_t *cu_seqlens, const moba_shape_t *shape,
+                             int32_t block_size, int32_t topk, const moba_gate_t *gate,
+                             float softmax_scale, void *out, float *lse, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Same as moba_fwd_ex with softmax_scale = 1/sqrt(d) and stream-ordered scratch of at most
  * MOBA_WORKSPACE_LIMIT_GIB GiB (environment, default 48) per call. */
 moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
                        const moba_shape_t *shape, int32_t block_size, int32_t topk, void *out,

@@ -49,6 +49,10 @@ def _load():
                                       p, p, i64, dbl, p, p]
         lib.oracle_moba.argtypes = [p, p, p, i32, i64, i32, i32, i32, p, i32, i32, i32, dbl,
                                     p, i64, p, p, p, p]
+        lib.oracle_select_window.argtypes = [p, i32, i32, i64, i32, i32, i32, p, i64, p]
+        lib.oracle_minmaxpool.argtypes = [p, i32, i64, i32, i32, p, i32, i32, p, p]
+        lib.oracle_select_pooled.argtypes = [p, i32, p, p, p, i64, i32, i32, i32, p, i32, i32,
+                                             i32, i32, i32, p, i64, p, p]
         lib.oracle_dense_causal.argtypes = [p, p, p, i32, i64, i32, i32, i32, p, i32, p, i64,
                                             dbl, p, p]
         for f in (lib.oracle_meanpool, lib.oracle_select, lib.oracle_attend, lib.oracle_moba,
@@ -121,6 +125,54 @@ def select(q, kbar, cu_seqlens, block_size, topk, rows=None, want_scores=False):
                           block_size, topk, _ptr(r), n, _ptr(sel), _ptr(tie), _ptr(scores),
                           max_blocks)
     return sel, tie.astype(bool), scores
+
+
+def select_window(cu_seqlens, block_size, topk, n_sink, num_q_heads, rows=None, total_tokens=None):
+    """Fixed gate (sliding window, optionally with n_sink initial blocks):
+    sel[n][Hq][topk] int32."""
+    cu = _cu(cu_seqlens)
+    T = int(cu[-1]) if total_tokens is None else int(total_tokens)
+    r, n = _rows(rows)
+    n = T if r is None else n
+    assert 0 <= n_sink < topk
+    sel = np.zeros((n, num_q_heads, topk), dtype=np.int32)
+    _load().oracle_select_window(_ptr(cu), cu.size - 1, block_size, T, num_q_heads, topk, n_sink,
+                                 _ptr(r), n, _ptr(sel))
+    return sel
+
+
+def minmaxpool(k, cu_seqlens, block_size):
+    """(K-max, K-min)[total_blocks][Hkv][d] (float64): elementwise max / min
+    over each block's rows."""
+    bf = _check_inputs(k)
+    cu = _cu(cu_seqlens)
+    T, Hkv, d = k.shape
+    nb = int(block_first(cu, block_size)[-1])
+    kmax = np.zeros((max(nb, 1), Hkv, d), dtype=np.float64)
+    kmin = np.zeros((max(nb, 1), Hkv, d), dtype=np.float64)
+    _load().oracle_minmaxpool(_ptr(k), bf, T, Hkv, d, _ptr(cu), cu.size - 1, block_size,
+                              _ptr(kmax), _ptr(kmin))
+    return kmax[:nb], kmin[:nb]
+
+
+def select_pooled(q, kbar, kmax, kmin, cu_seqlens, block_size, topk, extra_max, extra_min,
+                  rows=None):
+    """Gate with extra blocks from max- and min-pooled keys:
+    (sel[n][Hq][topk] int32, near_tie[n][Hq] bool)."""
+    bf = _check_inputs(q)
+    cu = _cu(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = kbar.shape[1]
+    assert topk - extra_max - extra_min >= 1 and extra_max >= 0 and extra_min >= 0
+    arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (kbar, kmax, kmin)]
+    r, n = _rows(rows)
+    n = T if r is None else n
+    sel = np.zeros((n, Hq, topk), dtype=np.int32)
+    tie = np.zeros((n, Hq), dtype=np.uint8)
+    _load().oracle_select_pooled(_ptr(q), bf, _ptr(arrs[0]), _ptr(arrs[1]), _ptr(arrs[2]), T, Hq,
+                                 Hkv, d, _ptr(cu), cu.size - 1, block_size, topk, extra_max,
+                                 extra_min, _ptr(r), n, _ptr(sel), _ptr(tie))
+    return sel, tie.astype(bool)
 
 
 def attend(q, k, v, cu_seqlens, block_size, topk, sel, scale=None, rows=None):

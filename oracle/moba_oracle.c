@@ -188,6 +188,145 @@ void oracle_select(const void *q, int is_bf16, const double *kbar, int64_t T,
   free(first);
 }
 
+/* Fixed gates: sliding window and attention sink.
+ * [S] section 3.4 "Context Partitioning": a sliding window is MoBA with a gate
+ * that always picks the most recent blocks, an attention sink one that always
+ * picks the initial and the recent blocks.
+ * Reading: the topk slots hold the n_sink initial blocks (0 <= n_sink < topk)
+ * and the topk - n_sink most recent blocks up to and including the current
+ * block c; a row with at most topk blocks so far takes all of them. The
+ * selection is the same for every head.
+ * sel: [n_rows][Hq][topk], ascending, -1 padded. */
+void oracle_select_window(const int32_t *cu, int S, int B, int64_t T, int Hq, int topk,
+                          int n_sink, const int64_t *rows, int64_t n_rows, int32_t *sel) {
+  if (!rows) n_rows = T;
+  int w = topk - n_sink;  /* recent blocks, the current one included */
+  for (int64_t ri = 0; ri < n_rows; ++ri) {
+    int64_t t = rows ? rows[ri] : ri;
+    int s = seq_of_row(cu, S, t);
+    int c = (int)((t - cu[s]) / B);
+    for (int h = 0; h < Hq; ++h) {
+      int32_t *out = sel + (ri * Hq + h) * (int64_t)topk;
+      int n = 0;
+      for (int j = 0; j <= c; ++j)
+        if (j < n_sink || j > c - w) out[n++] = j;
+      while (n < topk) out[n++] = -1;
+    }
+  }
+}
+
+/* Max- and min-pooled keys: elementwise max / min over the block's rows.
+ * [R] authors' rebuttals (W1, on mean pooling / on QUEST): blocks chosen by
+ * max-pooled and min-pooled keys on top of the mean-pooled ranking. */
+void oracle_minmaxpool(const void *k, int is_bf16, int64_t T, int Hkv, int d,
+                       const int32_t *cu, int S, int B, double *kmax, double *kmin) {
+  (void)T;
+  int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (S + 1));
+  oracle_block_first(cu, S, B, first);
+  for (int s = 0; s < S; ++s) {
+    int64_t a = cu[s], L = (int64_t)cu[s + 1] - cu[s];
+    int64_t nb = ceil_div(L, B);
+    for (int64_t j = 0; j < nb; ++j) {
+      int64_t r0 = j * B, r1 = (j + 1) * B < L ? (j + 1) * B : L;
+      for (int g = 0; g < Hkv; ++g) {
+        double *mx = kmax + ((first[s] + j) * Hkv + g) * (int64_t)d;
+        double *mn = kmin + ((first[s] + j) * Hkv + g) * (int64_t)d;
+        for (int e = 0; e < d; ++e) { mx[e] = -INFINITY; mn[e] = INFINITY; }
+        for (int64_t r = r0; r < r1; ++r)
+          for (int e = 0; e < d; ++e) {
+            double x = load_elem(k, ((a + r) * Hkv + g) * (int64_t)d + e, is_bf16);
+            if (x > mx[e]) mx[e] = x;
+            if (x < mn[e]) mn[e] = x;
+          }
+      }
+    }
+  }
+  free(first);
+}
+
+/* Scores of earlier blocks 0..c-1 against one pooled-key table, sorted by
+ * (score desc, index asc); returns 1 when the pick-th and (pick+1)-th scores
+ * are a near tie (1e-3 relative), as for the mean gate. */
+static int rank_blocks(const void *q, int is_bf16, const double *pool, int64_t t, int Hq, int h,
+                       int Hkv, int g, int d, int64_t first, int c, int pick, cand_t *cand) {
+  for (int j = 0; j < c; ++j) {
+    const double *kb = pool + ((first + j) * Hkv + g) * (int64_t)d;
+    double acc = 0.0;
+    for (int e = 0; e < d; ++e) acc += load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16) * kb[e];
+    cand[j].s = acc;
+    cand[j].j = j;
+  }
+  qsort(cand, (size_t)c, sizeof(cand_t), cand_cmp);
+  if (pick < 1 || c <= pick) return 0;
+  double a = cand[pick - 1].s, b = cand[pick].s;
+  double m = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
+  return fabs(a - b) < 1e-3 * m;
+}
+
+/* Gate with extra blocks from max- and min-pooled keys.
+ * [R] authors' rebuttals: besides the blocks chosen by the mean-pooled gate,
+ * the top blocks by max pooling and by min pooling are selected as well.
+ * Reading: with W = topk slots, the mean-pooled gate keeps its own-block rule
+ * and picks W - extra_max - extra_min - 1 earlier blocks; the max-pooled and
+ * min-pooled rankings (raw inner products, same order and tie rule) add their
+ * best extra_max and extra_min earlier blocks; the selection is the union.
+ * Layout per (row, head): the union's earlier blocks ascending, then -1 for
+ * the slots a coinciding pick left empty, then the own block at position
+ * min(W, c+1) - 1, then -1. near_tie: any of the three rankings has a near
+ * tie at its boundary. */
+void oracle_select_pooled(const void *q, int is_bf16, const double *kbar, const double *kmax,
+                          const double *kmin, int64_t T, int Hq, int Hkv, int d,
+                          const int32_t *cu, int S, int B, int topk, int extra_max,
+                          int extra_min, const int64_t *rows, int64_t n_rows, int32_t *sel,
+                          uint8_t *near_tie) {
+  int64_t *first = (int64_t *)malloc(sizeof(int64_t) * (S + 1));
+  oracle_block_first(cu, S, B, first);
+  int G = Hq / Hkv;
+  if (!rows) n_rows = T;
+  int pick_mean = topk - extra_max - extra_min - 1;
+#pragma omp parallel
+  {
+    cand_t *cand = NULL;
+    uint8_t *in = NULL;
+    int64_t cap = 0;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t rh = 0; rh < n_rows * Hq; ++rh) {
+      int64_t ri = rh / Hq;
+      int h = (int)(rh % Hq);
+      int64_t t = rows ? rows[ri] : ri;
+      int s = seq_of_row(cu, S, t);
+      int c = (int)((t - cu[s]) / B);
+      int g = h / G;
+      if (c + 1 > cap) {
+        free(cand); free(in);
+        cap = c + 64;
+        cand = (cand_t *)malloc(sizeof(cand_t) * cap);
+        in = (uint8_t *)malloc((size_t)cap);
+      }
+      memset(in, 0, (size_t)c + 1);
+      const double *pools[3] = {kbar, kmax, kmin};
+      int picks[3] = {pick_mean, extra_max, extra_min};
+      uint8_t flag = 0;
+      for (int p = 0; p < 3; ++p) {
+        flag |= (uint8_t)rank_blocks(q, is_bf16, pools[p], t, Hq, h, Hkv, g, d, first[s], c,
+                                     picks[p], cand);
+        for (int r = 0; r < picks[p] && r < c; ++r) in[cand[r].j] = 1;
+      }
+      if (near_tie) near_tie[rh] = flag;
+      int32_t *out = sel + rh * (int64_t)topk;
+      int nsel = topk < c + 1 ? topk : c + 1;
+      int n = 0;
+      for (int j = 0; j < c; ++j)
+        if (in[j]) out[n++] = j;
+      while (n < nsel - 1) out[n++] = -1;
+      out[n++] = c;
+      while (n < topk) out[n++] = -1;
+    }
+    free(cand); free(in);
+  }
+  free(first);
+}
+
 /* Attention of one query row over an explicit key-row set.
  * [S] "The Core MoBA Attention Equation": Softmax(q K[I]^T) V[I], with the
  * caller's logit scale; lse = log sum_u exp(z_u). */
