@@ -109,6 +109,13 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate", choices=["mean", "window", "pooled"], default="mean",
+                    help="gate variant (mean: top-k by mean-pooled keys; window: sliding window "
+                    "with --n-sink initial blocks; pooled: mean top-k plus --extra-max / "
+                    "--extra-min blocks by max- / min-pooled keys, topk + extras slots)")
+    ap.add_argument("--n-sink", type=int, default=1)
+    ap.add_argument("--extra-max", type=int, default=1)
+    ap.add_argument("--extra-min", type=int, default=1)
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows the CPU oracle times (0 = sized for about 15 s)")
     args = ap.parse_args()
@@ -124,6 +131,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     B, k, Hq, Hkv = w.block_size, w.topk, w.num_q_heads, w.num_kv_heads
+    if args.gate == "pooled":
+        k += args.extra_max + args.extra_min  # slots: the mean gate's k plus the extra picks
     T = w.total_tokens
     log("workload %s: generating seeded inputs" % w.name)
     t0 = time.time()
@@ -143,11 +152,25 @@ def main():
     log("workspace %.1f GiB, %d pass(es) of %d kv heads" % (lay.total_bytes / 2**30, len(passes),
                                                          lay.kv_heads_per_pass))
 
+    def gate(g0):
+        if args.gate == "window":
+            moba.moba_gate_window(shape, B, k, args.n_sink, lay, ws, g0)
+        elif args.gate == "pooled":
+            moba.moba_gate_pooled(q, shape, B, k, args.extra_max, args.extra_min, lay, ws, g0)
+        else:
+            moba.moba_gate(q, shape, B, k, lay, ws, g0)
+
+    def pools():
+        if args.gate != "window":
+            moba.moba_meanpool(kk, shape, B, lay, ws)
+        if args.gate == "pooled":
+            moba.moba_minmaxpool(kk, shape, B, lay, ws)
+
     def step(tm):
         tm.run("seqtable", lambda: moba.moba_seqtable(cu, shape, B, lay, ws))
-        tm.run("meanpool", lambda: moba.moba_meanpool(kk, shape, B, lay, ws))
+        tm.run("meanpool", pools)
         for g0 in passes:
-            tm.run("gate", lambda: moba.moba_gate(q, shape, B, k, lay, ws, g0))
+            tm.run("gate", lambda: gate(g0))
             tm.run("dispatch", lambda: moba.moba_dispatch(shape, B, k, lay, ws, g0))
             tm.run("attn_diag", lambda: moba.moba_attn_fwd_diag(q, kk, v, shape, B, k, lay, ws, g0))
             tm.run("attn_hist", lambda: moba.moba_attn_fwd_hist(q, kk, shape, B, k, lay, ws, g0))
@@ -157,9 +180,9 @@ def main():
     nbins = lay.kv_heads_per_pass * lay.num_blocks_bound
     hist_rows = []
     moba.moba_seqtable(cu, shape, B, lay, ws)
-    moba.moba_meanpool(kk, shape, B, lay, ws)
+    pools()
     for g0 in passes:
-        moba.moba_gate(q, shape, B, k, lay, ws, g0)
+        gate(g0)
         moba.moba_dispatch(shape, B, k, lay, ws, g0)
         torch.cuda.synchronize()
         off = workspace_view(ws, lay.bins_offset + 4 * nbins, nbins + 1, torch.int32)
@@ -182,7 +205,11 @@ def main():
     stages = {n: (tot / args.steps, cnt) for n, (tot, cnt) in tm.totals().items()}
     log("step %.2f ms; stages %s" % (ms, {n: round(v[0], 3) for n, v in stages.items()}))
 
-    eff = effective_flop(w.lengths, B, k, Hq)
+    if args.gate == "mean":
+        eff = effective_flop(w.lengths, B, k, Hq)
+    else:  # keys actually attended: dispatched earlier blocks in full, own block causally
+        own = sum(int(((np.arange(L) % B) + 1).sum()) for L in w.lengths)
+        eff = 4.0 * HEAD_DIM * (B * float(sum(hist_rows)) + Hq * own)
     value = eff / (ms * 1e-3) / 1e12
     es = 2 if w.dtype == "bf16" else 4
     # dominant kernel: earlier-block attention, MFMA bound
@@ -201,8 +228,15 @@ def main():
 
     # memory-bound stages against the HBM roofline
     nb = sum(-(-L // B) for L in w.lengths)
-    mp_bytes = T * Hkv * HEAD_DIM * es + nb * Hkv * HEAD_DIM * 4
-    gate_bytes = T * Hq * HEAD_DIM * es + T * Hq * k * 4
+    if args.gate == "window":   # no pooling; the gate writes idx only
+        mp_bytes, gate_bytes = 0, T * Hq * k * 4
+    elif args.gate == "pooled":  # k read twice (mean, max/min); q read by three rankings
+        n_lists = (k - args.extra_max - args.extra_min) + args.extra_max + 1 + args.extra_min + 1
+        mp_bytes = 2 * T * Hkv * HEAD_DIM * es + 3 * nb * Hkv * HEAD_DIM * 8
+        gate_bytes = 3 * T * Hq * HEAD_DIM * es + T * Hq * (2 * n_lists + k) * 4
+    else:
+        mp_bytes = T * Hkv * HEAD_DIM * es + nb * Hkv * HEAD_DIM * 4
+        gate_bytes = T * Hq * HEAD_DIM * es + T * Hq * k * 4
     # dispatch: idx read by the count and the scatter pass, items written
     n_hist = sum(hist_rows)
     disp_bytes = 2 * T * Hq * k * 4 + n_hist * 4
@@ -212,6 +246,8 @@ def main():
     for name, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes), ("dispatch", disp_bytes),
                          ("merge", merge_bytes)):
         sm = stages[name][0]
+        if nbytes == 0 or sm <= 0:
+            continue
         hbm[name] = {"ms": round(sm, 4), "GB/s": round(nbytes / (sm * 1e-3) / 1e9, 1),
                      "frac": round(nbytes / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     attn_ms = stages["attn_diag"][0] + stages["attn_hist"][0]
@@ -252,6 +288,10 @@ def main():
         "config": {"workload": w.name, "seq_lens": list(w.lengths), "total_tokens": T,
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": HEAD_DIM, "block_size": B,
                    "topk": k, "kv_heads_per_pass": lay.kv_heads_per_pass,
+                   "gate": {"mean": {"kind": "mean"},
+                            "window": {"kind": "window", "n_sink": args.n_sink},
+                            "pooled": {"kind": "pooled", "extra_max": args.extra_max,
+                                       "extra_min": args.extra_min}}[args.gate],
                    "parallelism": "single GPU"},
         "effective_flop": eff,
         "attention_effective_TFLOPs": round(attn_eff, 2),

@@ -349,8 +349,9 @@ __global__ __launch_bounds__(256) void gate_window_kernel(const int32_t *__restr
   const int w = k - n_sink;
   int32_t *dst = idx + row * k;
   int n = 0;
-  for (int j = 0; j <= c && n < k; ++j)
-    if (j < n_sink || j > c - w) dst[n++] = j;
+  const int s_end = min(n_sink, c + 1);       // sink blocks 0 .. s_end-1
+  for (int j = 0; j < s_end; ++j) dst[n++] = j;
+  for (int j = max(s_end, c - w + 1); j <= c; ++j) dst[n++] = j;  // recent blocks
   for (; n < k; ++n) dst[n] = -1;
 }
 
