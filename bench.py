@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--n-sink", type=int, default=1)
     ap.add_argument("--extra-max", type=int, default=1)
     ap.add_argument("--extra-min", type=int, default=1)
+    ap.add_argument("--decode", default=None, metavar="SxL",
+                    help="time decode instead: S sequences with KV caches of L tokens each "
+                    "(e.g. 1x1048576 or 32x32768), one new query per sequence")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows the CPU oracle times (0 = sized for about 15 s)")
     args = ap.parse_args()
@@ -124,6 +127,10 @@ def main():
               "shard by kv-head group with no exchange between GPUs). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        decode_bench(args)
+        return
 
     import torch
     from block_sparse_long_moba_amd import moba, synth
@@ -303,6 +310,80 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def decode_bench(args):
+    """Decode: one new query per sequence over a KV cache (the 8B head shape,
+    block 4096, top-k 12). Reports the latency of moba_decode and its HBM
+    rate: the keys and values of the distinct blocks each (sequence, kv head)
+    selected, read once, plus queries, pooled keys and outputs. The same call
+    with topk covering every block is dense decode over the whole cache."""
+    import torch
+    from block_sparse_long_moba_amd import moba, synth
+    from block_sparse_long_moba_amd.tensors import to_device, workspace_view
+
+    S, L = (int(x) for x in args.decode.lower().split("x"))
+    Hq, Hkv, B, k = 32, 8, 4096, 12
+    log("decode: %d sequence(s) with caches of %d tokens: generating" % (S, L))
+    inp = synth.custom([L] * S, Hq, Hkv, HEAD_DIM, "bf16", B, k, 91)
+    cu = inp.cu_seqlens
+    qd = np.stack([inp.q[cu[s + 1] - 1] for s in range(S)])
+    q, kc, vc, cud = (to_device(x) for x in (qd, inp.k, inp.v, cu))
+    del inp
+    T = int(cu[-1])
+    res = {}
+    for name, topk in (("moba", k), ("dense", -(-L // B))):
+        sh = moba.make_shape(T, S, Hq, Hkv, HEAD_DIM, "bf16", max_seqlen=L)
+        ws = torch.empty(moba.moba_decode_workspace_size(sh, B, topk), dtype=torch.uint8,
+                         device="cuda")
+        moba.moba_decode_prepare(kc, cud, sh, B, topk, ws)
+        out, lse = moba.moba_decode(q, kc, vc, sh, B, topk, ws)
+        torch.cuda.synchronize()
+        # selected blocks per (sequence, kv head): the kernel reads each once
+        nb = -(-L // B)
+        NBb = -(-T // B) + S
+        table = (2 * 4 * (S + 1) + 15) // 16 * 16 + 16 * NBb
+        align = lambda x: (x + 255) // 256 * 256
+        off = align(align(table) + 8 * NBb * Hkv * HEAD_DIM)
+        idx = workspace_view(ws, off, S * Hq * topk, torch.int32).view(S, Hkv, Hq // Hkv, topk)
+        idx = idx.cpu().numpy()
+        kv_bytes = 0
+        for s in range(S):
+            for g in range(Hkv):
+                blocks = set(int(x) for x in idx[s, g].ravel() if x >= 0)
+                kv_bytes += sum(min(B, L - j * B) for j in blocks) * HEAD_DIM * 2 * 2
+        other = S * Hq * HEAD_DIM * 2 * 2 + S * Hq * (nb - 1) * HEAD_DIM * 4
+        for _ in range(args.warmup):
+            moba.moba_decode(q, kc, vc, sh, B, topk, ws, out=out, lse=lse)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            moba.moba_decode(q, kc, vc, sh, B, topk, ws, out=out, lse=lse)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        nbytes = kv_bytes + other
+        res[name] = {"topk": topk, "ms": round(ms, 4), "hbm_bytes": nbytes,
+                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log("%s decode: %.4f ms, %.1f GB/s" % (name, ms, res[name]["GB/s"]))
+        del ws
+    line = {
+        "metric": "MoBA decode latency (one query per sequence over its KV cache)",
+        "value": res["moba"]["ms"], "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, per-block key offsets)",
+        "config": {"workload": "decode_%dx%d" % (S, L), "sequences": S, "cache_tokens": L,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": HEAD_DIM, "block_size": B,
+                   "topk": k},
+        "roofline": {"bound": "hbm", "achieved": res["moba"]["GB/s"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": res["moba"]["frac"], "traffic": None},
+        "dense_decode": res["dense"],
+        "speedup_moba_vs_dense": round(res["dense"]["ms"] / res["moba"]["ms"], 3),
+        "moba": res["moba"],
+    }
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(inp, w, n_rows):

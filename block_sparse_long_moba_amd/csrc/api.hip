@@ -305,6 +305,75 @@ size_t workspace_limit_bytes() {
   return (size_t)(gib * (double)(size_t(1) << 30));
 }
 
+// ---- decode workspace: block table, pooled keys (with the bf16 split the
+// mean-pool kernel also writes), idx[S][Hq][k], fp32 parts [S*Hq*k][d] and
+// their lse.
+struct DecodeLayout {
+  int64_t NBb;
+  int maxblk;
+  size_t table, kbar, idx, part_o, part_lse, total;
+};
+
+moba_status_t decode_layout(const moba_shape_t *sh, int32_t B, int32_t k, DecodeLayout *D) {
+  // decode keeps S*Hq*k slots and ranks candidates by counting: no limit on k
+  moba_status_t st = check_shape(sh);
+  if (st != MOBA_SUCCESS) return st;
+  if (B < 1) return fail(MOBA_ERROR_INVALID_VALUE, "block_size must be >= 1");
+  if (k < 1) return fail(MOBA_ERROR_INVALID_VALUE, "topk must be >= 1");
+  if ((int64_t)sh->num_seqs * sh->num_q_heads * k >= (int64_t(1) << 31))
+    return fail(MOBA_ERROR_UNSUPPORTED, "num_seqs * num_q_heads * topk must be < 2^31");
+  const int G = sh->num_q_heads / sh->num_kv_heads;
+  if (G > 64) return fail(MOBA_ERROR_UNSUPPORTED, "decode: at most 64 query heads per kv head");
+  const int64_t T = sh->total_tokens;
+  const int S = sh->num_seqs;
+  const int64_t maxlen = sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, T) : T;
+  D->maxblk = (int)std::max<int64_t>(1, ceil_div(maxlen, B));
+  if (D->maxblk > kLdsBins)
+    return fail(MOBA_ERROR_UNSUPPORTED, "decode: a sequence may have %d blocks; at most %d",
+                D->maxblk, kLdsBins);
+  D->NBb = ceil_div(T, B) + S;
+  const size_t slots = (size_t)S * sh->num_q_heads * k *
+                       decode_splits(S, sh->num_q_heads, sh->num_kv_heads, B, k, D->maxblk);
+  size_t off = 0;
+  D->table = off;    off = align_up(off + table_bytes(S, D->NBb));
+  D->kbar = off;     off = align_up(off + (sizeof(float) + 4) * (size_t)D->NBb * sh->num_kv_heads * kHeadDim);
+  D->idx = off;      off = align_up(off + sizeof(int32_t) * std::max<size_t>(1, slots));
+  D->part_o = off;   off = align_up(off + sizeof(float) * kHeadDim * std::max<size_t>(1, slots));
+  D->part_lse = off; off = align_up(off + sizeof(float) * std::max<size_t>(1, slots));
+  D->total = off;
+  return MOBA_SUCCESS;
+}
+
+void decode_setup(const moba_shape_t *sh, int32_t B, int32_t k, float scale, const DecodeLayout &D,
+                  void *ws, Problem *pb, Work *w) {
+  *pb = Problem{};
+  pb->T = sh->total_tokens;
+  pb->S = sh->num_seqs;
+  pb->maxlen = (int)(sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, pb->T) : pb->T);
+  pb->Hq = sh->num_q_heads;
+  pb->Hkv = sh->num_kv_heads;
+  pb->G = pb->Hq / pb->Hkv;
+  pb->bf16 = sh->dtype == MOBA_DTYPE_BF16;
+  pb->B = B;
+  pb->k = k;
+  pb->scale = scale > 0.f ? scale : 1.0f / sqrtf((float)kHeadDim);
+  pb->NBb = D.NBb;
+  pb->P = pb->Hkv;
+  pb->Hp = pb->Hq;
+  pb->maxblk = D.maxblk;
+  pb->rows = attn_rows(pb->bf16);
+  char *b = (char *)ws;
+  *w = Work{};
+  w->blk_first = (int32_t *)(b + D.table);
+  w->cu = (int32_t *)(b + D.table + cu_copy_offset(pb->S));
+  w->blk_info = (int4 *)(b + D.table + info_offset(pb->S));
+  w->kbar = (float *)(b + D.kbar);
+  w->kbar_split = (__bf16 *)(w->kbar + (size_t)D.NBb * pb->Hkv * kHeadDim);
+  w->idx = (int32_t *)(b + D.idx);
+  w->part_o = b + D.part_o;
+  w->part_lse = (float *)(b + D.part_lse);
+}
+
 }  // namespace
 
 extern "C" {
@@ -533,6 +602,57 @@ moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int
                           void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
   const moba_gate_t mean{MOBA_GATE_MEAN, 0, 0, 0};
   return moba_fwd_gated(q, k, v, cu, sh, B, topk, &mean, scale, out, lse, ws, ws_bytes, s);
+}
+
+size_t moba_decode_workspace_size(const moba_shape_t *cache_shape, int32_t block_size,
+                                  int32_t topk) {
+  DecodeLayout D;
+  if (!cache_shape || decode_layout(cache_shape, block_size, topk, &D) != MOBA_SUCCESS) return 0;
+  return D.total;
+}
+
+moba_status_t moba_decode_prepare(const void *k_cache, const int32_t *cu,
+                                  const moba_shape_t *sh, int32_t B, int32_t topk, void *ws,
+                                  size_t ws_bytes, hipStream_t s) {
+  if (!sh) return fail(MOBA_ERROR_INVALID_VALUE, "shape is NULL");
+  DecodeLayout D;
+  moba_status_t st = decode_layout(sh, B, topk, &D);
+  if (st != MOBA_SUCCESS) return st;
+  if (ws_bytes < D.total)
+    return fail(MOBA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes; need %zu", ws_bytes,
+                D.total);
+  if (sh->num_seqs > 0 && !cu) return fail(MOBA_ERROR_INVALID_VALUE, "cu_seqlens is NULL");
+  if (sh->num_seqs == 0) return MOBA_SUCCESS;
+  if (!ws) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
+  if (sh->total_tokens > 0 && !k_cache) return fail(MOBA_ERROR_INVALID_VALUE, "k_cache is NULL");
+  Problem pb;
+  Work w;
+  decode_setup(sh, B, topk, 0.f, D, ws, &pb, &w);
+  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
+  if (sh->total_tokens > 0) MOBA_HIP(launch_meanpool(pb, w, k_cache, s), "meanpool");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const moba_shape_t *sh, int32_t B, int32_t topk, float scale,
+                          void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+  if (!sh) return fail(MOBA_ERROR_INVALID_VALUE, "shape is NULL");
+  DecodeLayout D;
+  moba_status_t st = decode_layout(sh, B, topk, &D);
+  if (st != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  if (ws_bytes < D.total)
+    return fail(MOBA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes; need %zu", ws_bytes,
+                D.total);
+  if (sh->num_seqs == 0) return MOBA_SUCCESS;
+  if (!q || !out || !ws) return fail(MOBA_ERROR_INVALID_VALUE, "q, out and workspace must be non-NULL");
+  if (sh->total_tokens > 0 && (!k_cache || !v_cache))
+    return fail(MOBA_ERROR_INVALID_VALUE, "k_cache and v_cache must be non-NULL");
+  Problem pb;
+  Work w;
+  decode_setup(sh, B, topk, scale, D, ws, &pb, &w);
+  MOBA_HIP(launch_decode(pb, w, q, k_cache, v_cache, out, lse, s), "decode");
+  return MOBA_SUCCESS;
 }
 
 moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_t *cu,

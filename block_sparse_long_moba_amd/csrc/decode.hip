@@ -1,0 +1,327 @@
+// Decode-phase MoBA: one new query per sequence over its KV cache.
+//
+// MoBA summary page (paper-graph-ui), section 3.4: the gate ("Affinity
+// Scoring", "Top-k Gating", "Causality Enforcement") and the block attention
+// apply unchanged to a single query; the review page's GSM-Infinite table
+// reports the "MoBA prefill, MoBA decode" configuration. The query of
+// sequence s is the token at its last cache row L_s - 1, so its own block c
+// is the cache's last (possibly partial) block, attended up to that row; the
+// pooled keys of the earlier blocks come from the cache (moba_meanpool).
+//
+// Three kernels: the gate ranks a query's candidates by counting (exactly the
+// (score desc, index asc) order of the prefill gate), the attention runs one
+// workgroup per (sequence, kv head, block) for every query head of the group
+// that chose the block (the block's keys and values are read once for all of
+// them), and the merge combines the per-block parts by log-sum-exp.
+#include <limits.h>
+
+#include <algorithm>
+
+#include "moba_internal.h"
+
+namespace moba {
+namespace {
+
+constexpr float kLog2eDec = 1.4426950408889634f;
+constexpr float kLn2Dec = 0.6931471805599453f;
+constexpr int kDecKeyLanes = 16;                 // lanes per key row (8 dims each)
+constexpr int kDecGroups = 256 / kDecKeyLanes;   // key groups per workgroup
+constexpr int kDecMaxHeads = 8;                  // query heads per sweep over a block
+
+template <typename T> struct Row8;
+template <> struct Row8<__bf16> {
+  __device__ static void load(const __bf16 *p, float *f) {
+    const uint4 u = *(const uint4 *)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(__bf16 *p, const float *f) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)f[i];
+    *(bf16x8 *)p = v;
+  }
+};
+template <> struct Row8<float> {
+  __device__ static void load(const float *p, float *f) {
+    const float4 a = ((const float4 *)p)[0], b = ((const float4 *)p)[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  __device__ static void store(float *p, const float *f) {
+    ((float4 *)p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+    ((float4 *)p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+  }
+};
+
+// Gate: one workgroup per (sequence, query head). Scores <q, kbar_j> of the
+// earlier blocks j < c in fp32 (the prefill vector gate's arithmetic); block j
+// is picked iff fewer than min(k-1, c) candidates rank above it under
+// (score desc, index asc); picks are written ascending, then the own block c,
+// then -1. A sequence with an empty cache gets -1 everywhere.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_gate_kernel(const T *__restrict__ q,
+                                                          const float *__restrict__ kbar,
+                                                          const int32_t *__restrict__ cu,
+                                                          const int32_t *__restrict__ blk_first,
+                                                          int Hq, int Hkv, int B, int k,
+                                                          int32_t *__restrict__ idx) {
+  const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int L = cu[s + 1] - cu[s];
+  int32_t *dst = idx + ((int64_t)s * Hq + h) * k;
+  if (L == 0) {
+    for (int i = tid; i < k; i += 256) dst[i] = -1;
+    return;
+  }
+  const int c = (L - 1) / B;
+  const int pick = min(k - 1, c);
+  const int g = h / (Hq / Hkv);
+  __shared__ float qs[kHeadDim];
+  __shared__ float sc[kLdsBins];
+  __shared__ uint8_t chosen[kLdsBins];
+  if (tid < kHeadDim) {
+    float f[8];
+    if ((tid & 7) == 0) {
+      Row8<T>::load(q + ((int64_t)s * Hq + h) * kHeadDim + tid, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qs[tid + i] = f[i];
+    }
+  }
+  __syncthreads();
+  const float *kb0 = kbar + ((int64_t)blk_first[s] * Hkv + g) * kHeadDim;
+  const int64_t kstride = (int64_t)Hkv * kHeadDim;
+  for (int j = tid; j < c; j += 256) {
+    const float *kb = kb0 + j * kstride;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < kHeadDim; e += 4) {
+      const float4 kv = *(const float4 *)(kb + e);
+      a0 = fmaf(qs[e], kv.x, a0);
+      a1 = fmaf(qs[e + 1], kv.y, a1);
+      a2 = fmaf(qs[e + 2], kv.z, a2);
+      a3 = fmaf(qs[e + 3], kv.w, a3);
+    }
+    sc[j] = (a0 + a1) + (a2 + a3);
+  }
+  __syncthreads();
+  for (int j = tid; j < c; j += 256) {
+    const float sj = sc[j];
+    int rank = 0;
+    for (int i = 0; i < c; ++i) {
+      const float si = sc[i];
+      rank += (si > sj) || (si == sj && i < j);
+    }
+    chosen[j] = rank < pick;
+  }
+  __syncthreads();
+  for (int j = tid; j < c; j += 256) {
+    if (!chosen[j]) continue;
+    int pos = 0;
+    for (int i = 0; i < j; ++i) pos += chosen[i];
+    dst[pos] = j;
+  }
+  if (tid == 0) {
+    dst[pick] = c;
+    for (int i = pick + 1; i < k; ++i) dst[i] = -1;
+  }
+}
+
+// Attention: one workgroup per (sequence, kv head g, block j <= c). 16 lanes
+// cover one key row (8 dims each, 256 contiguous bytes); 16 key groups walk
+// the block's rows (the own block up to the query's row) with an online
+// softmax per group, combined at the end through LDS. Writes the part of
+// slot (s, h, position of j in h's selection): o (fp32) and lse.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_attn_kernel(
+    const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ idx, int Hq, int Hkv, int B,
+    int k, int ns, float scale_log2, float *__restrict__ part_o, float *__restrict__ part_lse) {
+  const int s = blockIdx.x, g = blockIdx.y, j = blockIdx.z / ns, sp = blockIdx.z % ns;
+  const int tid = threadIdx.x;
+  const int L = cu[s + 1] - cu[s];
+  if (L == 0 || j > (L - 1) / B) return;
+  const int G = Hq / Hkv;
+  __shared__ int heads[64], slots[64], nheads;
+  if (tid == 0) {
+    int n = 0;
+    for (int hl = 0; hl < G && n < 64; ++hl) {
+      const int h = g * G + hl;
+      const int32_t *row = idx + ((int64_t)s * Hq + h) * k;
+      for (int i = 0; i < k; ++i)
+        if (row[i] == j) { heads[n] = h; slots[n] = i; ++n; break; }
+    }
+    nheads = n;
+  }
+  __syncthreads();
+  const int nh = nheads;
+  if (nh == 0) return;
+  const int li = tid % kDecKeyLanes, kg = tid / kDecKeyLanes;
+  // keys [k0, k1) of the block: split sp of ns (the own block may end early;
+  // an empty split still writes its part, with lse -inf)
+  const int chunk = B / ns;
+  const int k0 = sp * chunk, k1 = min(min(B, L - j * B), k0 + chunk);
+  const int nk = max(0, k1 - k0);
+  const int64_t r0 = cu[s] + (int64_t)j * B + k0;
+  const int64_t kstride = (int64_t)Hkv * kHeadDim;
+  const T *kb = kc + (r0 * Hkv + g) * kHeadDim + 8 * li;
+  const T *vb = vc + (r0 * Hkv + g) * kHeadDim + 8 * li;
+  __shared__ float gm[kDecGroups][kDecMaxHeads], gl[kDecGroups][kDecMaxHeads];
+  __shared__ float gacc[kDecGroups][kDecMaxHeads][kHeadDim];
+  for (int h0 = 0; h0 < nh; h0 += kDecMaxHeads) {
+    const int nq = min(kDecMaxHeads, nh - h0);
+    float qv[kDecMaxHeads][8], m[kDecMaxHeads], l[kDecMaxHeads], acc[kDecMaxHeads][8];
+#pragma unroll
+    for (int qi = 0; qi < kDecMaxHeads; ++qi) {
+      m[qi] = -INFINITY;
+      l[qi] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
+      if (qi < nq) {
+        Row8<T>::load(q + ((int64_t)s * Hq + heads[h0 + qi]) * kHeadDim + 8 * li, qv[qi]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[qi][e] *= scale_log2;  // scores in log2 units
+      }
+    }
+    auto consume = [&](const float (&kf)[8], const float (&vf)[8]) {
+#pragma unroll
+      for (int qi = 0; qi < kDecMaxHeads; ++qi) {
+        if (qi >= nq) break;
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[qi][e], kf[e], d);
+#pragma unroll
+        for (int o = kDecKeyLanes / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, kDecKeyLanes);
+        const float mn = fmaxf(m[qi], d);
+        const float alpha = __builtin_amdgcn_exp2f(m[qi] - mn);
+        const float p = __builtin_amdgcn_exp2f(d - mn);
+        l[qi] = l[qi] * alpha + p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qi][e] = fmaf(acc[qi][e], alpha, p * vf[e]);
+        m[qi] = mn;
+      }
+    };
+    // four rows per group in flight, then the rest one by one
+    constexpr int U = 4;
+    int key = kg;
+    for (; key + (U - 1) * kDecGroups < nk; key += U * kDecGroups) {
+      float kf[U][8], vf[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Row8<T>::load(kb + (int64_t)(key + u * kDecGroups) * kstride, kf[u]);
+        Row8<T>::load(vb + (int64_t)(key + u * kDecGroups) * kstride, vf[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) consume(kf[u], vf[u]);
+    }
+    for (; key < nk; key += kDecGroups) {
+      float kf[8], vf[8];
+      Row8<T>::load(kb + (int64_t)key * kstride, kf);
+      Row8<T>::load(vb + (int64_t)key * kstride, vf);
+      consume(kf, vf);
+    }
+#pragma unroll
+    for (int qi = 0; qi < kDecMaxHeads; ++qi) {
+      if (qi >= nq) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gacc[kg][qi][8 * li + e] = acc[qi][e];
+      if (li == 0) { gm[kg][qi] = m[qi]; gl[kg][qi] = l[qi]; }
+    }
+    __syncthreads();
+    for (int x = tid; x < nq * kHeadDim; x += 256) {
+      const int qi = x / kHeadDim, e = x % kHeadDim;
+      float M = -INFINITY;
+      for (int gi = 0; gi < kDecGroups; ++gi) M = fmaxf(M, gm[gi][qi]);
+      float Ls = 0.f, o = 0.f;
+      for (int gi = 0; gi < kDecGroups; ++gi) {
+        const float wgt = gm[gi][qi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(gm[gi][qi] - M);
+        Ls += gl[gi][qi] * wgt;
+        o += gacc[gi][qi][e] * wgt;
+      }
+      const int64_t sl = (((int64_t)s * Hq + heads[h0 + qi]) * k + slots[h0 + qi]) * ns + sp;
+      part_o[sl * kHeadDim + e] = M == -INFINITY ? 0.f : o / Ls;
+      if (e == 0) part_lse[sl] = M == -INFINITY ? -INFINITY : (M + __log2f(Ls)) * kLn2Dec;
+    }
+    __syncthreads();
+  }
+}
+
+// Merge: one workgroup of 128 threads per (sequence, query head): the
+// log-sum-exp combination of its min(k, c+1) parts in ascending block order.
+template <typename T>
+__global__ __launch_bounds__(128) void decode_merge_kernel(const float *__restrict__ part_o,
+                                                           const float *__restrict__ part_lse,
+                                                           const int32_t *__restrict__ cu,
+                                                           int S, int Hq, int B, int k, int ns,
+                                                           T *__restrict__ out,
+                                                           float *__restrict__ lse) {
+  const int s = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const int L = cu[s + 1] - cu[s];
+  T *dst = out + ((int64_t)s * Hq + h) * kHeadDim;
+  if (L == 0) {
+    dst[e] = (T)0.f;
+    if (e == 0 && lse) lse[(int64_t)h * S + s] = -INFINITY;
+    return;
+  }
+  const int n = min(k, (L - 1) / B + 1) * ns;  // parts of the selected blocks, in block order
+  const int64_t base = ((int64_t)s * Hq + h) * k * ns;
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, part_lse[base + i]);
+  float sum = 0.f;
+  for (int i = 0; i < n; ++i)
+    if (part_lse[base + i] > -INFINITY)
+      sum += __builtin_amdgcn_exp2f((part_lse[base + i] - M) * kLog2eDec);
+  const float Lt = M + __logf(sum);
+  float o = 0.f;
+  for (int i = 0; i < n; ++i)
+    if (part_lse[base + i] > -INFINITY)
+      o += __builtin_amdgcn_exp2f((part_lse[base + i] - Lt) * kLog2eDec) *
+           part_o[(base + i) * kHeadDim + e];
+  dst[e] = (T)o;
+  if (e == 0 && lse) lse[(int64_t)h * S + s] = Lt;
+}
+
+}  // namespace
+
+int decode_splits(int S, int Hq, int Hkv, int B, int k, int maxblk) {
+  // split a block's keys over several workgroups while the (sequence, kv
+  // head, chosen block) items are too few to keep the memory system busy
+  const int64_t items = (int64_t)S * Hkv * std::min<int64_t>(maxblk, (int64_t)(Hq / Hkv) * k);
+  int ns = 1;
+  while (ns < 8 && items * ns < 2048 && B % (2 * ns * kDecGroups) == 0) ns *= 2;
+  return ns;
+}
+
+hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const void *kc,
+                         const void *vc, void *out, float *lse, hipStream_t s) {
+  if (pb.S == 0) return hipSuccess;
+  const int ns = decode_splits(pb.S, pb.Hq, pb.Hkv, pb.B, pb.k, pb.maxblk);
+  const dim3 gg((unsigned)pb.S, (unsigned)pb.Hq);
+  const dim3 ga((unsigned)pb.S, (unsigned)pb.Hkv, (unsigned)(pb.maxblk * ns));
+  float *po = (float *)w.part_o;
+  const float sl2 = pb.scale * kLog2eDec;
+  if (pb.bf16) {
+    decode_gate_kernel<__bf16><<<gg, 256, 0, s>>>((const __bf16 *)q, w.kbar, w.cu, w.blk_first,
+                                                  pb.Hq, pb.Hkv, pb.B, pb.k, w.idx);
+    decode_attn_kernel<__bf16><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
+                                                  (const __bf16 *)vc, w.cu, w.idx, pb.Hq, pb.Hkv,
+                                                  pb.B, pb.k, ns, sl2, po, w.part_lse);
+    decode_merge_kernel<__bf16><<<gg, 128, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
+                                                   ns, (__bf16 *)out, lse);
+  } else {
+    decode_gate_kernel<float><<<gg, 256, 0, s>>>((const float *)q, w.kbar, w.cu, w.blk_first,
+                                                 pb.Hq, pb.Hkv, pb.B, pb.k, w.idx);
+    decode_attn_kernel<float><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
+                                                 (const float *)vc, w.cu, w.idx, pb.Hq, pb.Hkv,
+                                                 pb.B, pb.k, ns, sl2, po, w.part_lse);
+    decode_merge_kernel<float><<<gg, 128, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
+                                                  ns, (float *)out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moba

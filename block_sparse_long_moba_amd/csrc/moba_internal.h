@@ -78,6 +78,9 @@ hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, con
                             int g0, hipStream_t s);
 hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, float *lse,
                         hipStream_t s);
+int decode_splits(int S, int Hq, int Hkv, int B, int k, int maxblk);
+hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const void *kc,
+                         const void *vc, void *out, float *lse, hipStream_t s);
 hipError_t launch_dense(const void *q, const void *k, const void *vt, const int32_t *cu,
                         const int32_t *blk_first64, int bf16, int64_t T, int S, int maxlen,
                         int Hq, int Hkv, int64_t NBb64, float scale, void *out, float *lse,

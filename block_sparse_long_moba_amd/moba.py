@@ -22,6 +22,7 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_works
            "moba_seqtable", "moba_meanpool", "moba_gate", "moba_minmaxpool", "moba_gate_window",
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
            "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
+           "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
            "moba_dense_causal_workspace_size", "moba_dense_causal_fwd"]
 
 GATE_MEAN, GATE_WINDOW, GATE_POOLED = 0, 1, 2
@@ -102,6 +103,9 @@ def lib():
             "moba_fwd_gated": ([P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, Z,
                                 P], I32),
             "moba_fwd": ([P, P, P, P, S, I32, I32, P, P, P], I32),
+            "moba_decode_workspace_size": ([S, I32, I32], Z),
+            "moba_decode_prepare": ([P, P, S, I32, I32, P, Z, P], I32),
+            "moba_decode": ([P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
             "moba_dense_causal_workspace_size": ([S], Z),
             "moba_dense_causal_fwd": ([P, P, P, P, S, F, P, P, P, Z, P], I32),
         }
@@ -260,6 +264,33 @@ def moba_fwd_gated(q, k, v, cu_seqlens, block_size, topk, gate, workspace, out=N
                                 block_size, topk, ctypes.byref(gate), softmax_scale, _ptr(out),
                                 _ptr(lse), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def moba_decode_workspace_size(cache_shape: Shape, block_size: int, topk: int) -> int:
+    return lib().moba_decode_workspace_size(ctypes.byref(cache_shape), block_size, topk)
+
+
+def moba_decode_prepare(k_cache, cu_seqlens, cache_shape, block_size, topk, workspace,
+                        stream=None):
+    _check(lib().moba_decode_prepare(_ptr(k_cache), _ptr(cu_seqlens), ctypes.byref(cache_shape),
+                                     block_size, topk, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+
+
+def moba_decode(q, k_cache, v_cache, cache_shape, block_size, topk, workspace, out=None,
+                lse=None, softmax_scale=0.0, stream=None):
+    """One query per sequence (q [S][Hq][d]) over the cache; returns (out, lse [Hq][S])."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    _check(lib().moba_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.byref(cache_shape),
+                             block_size, topk, softmax_scale, _ptr(out), _ptr(lse),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream)))
     return out, lse
 
 

@@ -291,6 +291,30 @@ moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_
                        const moba_shape_t *shape, int32_t block_size, int32_t topk, void *out,
                        float *lse, hipStream_t stream);
 
+/* ---- Decode: one new query per sequence over its KV cache (section 3.4's
+ * gate and block attention applied to a single query; the review page's
+ * GSM-Infinite table reports MoBA used for both prefill and decode).
+ * The cache is k_cache, v_cache [T][Hkv][d] packed by cu_seqlens[S+1] (the
+ * shape describes it: total_tokens = T, num_seqs = S); sequence s's cache
+ * already holds the new token as its last row L_s - 1, the query's position.
+ * q is [S][Hq][d]; out [S][Hq][d] (element type of q) and lse [Hq][S]
+ * (float32, may be NULL). The query's own block is the cache's last block,
+ * attended up to the last row; its k-1 earlier blocks are chosen as in
+ * moba_gate. A sequence with an empty cache gets out = 0 and lse = -inf.
+ * The workspace holds the block table and pooled keys of the cache, which
+ * moba_decode_prepare computes (once per cache; a caller that keeps them
+ * up to date may skip it), plus per-call scratch. */
+size_t moba_decode_workspace_size(const moba_shape_t *cache_shape, int32_t block_size,
+                                  int32_t topk);
+moba_status_t moba_decode_prepare(const void *k_cache, const int32_t *cu_seqlens,
+                                  const moba_shape_t *cache_shape, int32_t block_size,
+                                  int32_t topk, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+moba_status_t moba_decode(const void *q, const void *k_cache, const void *v_cache,
+                          const moba_shape_t *cache_shape, int32_t block_size, int32_t topk,
+                          float softmax_scale, void *out, float *lse, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* ---- Dense causal attention on the same layout ("Standard Attention
  * Baseline" with a causal mask, per sequence): the full-attention reference
  * the pages compare MoBA against. workspace may be NULL (then scratch is

@@ -123,3 +123,50 @@ def test_status_strings():
     L = moba.lib()
     for code, name in moba.STATUS.items():
         assert L.moba_status_string(code).decode() == name
+
+
+def test_gate_variant_validation():
+    L = moba.lib()
+    sh = shape()
+    lay = moba.moba_plan(sh, 4096, 12)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # window: n_sink must lie in [0, topk)
+    assert L.moba_gate_window(ctypes.byref(sh), 4096, 12, 12, ctypes.byref(lay), fake, 0,
+                              None) == 1
+    assert L.moba_gate_window(ctypes.byref(sh), 4096, 12, -1, ctypes.byref(lay), fake, 0,
+                              None) == 1
+    # pooled: the own block needs a slot; extras are bounded
+    assert L.moba_gate_pooled(fake, ctypes.byref(sh), 4096, 12, 6, 6, ctypes.byref(lay), fake,
+                              0, None) == 1
+    assert L.moba_gate_pooled(fake, ctypes.byref(sh), 4096, 12, 17, 0, ctypes.byref(lay), fake,
+                              0, None) == 2
+    assert L.moba_gate_pooled(None, ctypes.byref(sh), 4096, 12, 1, 1, ctypes.byref(lay), fake,
+                              0, None) == 1
+    # moba_fwd_gated: NULL gate, unknown kind
+    assert L.moba_fwd_gated(fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, None, 0.0, fake,
+                            None, fake, 1 << 40, None) == 1
+    bad = moba.Gate(7, 0, 0, 0)
+    assert L.moba_fwd_gated(fake, fake, fake, fake, ctypes.byref(sh), 4096, 12,
+                            ctypes.byref(bad), 0.0, fake, None, fake, 1 << 40, None) == 1
+    assert b"gate" in L.moba_last_error()
+
+
+def test_decode_validation_and_sizes():
+    L = moba.lib()
+    cache = shape(T=1 << 20, S=1)
+    n = moba.moba_decode_workspace_size(cache, 4096, 12)
+    assert n > 0
+    # workspace grows with topk (slots), and a dense topk is accepted for decode
+    assert moba.moba_decode_workspace_size(cache, 4096, 256) > n
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moba_decode(fake, fake, fake, ctypes.byref(cache), 4096, 12, 0.0, fake, None, fake,
+                         16, None) == 3
+    assert L.moba_decode(None, fake, fake, ctypes.byref(cache), 4096, 12, 0.0, fake, None, fake,
+                         n, None) == 1
+    assert L.moba_decode(fake, fake, fake, ctypes.byref(cache), 4096, 0, 0.0, fake, None, fake,
+                         n, None) == 1
+    assert L.moba_decode_prepare(fake, None, ctypes.byref(cache), 4096, 12, fake, n, None) == 1
+    # no sequences: nothing to do
+    empty = shape(T=0, S=0)
+    assert L.moba_decode(None, None, None, ctypes.byref(empty), 4096, 12, 0.0, None, None, None,
+                         moba.moba_decode_workspace_size(empty, 4096, 12), None) == 0
