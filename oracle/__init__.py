@@ -53,6 +53,8 @@ def _load():
         lib.oracle_minmaxpool.argtypes = [p, i32, i64, i32, i32, p, i32, i32, p, p]
         lib.oracle_select_pooled.argtypes = [p, i32, p, p, p, i64, i32, i32, i32, p, i32, i32,
                                              i32, i32, i32, p, i64, p, p]
+        lib.oracle_attend_bwd.argtypes = [p, p, p, p, i32, i64, i32, i32, i32, p, i32, i32, i32,
+                                          p, dbl, p, p, p]
         lib.oracle_dense_causal.argtypes = [p, p, p, i32, i64, i32, i32, i32, p, i32, p, i64,
                                             dbl, p, p]
         for f in (lib.oracle_meanpool, lib.oracle_select, lib.oracle_attend, lib.oracle_moba,
@@ -191,6 +193,27 @@ def attend(q, k, v, cu_seqlens, block_size, topk, sel, scale=None, rows=None):
     _load().oracle_attend(_ptr(q), _ptr(k), _ptr(v), bf, T, Hq, Hkv, d, _ptr(cu), cu.size - 1,
                           block_size, topk, _ptr(s), _ptr(r), n, scale, _ptr(out), _ptr(lse))
     return out, lse
+
+
+def attend_bwd(q, k, v, dout, cu_seqlens, block_size, topk, sel, scale=None):
+    """Gradients of the attention over a selection, all rows:
+    (dq[T][Hq][d], dk[T][Hkv][d], dv[T][Hkv][d]) in float64."""
+    bf = _check_inputs(q, k, v)
+    cu = _cu(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    s = np.ascontiguousarray(sel, dtype=np.int32)
+    assert s.shape == (T, Hq, topk)
+    go = np.ascontiguousarray(dout, dtype=np.float64)
+    assert go.shape == (T, Hq, d)
+    dq = np.zeros((T, Hq, d))
+    dk = np.zeros((T, Hkv, d))
+    dv = np.zeros((T, Hkv, d))
+    _load().oracle_attend_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(go), bf, T, Hq, Hkv, d, _ptr(cu),
+                              cu.size - 1, block_size, topk, _ptr(s), scale, _ptr(dq), _ptr(dk),
+                              _ptr(dv))
+    return dq, dk, dv
 
 
 def moba(q, k, v, cu_seqlens, block_size, topk, scale=None, rows=None):
