@@ -43,8 +43,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "86d86b8ff9ec5a4412b0b42585e002b92228c91a44482e4eab60e8b6a8e63af9",
-    "fetch_kib": 22811532.7, "write_kib": 25406642.5,
+    "sha256": "dd1dbb1a97ebd7f47d3a11ab1b9a4e9e24b2bd40a7b05c6b49558a98ec694f54",
+    "fetch_kib": 18382821.3, "write_kib": 25358787.8,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 
