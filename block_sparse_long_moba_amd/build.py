@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoba.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "prep.hip", "gate.hip", "dispatch.hip", "attn.hip", "decode.hip"]
+SOURCES = ["api.hip", "prep.hip", "gate.hip", "dispatch.hip", "attn.hip", "decode.hip", "bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <string>
 
+#include "bwd.h"
 #include "moba_internal.h"
 
 using namespace moba;
@@ -146,6 +147,23 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   L->items_offset = off;     off = align_up(off + sizeof(uint32_t) * (size_t)std::max<int64_t>(1, hist_items));
   L->part_o_offset = off;    off = align_up(off + es * (size_t)slots * kHeadDim);
   L->part_lse_offset = off;  off = align_up(off + sizeof(float) * (size_t)slots);
+  L->total_bytes = off;
+  return MOBA_SUCCESS;
+}
+
+// Backward plan: the forward plan up to the items, then fp32 partial dq per
+// slot (in place of the partial outputs) and D per (head, row) (in place of
+// their lse). The vt region holds K^T.
+moba_status_t bwd_plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_req,
+                            moba_layout_t *L) {
+  moba_status_t st = plan_impl(sh, B, k, P_req, L);
+  if (st != MOBA_SUCCESS) return st;
+  const int64_t T = sh->total_tokens;
+  const int64_t slots = T * L->q_heads_per_pass * k;
+  size_t off = L->part_o_offset;
+  off = align_up(off + sizeof(float) * (size_t)slots * kHeadDim);
+  L->part_lse_offset = off;
+  off = align_up(off + sizeof(float) * (size_t)T * sh->num_q_heads);
   L->total_bytes = off;
   return MOBA_SUCCESS;
 }
@@ -602,6 +620,78 @@ moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int
                           void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
   const moba_gate_t mean{MOBA_GATE_MEAN, 0, 0, 0};
   return moba_fwd_gated(q, k, v, cu, sh, B, topk, &mean, scale, out, lse, ws, ws_bytes, s);
+}
+
+moba_status_t moba_bwd_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                            int32_t kv_heads_per_pass, moba_layout_t *layout) {
+  if (!layout) return fail(MOBA_ERROR_INVALID_VALUE, "layout is NULL");
+  return bwd_plan_impl(shape, block_size, topk, kv_heads_per_pass, layout);
+}
+
+size_t moba_bwd_workspace_size(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                               int32_t kv_heads_per_pass) {
+  moba_layout_t L;
+  if (bwd_plan_impl(shape, block_size, topk, kv_heads_per_pass, &L) != MOBA_SUCCESS) return 0;
+  return L.total_bytes;
+}
+
+moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *out,
+                       const float *lse, const void *dout, const int32_t *cu,
+                       const moba_shape_t *sh, int32_t B, int32_t topk, const moba_gate_t *gate,
+                       float scale, void *dq, void *dk, void *dv, void *ws, size_t ws_bytes,
+                       hipStream_t s) {
+  moba_status_t st = check_moba_args(sh, B, topk);
+  if (st != MOBA_SUCCESS) return st;
+  const moba_gate_t mean{MOBA_GATE_MEAN, 0, 0, 0};
+  if (!gate) gate = &mean;
+  if ((st = check_gate(gate, topk)) != MOBA_SUCCESS) return st;
+  if (sh->dtype != MOBA_DTYPE_BF16)
+    return fail(MOBA_ERROR_UNSUPPORTED, "backward pass: bf16 only");
+  if ((st = check_io(q, k, v, cu, out, sh)) != MOBA_SUCCESS) return st;
+  if (sh->total_tokens > 0 && (!lse || !dout || !dq || !dk || !dv))
+    return fail(MOBA_ERROR_INVALID_VALUE, "lse, dout, dq, dk and dv must be non-NULL");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  moba_layout_t L;
+  if ((st = bwd_plan_impl(sh, B, topk, sh->num_kv_heads, &L)) != MOBA_SUCCESS) return st;
+  while (L.total_bytes > ws_bytes && L.kv_heads_per_pass > 1) {
+    if ((st = bwd_plan_impl(sh, B, topk, L.kv_heads_per_pass - 1, &L)) != MOBA_SUCCESS) return st;
+  }
+  if (L.total_bytes > ws_bytes)
+    return fail(MOBA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes; need at least %zu",
+                ws_bytes, L.total_bytes);
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if (!ws) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
+  Problem pb = make_problem(sh, B, topk, scale, &L);
+  Work w = carve(pb, &L, ws);
+  BwdWork bw{(float *)((char *)ws + L.part_o_offset), (float *)((char *)ws + L.part_lse_offset)};
+  const BwdIo io{q, k, v, dout, lse, dq, dk, dv};
+  // the pooled gate keeps scratch lists in part_o and writes a per-slot lse
+  // in part_lse: both go to the partial-dq region (lists at its start, at
+  // most (topk + 2) ints per (row, head); the lse in its last slots floats),
+  // so D stays intact
+  const int64_t slots = pb.T * pb.Hp * topk;
+  w.part_o = bw.dq_part;
+  w.part_lse = bw.dq_part + slots * (kHeadDim - 1);
+  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
+  if (gate->kind != MOBA_GATE_WINDOW) MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
+  if (gate->kind == MOBA_GATE_POOLED) MOBA_HIP(launch_minmaxpool(pb, w, k, s), "minmaxpool");
+  MOBA_HIP(launch_bwd_delta(pb, out, dout, bw.delta, s), "bwd_delta");
+  for (int g0 = 0; g0 < pb.Hkv; g0 += pb.P) {
+    if (gate->kind == MOBA_GATE_WINDOW)
+      MOBA_HIP(launch_gate_window(pb, w, gate->n_sink, s), "gate_window");
+    else if (gate->kind == MOBA_GATE_POOLED)
+      MOBA_HIP(launch_gate_pooled(pb, w, q, g0, gate->extra_max, gate->extra_min, s),
+               "gate_pooled");
+    else
+      MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
+    MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
+    MOBA_HIP(launch_vtrans(k, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+             "ktrans");
+    MOBA_HIP(launch_bwd_dq(pb, w, bw, io, g0, s), "bwd_dq");
+    MOBA_HIP(launch_bwd_dq_sum(pb, w, bw, io, g0, s), "bwd_dq_sum");
+    MOBA_HIP(launch_bwd_dkdv(pb, w, bw, io, g0, s), "bwd_dkdv");
+  }
+  return MOBA_SUCCESS;
 }
 
 size_t moba_decode_workspace_size(const moba_shape_t *cache_shape, int32_t block_size,

@@ -1,0 +1,607 @@
+// Backward pass of the block-sparse attention on the matrix cores (bf16).
+//
+// MoBA summary page (paper-graph-ui), section 3.4: every query attends, with
+// one softmax, over the union of its own block (causally) and the earlier
+// blocks its gate chose. The choice is discrete, so gradients reach q, k and v
+// through that attention only and the gate receives none. With
+// P = softmax(scale q K^T) over the union, O = P V and D = <dO, O> per
+// (row, head):
+//   dS = P (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// P is recomputed from the forward pass's log-sum-exp; nothing of the forward
+// pass is stored besides O and the lse.
+//
+// Two orientations, no atomics, fixed summation order:
+// - rows resident (bwd_dq_kernel): the forward pass's work split (own block:
+//   256 query rows of one head per workgroup, causal; earlier blocks: a tile of
+//   up to 256 gathered rows of one bin), keys streamed through LDS in tiles of
+//   64. Per tile S^T = K Q^T, dP^T = V dO^T, dS, and dQ^T += K^T dS^T (K^T
+//   comes pre-transposed per block, like V^T in the forward pass). Each
+//   (row, head, slot) gets an fp32 partial dQ; a sum over the slots follows.
+// - keys resident (bwd_dkdv_kernel): one workgroup per (kv head, block, chunk
+//   of 256 keys), 8 waves of 32 keys with K and V in registers as MFMA B
+//   operands. The block's own rows (for each query head of the kv head,
+//   causally) and then the rows of its bin stream through LDS in tiles of 32
+//   rows, stored both row-major and transposed. Per tile S = Q K^T,
+//   dP = dO V^T, dS, dV^T += dO^T P and dK^T += Q^T dS; dK and dV are written
+//   once.
+// Lane layouts: v_mfma_f32_32x32x16_bf16, lane l holds A[m = l%32][k = 8(l/32)
+// .. +7] and B[k = 8(l/32) .. +7][n = l%32]; accumulator i of lane l is
+// C[8(i/4) + 4(l/32) + i%4][l%32]. Feeding M-row m from source row perm(m)
+// (bits 2 and 3 swapped) makes accumulator i of lane half hh hold source row
+// 16(i/8) + 8hh + i%8: two runs of 8 consecutive rows, exactly the 8-wide K
+// slices the next product takes from the same lane.
+#include <math.h>
+
+#include "bwd.h"
+
+namespace moba {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
+constexpr int kDqRows = kRowsBf16;        // query rows per dQ workgroup (8 waves x 32)
+constexpr int kKvKeys = 256;              // keys per dK/dV workgroup (8 waves x 32)
+constexpr int kKvRows = 32;               // rows per dK/dV tile
+
+enum { BWD_HIST = 0, BWD_DIAG = 1 };
+
+struct BwdArgs {
+  const __bf16 *q, *k, *v, *kt, *dout;
+  const float *lse, *delta;  // [Hq][T]
+  int64_t T;
+  int Hq, Hkv, G, B, topk;
+  float c2, scale;  // c2 = scale * log2(e)
+  int g0, h0, Hp;
+  int64_t NBb, nbins;
+  const int4 *info;
+  const uint32_t *tile_off, *bin_off, *items;
+  const int4 *tile_rec;
+  float *dq_part;
+  __bf16 *dk, *dv;
+};
+
+__device__ __forceinline__ floatx16 mfma(const bf16x8 &a, const bf16x8 &b, const floatx16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int perm32(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Raw buffer descriptor from wave-uniform values; offsets past `bytes` read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, int64_t bytes) {
+  const uint64_t v = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7fffffff ? bytes : 0x7fffffff));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           kBufferWord3);
+}
+
+// Wait for every vector memory load of the wave (and its LDS accesses).
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x70); }
+
+__device__ __forceinline__ void store_bf16x4(__bf16 *p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  *(bf16x4 *)p = v;
+}
+
+// D[h][t] = <dO[t][h], O[t][h]> in fp32; 16 lanes per (row, head), rows
+// ordered head-major so a workgroup writes 16 consecutive entries.
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16 *__restrict__ out,
+                                                        const __bf16 *__restrict__ dout,
+                                                        int64_t T, int Hq,
+                                                        float *__restrict__ delta) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= T * Hq) return;
+  const int lane = threadIdx.x & 15;
+  const int h = (int)(row / T);
+  const int64_t t = row - (int64_t)h * T;
+  const int64_t off = (t * Hq + h) * kHeadDim + lane * 8;
+  const bf16x8 o = *(const bf16x8 *)(out + off);
+  const bf16x8 g = *(const bf16x8 *)(dout + off);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += (float)o[j] * (float)g[j];
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  s += __shfl_xor(s, 8);
+  if (lane == 0) delta[row] = s;
+}
+
+// ---- dQ: rows resident, keys streamed.
+//
+// LDS: two stages of {K tile, V tile, K^T tile}, 16 KiB each. K and V tiles
+// are 64 rows x 16 chunks of 16 B, chunk c of row r at position c ^ (r & 15);
+// the K^T tile is 128 rows (d) x 8 chunks (of 8 keys), chunk c of row r at
+// c ^ ((r >> 1) & 7). Every wave fills 2 KiB of each with direct loads.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
+  constexpr int TILE = 16384, STAGE = 3 * TILE, LPW = 2;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int r = wave * 32 + n;  // this lane's query row inside the tile
+
+  int g, p, nkt, nrows, hq, qpos = 0;
+  int64_t t, kbeg, slot, gb;
+  if (MODE == BWD_HIST) {
+    // the forward pass's tiles of its earlier-block attention, XCD-contiguous
+    const uint32_t ntiles = a.tile_off[a.nbins];
+    const uint32_t per = (ntiles + 7) >> 3;
+    const uint32_t jj = blockIdx.x >> 3;
+    if (jj >= per) return;
+    const uint32_t tile = (blockIdx.x & 7) * per + jj;
+    if (tile >= ntiles) return;
+    const int4 rec = a.tile_rec[tile];
+    p = (int)((uint32_t)rec.z / a.NBb);
+    gb = (uint32_t)rec.z % a.NBb;
+    nrows = rec.y;
+    slot = a.items[(uint32_t)rec.x + (r < nrows ? r : 0)];
+    const int64_t th = slot / a.topk;
+    t = th / a.Hp;
+    hq = a.h0 + (int)(th % a.Hp);
+    g = a.g0 + p;
+    kbeg = rec.w;
+    nkt = a.B / kKeyTile;
+  } else {
+    // (kv head of the pass, block, query tile with the most keys first, query
+    // head of the group); every XCD takes a contiguous run
+    const int nq = (a.B + kDqRows - 1) / kDqRows;
+    const uint32_t total = (uint32_t)(a.Hp * a.NBb * nq);
+    const uint32_t per = (total + 7) >> 3;
+    const uint32_t jj = blockIdx.x >> 3;
+    if (jj >= per) return;
+    const uint32_t wi = (blockIdx.x & 7) * per + jj;
+    if (wi >= total) return;
+    uint32_t rest = wi / (uint32_t)a.G;
+    const int qt = nq - 1 - (int)(rest % (uint32_t)nq);
+    rest /= (uint32_t)nq;
+    gb = rest % (uint32_t)a.NBb;
+    const int hl = (int)(rest / (uint32_t)a.NBb) * a.G + (int)(wi % (uint32_t)a.G);
+    const int4 bi = a.info[gb];
+    if (bi.x < 0 || qt * kDqRows >= bi.z) return;
+    hq = a.h0 + hl;
+    g = hq / a.G;
+    p = g - a.g0;
+    nrows = min(kDqRows, bi.z - qt * kDqRows);
+    const int qfirst = qt * kDqRows;
+    qpos = qfirst + r;
+    t = bi.y + qfirst + (r < nrows ? r : 0);
+    nkt = (min(bi.z, qfirst + kDqRows) + kKeyTile - 1) / kKeyTile;
+    kbeg = bi.y;
+    const int nsel = min(a.topk, bi.w + 1);  // the own block is the last chosen slot
+    slot = (t * a.Hp + hl) * a.topk + nsel - 1;
+  }
+
+  // this lane's query row and output gradient as B operands (k = d)
+  bf16x8 qB[8], doB[8];
+  {
+    const int64_t off = (t * a.Hq + hq) * kHeadDim + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qB[kk] = *(const bf16x8 *)(a.q + off + 16 * kk);
+      doB[kk] = *(const bf16x8 *)(a.dout + off + 16 * kk);
+    }
+  }
+  const float lse2 = a.lse[(int64_t)hq * a.T + t] * kLog2e;
+  const float Dr = a.delta[(int64_t)hq * a.T + t];
+  const float c2 = a.c2;
+
+  // direct-load sources (byte offsets from the tile base): K and V regions
+  // are 4 rows, K^T regions 8 rows
+  const int64_t kstride = (int64_t)a.Hkv * kHeadDim;
+  uint32_t kso[LPW], tso[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int region = wave * LPW + j;
+    const int krow = region * 4 + (lane >> 4);
+    kso[j] = (uint32_t)krow * (uint32_t)kstride * 2u + (uint32_t)(((lane & 15) ^ (krow & 15)) * 16);
+    const int trow = region * 8 + (lane >> 3);
+    tso[j] = (uint32_t)trow * (uint32_t)a.B * 2u + (uint32_t)(((lane & 7) ^ ((trow >> 1) & 7)) * 16);
+  }
+  char *const lds_w = lds + wave * LPW * 1024;
+  const __bf16 *kt0 = a.k + kbeg * kstride + (int64_t)g * kHeadDim;
+  const __bf16 *vt0 = a.v + kbeg * kstride + (int64_t)g * kHeadDim;
+  const __bf16 *tt0 = a.kt + ((int64_t)p * a.NBb + gb) * kHeadDim * a.B;
+  const int64_t span = (a.T - kbeg) * kstride * 2;  // bytes to the end of the tensor (upper bound)
+  const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(kt0, span);
+  const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(vt0, span);
+  const __amdgpu_buffer_rsrc_t trs = uniform_rsrc(tt0, (int64_t)kHeadDim * a.B * 2);
+  auto issue = [&](int kt, int stage) {
+    const uint32_t soff = (uint32_t)kt * kKeyTile * (uint32_t)kstride * 2u;
+    const uint32_t toff = (uint32_t)kt * kKeyTile * 2u;
+    char *base = lds_w + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(base + j * 1024), 16, kso[j], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(base + TILE + j * 1024), 16, kso[j], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (lds_ptr_t)(base + 2 * TILE + j * 1024), 16, tso[j], toff, 0, 0);
+    }
+  };
+  // LDS read offsets of this lane's A operands
+  const int pr = perm32(n);
+  uint32_t krd[8], trd[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) krd[kk] = pr * 256 + (((2 * kk + hh) ^ (pr & 15)) * 16);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) trd[c] = n * 128 + (((2 * c + hh) ^ ((n >> 1) & 7)) * 16);
+
+  floatx16 dq[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[dt][i] = 0.f;
+
+  auto compute = [&](int kt, int stage) {
+    const char *Ks = lds + stage * STAGE;
+    const char *Vs = Ks + TILE;
+    const char *Ts = Ks + 2 * TILE;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      floatx16 sc, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { sc[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        sc = mfma(*(const bf16x8 *)(Ks + st * 8192 + krd[kk]), qB[kk], sc);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        dp = mfma(*(const bf16x8 *)(Vs + st * 8192 + krd[kk]), doB[kk], dp);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * c + j;
+          float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], c2, -lse2));
+          if (MODE == BWD_DIAG && kt * kKeyTile + 32 * st + 16 * c + 8 * hh + j > qpos) pv = 0.f;
+          b[j] = (__bf16)(pv * (dp[i] - Dr));
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          dq[dt] = mfma(*(const bf16x8 *)(Ts + dt * 4096 + trd[2 * st + c]), b, dq[dt]);
+      }
+      // keep the two halves apart: interleaving them costs registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  issue(0, 0);
+  wait_all_loads();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    if (kt + 1 < nkt) issue(kt + 1, 1);
+    compute(kt, 0);
+    wait_all_loads();
+    __syncthreads();
+    if (kt + 1 < nkt) {
+      if (kt + 2 < nkt) issue(kt + 2, 0);
+      compute(kt + 1, 1);
+      wait_all_loads();
+      __syncthreads();
+    }
+  }
+
+  if (r >= nrows) return;
+  float *dst = a.dq_part + slot * kHeadDim + 4 * hh;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa)
+      *(float4 *)(dst + 32 * dt + 8 * aa) =
+          make_float4(dq[dt][4 * aa] * sc, dq[dt][4 * aa + 1] * sc, dq[dt][4 * aa + 2] * sc,
+                      dq[dt][4 * aa + 3] * sc);
+}
+
+__device__ __forceinline__ int seq_of(const int32_t *cu, int S, int64_t t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// dQ[t][h] = sum of the partials of its slots: the own block (last chosen
+// slot) first, then the earlier blocks in slot order (those the dispatch
+// stage routed: 0 <= block < own). 32 lanes per (row, head).
+__global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict__ dq_part,
+                                                         const int32_t *__restrict__ idx,
+                                                         const int32_t *__restrict__ cu, int S,
+                                                         int64_t T, int Hq, int h0, int Hp, int B,
+                                                         int k, __bf16 *__restrict__ dq) {
+  const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (row >= T * Hp) return;
+  const int lane = threadIdx.x & 31;
+  const int64_t t = row / Hp;
+  const int hl = (int)(row % Hp);
+  const int s = seq_of(cu, S, t);
+  const int c = (int)((t - cu[s]) / B);
+  const int nsel = min(k, c + 1);
+  const float *base = dq_part + row * k * kHeadDim + lane * 4;
+  float4 acc = *(const float4 *)(base + (int64_t)(nsel - 1) * kHeadDim);
+  const int32_t *sel = idx + row * k;
+  for (int i = 0; i < nsel - 1; ++i) {
+    const int j = sel[i];
+    if (j >= 0 && j < c) {
+      const float4 x = *(const float4 *)(base + (int64_t)i * kHeadDim);
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+  }
+  store_bf16x4(dq + (t * Hq + h0 + hl) * kHeadDim + lane * 4, acc.x, acc.y, acc.z, acc.w);
+}
+
+// ---- dK, dV: keys resident, rows streamed.
+//
+// LDS per stage: Q and dO tiles row-major (32 rows of 256 B at a pitch of
+// 272 B), then Q^T and dO^T (128 rows (d) of 32 elements at a pitch of 80 B);
+// after both stages, per stage the 32 rows' lse (log2 units) and D. The
+// padding makes the 16 rows (or d rows) that 16 lanes read at one chunk
+// column fall in 16 different 16-byte bank groups, and every lane's operand
+// addresses a base plus compile-time offsets. Rows past the end of a tile
+// have q = dO = 0, lse = +inf and D = 0, so their probabilities and dS are
+// exactly 0.
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int NP = 272, TP = 80;  // pitches of the row-major and transposed tiles
+  constexpr int QN = 0, DN = 32 * NP, QT = 64 * NP, DTT = 64 * NP + 128 * TP;
+  constexpr int STAGE = 64 * NP + 256 * TP, LD = 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE + 2 * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int nch = (a.B + kKvKeys - 1) / kKvKeys;
+  // workgroup x: bin 8 * ((x / 8) / nch) + x % 8, chunk (x / 8) % nch; every
+  // XCD takes every 8th bin, the chunks of one bin back to back
+  const int64_t xg = blockIdx.x >> 3;
+  const int64_t b = (xg / nch) * 8 + (blockIdx.x & 7);
+  const int kc = (int)(xg % nch);
+  if (b >= a.nbins) return;
+  const int p = (int)(b / a.NBb);
+  const int64_t gb = b % a.NBb;
+  const int4 bi = a.info[gb];
+  if (bi.x < 0 || kc * kKvKeys >= bi.z) return;
+  const int g = a.g0 + p;
+  const int k0 = kc * kKvKeys;
+  const int kw = k0 + 32 * wave;  // first key of this wave, local to the block
+  const int key = kw + n;
+  const bool kvalid = key < bi.z;
+
+  // K and V rows of this lane's key as MFMA B operands (k = d); a lane past
+  // the block's end takes the block's first row (its results are dropped)
+  bf16x8 kB[8], vB[8];
+  {
+    const int64_t off = ((int64_t)(bi.y + (kvalid ? key : 0)) * a.Hkv + g) * kHeadDim + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      kB[kk] = *(const bf16x8 *)(a.k + off + 16 * kk);
+      vB[kk] = *(const bf16x8 *)(a.v + off + 16 * kk);
+    }
+  }
+  floatx16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.f; dv[dt][i] = 0.f; }
+
+  // tiles: the own block's rows from k0 on, per query head of the kv head,
+  // then the bin's items
+  const int own_per_head = (bi.z - k0 + kKvRows - 1) / kKvRows;
+  const int n_own = a.G * own_per_head;
+  const uint32_t ibeg = a.bin_off[b], iend = a.bin_off[b + 1];
+  const int ntiles = n_own + (int)((iend - ibeg + kKvRows - 1) / kKvRows);
+
+  // loader: thread (row lr, chunk lc of 8 elements)
+  const int lr = threadIdx.x & 31, lc = threadIdx.x >> 5;
+  auto item_of = [&](int it) -> uint32_t {
+    if (it < n_own || it >= ntiles) return 0u;
+    const uint32_t j = ibeg + (uint32_t)(it - n_own) * kKvRows + lr;
+    return a.items[j < iend ? j : iend - 1];
+  };
+  bf16x8 sq, sdo;
+  float sl = 0.f, sd = 0.f;
+  bool sok = false;
+  auto fetch = [&](int it, uint32_t item) {
+    int64_t t;
+    int h;
+    if (it < n_own) {
+      const int gi = it / own_per_head;
+      const int rl = k0 + (it - gi * own_per_head) * kKvRows + lr;
+      sok = rl < bi.z;
+      t = bi.y + (sok ? rl : k0);
+      h = a.h0 + p * a.G + gi;
+    } else {
+      const uint32_t j = ibeg + (uint32_t)(it - n_own) * kKvRows + lr;
+      sok = j < iend;
+      const int64_t row = (int64_t)item / a.topk;
+      t = row / a.Hp;
+      h = a.h0 + (int)(row % a.Hp);
+    }
+    const int64_t off = (t * a.Hq + h) * kHeadDim + 8 * lc;
+    sq = *(const bf16x8 *)(a.q + off);
+    sdo = *(const bf16x8 *)(a.dout + off);
+    if (lc == 0) {
+      sl = a.lse[(int64_t)h * a.T + t] * kLog2e;
+      sd = a.delta[(int64_t)h * a.T + t];
+    }
+  };
+  auto stash = [&](int stage) {
+    char *S_ = lds + stage * STAGE;
+    if (!sok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { sq[e] = (__bf16)0.f; sdo[e] = (__bf16)0.f; }
+    }
+    *(bf16x8 *)(S_ + QN + lr * NP + lc * 16) = sq;
+    *(bf16x8 *)(S_ + DN + lr * NP + lc * 16) = sdo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int off = (8 * lc + e) * TP + lr * 2;
+      *(__bf16 *)(S_ + QT + off) = sq[e];
+      *(__bf16 *)(S_ + DTT + off) = sdo[e];
+    }
+    if (lc == 0) {
+      float *L = (float *)(lds + LD + stage * 256);
+      L[lr] = sok ? sl : INFINITY;
+      L[32 + lr] = sok ? sd : 0.f;
+    }
+  };
+
+  // LDS read offsets: Q / dO rows as A operands of S and dP (row perm(n));
+  // Q^T / dO^T rows (d = 32 dt + n) as A operands of dK^T and dV^T
+  const int qrd = perm32(n) * NP + hh * 16;  // + 32 kk: chunk 2 kk + hh
+  const int trd = n * TP + hh * 16;          // + 2560 dt + 32 c: rows 16 c + 8 hh ..
+  const float c2 = a.c2;
+
+  auto compute = [&](int it, int stage) {
+    if (kw >= bi.z) return;  // every key of this wave is past the block's end
+    const bool own = it < n_own;
+    int rt = 0;  // local position of the tile's first row (own tiles)
+    if (own) {
+      const int gi = it / own_per_head;
+      rt = k0 + (it - gi * own_per_head) * kKvRows;
+      if (rt + kKvRows - 1 < kw) return;  // every row precedes every key of this wave
+    }
+    const char *S_ = lds + stage * STAGE;
+    const float *L = (const float *)(lds + LD + stage * 256);
+    floatx16 s, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = mfma(*(const bf16x8 *)(S_ + QN + qrd + 32 * kk), kB[kk], s);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) dp = mfma(*(const bf16x8 *)(S_ + DN + qrd + 32 * kk), vB[kk], dp);
+    bf16x8 pb[2], db[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      // accumulators 8c .. 8c+7 hold rows 16c + 8hh .. +7 of the tile
+      const float4 l0 = *(const float4 *)(L + 16 * c + 8 * hh);
+      const float4 l1 = *(const float4 *)(L + 16 * c + 8 * hh + 4);
+      const float4 d0 = *(const float4 *)(L + 32 + 16 * c + 8 * hh);
+      const float4 d1 = *(const float4 *)(L + 32 + 16 * c + 8 * hh + 4);
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = 8 * c + j;
+        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[j]));
+        if (own && key > rt + 16 * c + 8 * hh + j) pv = 0.f;
+        pb[c][j] = (__bf16)pv;
+        db[c][j] = (__bf16)(pv * (dp[i] - dd[j]));
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dv[dt] = mfma(*(const bf16x8 *)(S_ + DTT + trd + dt * 32 * TP + 32 * c), pb[c], dv[dt]);
+        dk[dt] = mfma(*(const bf16x8 *)(S_ + QT + trd + dt * 32 * TP + 32 * c), db[c], dk[dt]);
+      }
+  };
+
+  if (ntiles > 0) {
+    fetch(0, item_of(0));
+    stash(0);
+    __syncthreads();
+    uint32_t nxt = item_of(1);
+    for (int it = 0; it < ntiles; ++it) {
+      const int stage = it & 1;
+      const bool more = it + 1 < ntiles;
+      if (more) fetch(it + 1, nxt);
+      nxt = item_of(it + 2);
+      compute(it, stage);
+      if (more) stash(stage ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (!kvalid) return;
+  const int64_t o = ((int64_t)(bi.y + key) * a.Hkv + g) * kHeadDim + 4 * hh;
+  const float sc = a.scale;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      store_bf16x4(a.dk + o + 32 * dt + 8 * aa, dk[dt][4 * aa] * sc, dk[dt][4 * aa + 1] * sc,
+                   dk[dt][4 * aa + 2] * sc, dk[dt][4 * aa + 3] * sc);
+      store_bf16x4(a.dv + o + 32 * dt + 8 * aa, dv[dt][4 * aa], dv[dt][4 * aa + 1],
+                   dv[dt][4 * aa + 2], dv[dt][4 * aa + 3]);
+    }
+}
+
+BwdArgs make_args(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io, int g0) {
+  BwdArgs a{};
+  a.q = (const __bf16 *)io.q;
+  a.k = (const __bf16 *)io.k;
+  a.v = (const __bf16 *)io.v;
+  a.kt = (const __bf16 *)w.vt;
+  a.dout = (const __bf16 *)io.dout;
+  a.lse = io.lse;
+  a.delta = bw.delta;
+  a.T = pb.T;
+  a.Hq = pb.Hq; a.Hkv = pb.Hkv; a.G = pb.G; a.B = pb.B; a.topk = pb.k;
+  a.scale = pb.scale;
+  a.c2 = pb.scale * kLog2e;
+  a.g0 = g0; a.h0 = g0 * pb.G; a.Hp = pb.Hp;
+  a.NBb = pb.NBb;
+  a.nbins = (int64_t)pb.P * pb.NBb;
+  a.info = w.blk_info;
+  a.tile_off = w.tile_off; a.bin_off = w.bin_off; a.items = w.items; a.tile_rec = w.tile_rec;
+  a.dq_part = bw.dq_part;
+  a.dk = (__bf16 *)io.dk;
+  a.dv = (__bf16 *)io.dv;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_delta(const Problem &pb, const void *out, const void *dout, float *delta,
+                            hipStream_t s) {
+  const int64_t rows = pb.T * pb.Hq;
+  if (rows == 0) return hipSuccess;
+  bwd_delta_kernel<<<dim3((unsigned)((rows + 15) / 16)), 256, 0, s>>>(
+      (const __bf16 *)out, (const __bf16 *)dout, pb.T, pb.Hq, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io,
+                         int g0, hipStream_t s) {
+  const BwdArgs a = make_args(pb, w, bw, io, g0);
+  const int64_t nq = (pb.B + kDqRows - 1) / kDqRows;
+  const int64_t gdiag = (pb.Hp * pb.NBb * nq + 7) / 8 * 8;
+  bwd_dq_kernel<BWD_DIAG><<<dim3((unsigned)gdiag), 512, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pb.k <= 1) return e;
+  const int64_t ghist = (w.max_tiles + 7) / 8 * 8;
+  bwd_dq_kernel<BWD_HIST><<<dim3((unsigned)ghist), 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_sum(const Problem &pb, const Work &w, const BwdWork &bw,
+                             const BwdIo &io, int g0, hipStream_t s) {
+  const int64_t rows = pb.T * pb.Hp;
+  if (rows == 0) return hipSuccess;
+  bwd_dq_sum_kernel<<<dim3((unsigned)((rows + 7) / 8)), 256, 0, s>>>(
+      bw.dq_part, w.idx, w.cu, pb.S, pb.T, pb.Hq, g0 * pb.G, pb.Hp, pb.B, pb.k,
+      (__bf16 *)io.dq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io,
+                           int g0, hipStream_t s) {
+  const BwdArgs a = make_args(pb, w, bw, io, g0);
+  const int64_t nch = (pb.B + kKvKeys - 1) / kKvKeys;
+  const int64_t grid = (a.nbins + 7) / 8 * 8 * nch;
+  bwd_dkdv_kernel<<<dim3((unsigned)grid), 512, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moba

@@ -23,6 +23,7 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_works
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
            "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
            "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
+           "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd",
            "moba_dense_causal_workspace_size", "moba_dense_causal_fwd"]
 
 GATE_MEAN, GATE_WINDOW, GATE_POOLED = 0, 1, 2
@@ -106,6 +107,10 @@ def lib():
             "moba_decode_workspace_size": ([S, I32, I32], Z),
             "moba_decode_prepare": ([P, P, S, I32, I32, P, Z, P], I32),
             "moba_decode": ([P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
+            "moba_bwd_plan": ([S, I32, I32, I32, LP], I32),
+            "moba_bwd_workspace_size": ([S, I32, I32, I32], Z),
+            "moba_bwd": ([P, P, P, P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, P,
+                          Z, P], I32),
             "moba_dense_causal_workspace_size": ([S], Z),
             "moba_dense_causal_fwd": ([P, P, P, P, S, F, P, P, P, Z, P], I32),
         }
@@ -292,6 +297,34 @@ def moba_decode(q, k_cache, v_cache, cache_shape, block_size, topk, workspace, o
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream)))
     return out, lse
+
+
+def moba_bwd_plan(shape: Shape, block_size: int, topk: int, kv_heads_per_pass: int = 0) -> Layout:
+    lay = Layout()
+    _check(lib().moba_bwd_plan(ctypes.byref(shape), block_size, topk, kv_heads_per_pass,
+                               ctypes.byref(lay)))
+    return lay
+
+
+def moba_bwd_workspace_size(shape: Shape, block_size: int, topk: int,
+                            kv_heads_per_pass: int = 0) -> int:
+    return lib().moba_bwd_workspace_size(ctypes.byref(shape), block_size, topk, kv_heads_per_pass)
+
+
+def moba_bwd(q, k, v, out, lse, dout, cu_seqlens, block_size, topk, workspace, gate=None,
+             dq=None, dk=None, dv=None, softmax_scale=0.0, max_seqlen=0, stream=None):
+    """Gradients (dq, dk, dv) of the forward pass that wrote out and lse."""
+    import torch
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    _check(lib().moba_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                          _ptr(cu_seqlens), ctypes.byref(sh), block_size, topk,
+                          None if gate is None else ctypes.byref(gate), softmax_scale, _ptr(dq),
+                          _ptr(dk), _ptr(dv), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv
 
 
 def moba_dense_causal_workspace_size(shape: Shape) -> int:

@@ -315,6 +315,40 @@ moba_status_t moba_decode(const void *q, const void *k_cache, const void *v_cach
                           float softmax_scale, void *out, float *lse, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Backward pass (section 3.4: MoBA is trained end to end; gradients
+ * flow through the attention over the chosen blocks, and the block choice,
+ * a discrete top-k, passes none to the gate or the pooled keys).
+ * With P the softmax of the scaled logits over the query's chosen union (own
+ * block causal), D = <dO, O> per (row, head) and dS = P (dO V^T - D):
+ *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dO,
+ * each kv head summing over the query heads that read it.
+ * Inputs: q, k, v as for the forward pass; out [T][Hq][d] and lse [Hq][T]
+ * (natural log) as the forward pass with the same gate, block_size, topk
+ * and softmax_scale wrote them; dout [T][Hq][d]. Outputs dq [T][Hq][d],
+ * dk and dv [T][Hkv][d], all overwritten (element type of q). The gate is
+ * recomputed from q and k (it is deterministic), so out and lse must come
+ * from these very inputs; the probabilities are recomputed from lse.
+ * gate may be NULL (MOBA_GATE_MEAN). bf16 only: fp32 returns
+ * MOBA_ERROR_UNSUPPORTED. Same limits as the forward pass otherwise. */
+
+/* Host only. Workspace plan of the backward pass for a pass size (0 = all kv
+ * heads; see moba_plan): the forward plan's regions, except that the vt
+ * region holds K^T per block, part_o_offset is the fp32 partial dq of each
+ * (row, head, slot) ([T][Hp][topk][d]) and part_lse_offset is D ([Hq][T]
+ * float32). */
+moba_status_t moba_bwd_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                            int32_t kv_heads_per_pass, moba_layout_t *layout);
+/* Bytes of workspace moba_bwd needs for the given pass size; 0 if invalid. */
+size_t moba_bwd_workspace_size(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                               int32_t kv_heads_per_pass);
+/* Whole backward pass, in passes sized to fit workspace_bytes (at least
+ * moba_bwd_workspace_size(shape, block_size, topk, 1)). */
+moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *out,
+                       const float *lse, const void *dout, const int32_t *cu_seqlens,
+                       const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                       const moba_gate_t *gate, float softmax_scale, void *dq, void *dk,
+                       void *dv, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---- Dense causal attention on the same layout ("Standard Attention
  * Baseline" with a causal mask, per sequence): the full-attention reference
  * the pages compare MoBA against. workspace may be NULL (then scratch is

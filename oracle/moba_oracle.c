@@ -418,62 +418,66 @@ void oracle_attend_bwd(const void *q, const void *k, const void *v, const double
                        int is_bf16, int64_t T, int Hq, int Hkv, int d, const int32_t *cu, int S,
                        int B, int topk, const int32_t *sel, double scale, double *dq, double *dk,
                        double *dv) {
-  int G = Hq / Hkv;
+  const int G = Hq / Hkv;
   memset(dq, 0, sizeof(double) * (size_t)T * Hq * d);
   memset(dk, 0, sizeof(double) * (size_t)T * Hkv * d);
   memset(dv, 0, sizeof(double) * (size_t)T * Hkv * d);
   int64_t cap = (int64_t)topk * B + 1;
-  int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * cap);
-  double *z = (double *)malloc(sizeof(double) * cap);
-  double *dp = (double *)malloc(sizeof(double) * cap);
-  /* serial over (t, h): dk and dv receive contributions from many rows */
-  for (int64_t t = 0; t < T; ++t) {
-    int s = seq_of_row(cu, S, t);
-    int64_t a = cu[s], L = (int64_t)cu[s + 1] - cu[s], local = t - a, c = local / B;
-    for (int h = 0; h < Hq; ++h) {
-      int g = h / G;
-      const int32_t *my = sel + (t * Hq + h) * (int64_t)topk;
-      int64_t nk = 0;
-      for (int i = 0; i < topk; ++i) {
-        int64_t j = my[i];
-        if (j < 0) continue;
-        int64_t r0 = j * B, r1 = (j == c) ? local + 1 : ((j + 1) * B < L ? (j + 1) * B : L);
-        for (int64_t r = r0; r < r1; ++r) keys[nk++] = a + r;
-      }
-      double m = -INFINITY;
-      for (int64_t i = 0; i < nk; ++i) {
-        double acc = 0.0;
-        for (int e = 0; e < d; ++e)
-          acc += load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16) *
-                 load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
-        z[i] = scale * acc;
-        if (z[i] > m) m = z[i];
-      }
-      double l = 0.0;
-      for (int64_t i = 0; i < nk; ++i) { z[i] = exp(z[i] - m); l += z[i]; }
-      const double *go = dout + (t * Hq + h) * (int64_t)d;
-      double D = 0.0;
-      for (int64_t i = 0; i < nk; ++i) {
-        z[i] /= l;  /* P_u */
-        double acc = 0.0;
-        for (int e = 0; e < d; ++e) acc += go[e] * load_elem(v, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
-        dp[i] = acc;
-        D += z[i] * acc;
-      }
-      double *gq = dq + (t * Hq + h) * (int64_t)d;
-      for (int64_t i = 0; i < nk; ++i) {
-        double ds = z[i] * (dp[i] - D);
-        double *gk = dk + (keys[i] * Hkv + g) * (int64_t)d;
-        double *gv = dv + (keys[i] * Hkv + g) * (int64_t)d;
-        for (int e = 0; e < d; ++e) {
-          gq[e] += scale * ds * load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
-          gk[e] += scale * ds * load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16);
-          gv[e] += z[i] * go[e];
+  /* kv heads are independent (each owns its query heads' rows of dq and its
+   * own dk, dv); inside one, rows and heads run in order */
+#pragma omp parallel for schedule(static, 1)
+  for (int g = 0; g < Hkv; ++g) {
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * cap);
+    double *z = (double *)malloc(sizeof(double) * cap);
+    double *dp = (double *)malloc(sizeof(double) * cap);
+    for (int64_t t = 0; t < T; ++t) {
+      int s = seq_of_row(cu, S, t);
+      int64_t a = cu[s], L = (int64_t)cu[s + 1] - cu[s], local = t - a, c = local / B;
+      for (int h = g * G; h < (g + 1) * G; ++h) {
+        const int32_t *my = sel + (t * Hq + h) * (int64_t)topk;
+        int64_t nk = 0;
+        for (int i = 0; i < topk; ++i) {
+          int64_t j = my[i];
+          if (j < 0) continue;
+          int64_t r0 = j * B, r1 = (j == c) ? local + 1 : ((j + 1) * B < L ? (j + 1) * B : L);
+          for (int64_t r = r0; r < r1; ++r) keys[nk++] = a + r;
+        }
+        double m = -INFINITY;
+        for (int64_t i = 0; i < nk; ++i) {
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e)
+            acc += load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16) *
+                   load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+          z[i] = scale * acc;
+          if (z[i] > m) m = z[i];
+        }
+        double l = 0.0;
+        for (int64_t i = 0; i < nk; ++i) { z[i] = exp(z[i] - m); l += z[i]; }
+        const double *go = dout + (t * Hq + h) * (int64_t)d;
+        double D = 0.0;
+        for (int64_t i = 0; i < nk; ++i) {
+          z[i] /= l;  /* P_u */
+          double acc = 0.0;
+          for (int e = 0; e < d; ++e)
+            acc += go[e] * load_elem(v, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+          dp[i] = acc;
+          D += z[i] * acc;
+        }
+        double *gq = dq + (t * Hq + h) * (int64_t)d;
+        for (int64_t i = 0; i < nk; ++i) {
+          double ds = z[i] * (dp[i] - D);
+          double *gk = dk + (keys[i] * Hkv + g) * (int64_t)d;
+          double *gv = dv + (keys[i] * Hkv + g) * (int64_t)d;
+          for (int e = 0; e < d; ++e) {
+            gq[e] += scale * ds * load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+            gk[e] += scale * ds * load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16);
+            gv[e] += z[i] * go[e];
+          }
         }
       }
     }
+    free(keys); free(z); free(dp);
   }
-  free(keys); free(z); free(dp);
 }
 
 /* Full MoBA forward for a list of rows: meanpool, select, attend.

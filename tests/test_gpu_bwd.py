@@ -1,0 +1,164 @@
+"""GPU parity of the backward pass (dq, dk, dv) through the C ABI against the
+fp64 oracle's gradients over the same selection, on every element of small
+shapes that span several row and key tiles, ragged tails, empty and one-row
+sequences, GQA groups of 1 to 8, top-k 1, a top-k that covers every block,
+and the gate variants.
+
+Tolerance (bf16 inputs; fp32 accumulation): the kernels round P and dS to
+bf16 before the products that use them (relative error up to 2^-9 each),
+take D = <dO, O> from the bf16 forward output (relative error up to 2^-9 of
+|dO| |O|), and round dq, dk, dv to bf16 at the end (2^-9). Summed over a
+row's or a key's terms these stay within a few parts per thousand of the
+sum of magnitudes, so the test asks for sum|err| / sum|ref| <= 1e-2 and
+max|err| <= 3e-2 max|ref| per tensor.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import check
+from block_sparse_long_moba_amd import moba, synth
+from block_sparse_long_moba_amd.tensors import to_device, to_host_f64, workspace_view
+
+pytestmark = pytest.mark.gpu
+
+REL_SUM, REL_MAX = 1e-2, 3e-2
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moba.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def make_gate(kind):
+    if kind == "mean":
+        return None
+    if kind.startswith("window"):
+        return moba.gate_window(int(kind[len("window"):]))
+    ex = kind[len("pooled"):]
+    return moba.gate_pooled(int(ex[0]), int(ex[1]))
+
+
+def checked_selection(inp, B, k, kind, gidx):
+    """The GPU's selection after checking it against the oracle's (it may
+    differ only inside a near tie, and must then be a valid choice)."""
+    T = inp.q.shape[0]
+    rows = np.arange(T)
+    if kind == "mean":
+        kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+        sel, tie, scores = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, want_scores=True)
+        differs, _ = check.check_selection(gidx, sel, tie, scores, k)
+        return gidx, int(differs.sum())
+    if kind.startswith("window"):
+        sel = oracle.select_window(inp.cu_seqlens, B, k, int(kind[len("window"):]),
+                                   inp.q.shape[1], total_tokens=T)
+        assert np.array_equal(gidx, sel)
+        return gidx, 0
+    from test_gpu_gates import pooled_reference
+    ex = kind[len("pooled"):]
+    use, _, n_diff = pooled_reference(inp, B, k, int(ex[0]), int(ex[1]), gidx, rows)
+    assert np.array_equal(use, gidx)
+    return gidx, n_diff
+
+
+def compare(name, got, ref):
+    err = np.abs(got - ref)
+    stats = dict(max_abs=float(err.max(initial=0.0)), ref_max=float(np.abs(ref).max(initial=0.0)),
+                 rel_sum=float(err.sum() / max(np.abs(ref).sum(), 1e-300)))
+    assert np.all(np.isfinite(got)), name + ": non-finite GPU gradient"
+    assert stats["rel_sum"] <= REL_SUM, (name, stats)
+    assert stats["max_abs"] <= REL_MAX * stats["ref_max"] + 1e-6, (name, stats)
+    return stats
+
+
+BWD = [
+    # lengths,              Hq, Hkv,  B,   k, gate,       seed
+    ([1000],                 4,  2, 128,  3, "mean",     61),  # ragged tail, several tiles
+    ([0, 300, 64, 1, 700],   8,  2,  64,  4, "mean",     62),  # empty, short, one-row sequences
+    ([2048],                 4,  4, 512,  3, "mean",     63),  # two 256-key chunks per block
+    ([1500],                 4,  2, 192,  1, "mean",     64),  # topk 1: own block only
+    ([1200, 500],           16,  2, 192,  5, "mean",     65),  # G = 8, block size 3 * 64
+    ([900],                  4,  4, 128, 16, "mean",     66),  # topk covers every block: dense
+    ([1000, 700],            4,  2, 128,  4, "window1",  67),  # window gate with a sink
+    ([1500],                 8,  2, 128,  5, "pooled11", 68),  # pooled gate
+]
+
+
+@pytest.mark.parametrize("case", BWD, ids=lambda c: "L%s_h%d_%d_B%d_k%d_%s" % (
+    "-".join(map(str, c[0])), c[1], c[2], c[3], c[4], c[5]))
+def test_bwd_matches_oracle_on_every_element(case):
+    import torch
+    lengths, hq, hkv, B, k, kind, seed = case
+    note("bwd case %s" % (case,))
+    inp = synth.custom(lengths, hq, hkv, 128, "bf16", B, k, seed)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    sh = moba.shape_of(q, kk, cu)
+    gate = make_gate(kind)
+    fwd_ws = torch.empty(moba.moba_fwd_workspace_size(sh, B, k, 0), dtype=torch.uint8,
+                         device="cuda")
+    out, lse = moba.moba_fwd_gated(q, kk, v, cu, B, k, gate or moba.gate_mean(), fwd_ws)
+    T = inp.q.shape[0]
+    rng = np.random.default_rng(seed + 1000)
+    dout = torch.from_numpy(rng.standard_normal((T, hq, 128), dtype=np.float32)).to(
+        torch.bfloat16).cuda()
+    lay = moba.moba_bwd_plan(sh, B, k, 0)
+    assert lay.kv_heads_per_pass == hkv  # one pass: the workspace keeps every head's selection
+    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = moba.moba_bwd(q, kk, v, out, lse, dout, cu, B, k, ws, gate=gate)
+    torch.cuda.synchronize()
+    gidx = workspace_view(ws, lay.idx_offset, T * hq * k, torch.int32).view(T, hq, k).cpu().numpy()
+    sel, n_diff = checked_selection(inp, B, k, kind, gidx)
+    ref = oracle.attend_bwd(inp.q, inp.k, inp.v, to_host_f64(dout), inp.cu_seqlens, B, k,
+                            np.ascontiguousarray(sel))
+    stats = {name: compare(name, to_host_f64(got), r)
+             for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)}
+    note("stats %s selection_differs_in_near_ties=%d" % (stats, n_diff))
+
+
+def test_bwd_pass_sizes_agree_and_repeat():
+    """One pass of all kv heads and passes of one kv head give the same
+    gradients; dq and dk/dv do not depend on the bin item order beyond
+    rounding, and two runs of the same call agree to that rounding."""
+    import torch
+    inp = synth.custom([1500, 600], 8, 4, 128, "bf16", 128, 4, 71)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    sh = moba.shape_of(q, kk, cu)
+    out, lse = moba.moba_fwd(q, kk, v, cu, 128, 4)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(5)).to(
+        torch.bfloat16).cuda()
+    big = torch.empty(moba.moba_bwd_workspace_size(sh, 128, 4, 0), dtype=torch.uint8,
+                      device="cuda")
+    small = torch.empty(moba.moba_bwd_workspace_size(sh, 128, 4, 1), dtype=torch.uint8,
+                        device="cuda")
+    a = moba.moba_bwd(q, kk, v, out, lse, dout, cu, 128, 4, big)
+    b = moba.moba_bwd(q, kk, v, out, lse, dout, cu, 128, 4, small)
+    c = moba.moba_bwd(q, kk, v, out, lse, dout, cu, 128, 4, big)
+    torch.cuda.synchronize()
+    # dq sums its slots in a fixed order: bit-identical
+    assert torch.equal(a[0], b[0]) and torch.equal(a[0], c[0])
+    # dk, dv sum a bin's items in the order the dispatch stage filled it
+    for x, y in ((a, b), (a, c)):
+        for i in (1, 2):
+            d = (x[i].float() - y[i].float()).abs().max().item()
+            assert d <= 2.0 ** -7 * x[i].float().abs().max().item(), d
+
+
+def test_bwd_rejects_fp32_and_bad_arguments():
+    import torch
+    inp = synth.custom([300], 4, 2, 128, "fp32", 64, 2, 72)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moba.MobaError) as e:
+        moba.moba_bwd(q, kk, v, q, torch.empty(4, 300, device="cuda"), q, cu, 64, 2, ws)
+    assert e.value.status == 2
