@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--decode", default=None, metavar="SxL",
                     help="time decode instead: S sequences with KV caches of L tokens each "
                     "(e.g. 1x1048576 or 32x32768), one new query per sequence")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (dq, dk, dv; mean gate) instead of the forward")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows the CPU oracle times (0 = sized for about 15 s)")
     args = ap.parse_args()
@@ -130,6 +132,9 @@ def main():
 
     if args.decode:
         decode_bench(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
         return
 
     import torch
@@ -308,6 +313,138 @@ def main():
         "dense_causal": dense,
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bwd_bench(args):
+    """Backward pass of the workload (mean gate): D = <dO, O>, then per pass
+    the gate and dispatch again, K^T per block, partial dq (own block, earlier
+    blocks), their sum, and dk/dv; each stage bracketed by HIP events. The
+    forward pass that produced out and lse runs once, untimed. Effective
+    FLOP = 10*d per attended (row, head, key): the five products of the
+    attention gradient (S recomputed, dP, dV, dK, dQ)."""
+    import torch
+    from block_sparse_long_moba_amd import moba, synth
+    from block_sparse_long_moba_amd.tensors import to_device, workspace_view
+
+    w = synth.WORKLOADS[args.workload]
+    assert w.dtype == "bf16", "the backward pass is bf16 only"
+    B, k, Hq, Hkv = w.block_size, w.topk, w.num_q_heads, w.num_kv_heads
+    T = w.total_tokens
+    log("bwd, workload %s: generating seeded inputs" % w.name)
+    inp = synth.generate(w)
+    torch.cuda.set_device(0)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    shape = moba.shape_of(q, kk, cu, max_seqlen=max(w.lengths))
+    P = Hkv
+    while P > 1 and moba.moba_fwd_workspace_size(shape, B, k, P) > (48 << 30):
+        P //= 2
+    fws = torch.empty(moba.moba_fwd_workspace_size(shape, B, k, P), dtype=torch.uint8,
+                      device="cuda")
+    out, lse = moba.moba_fwd_ex(q, kk, v, cu, B, k, fws, max_seqlen=max(w.lengths))
+    torch.cuda.synchronize()
+    del fws
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 5)
+    dout = torch.randn(q.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    P = Hkv
+    while P > 1 and moba.moba_bwd_workspace_size(shape, B, k, P) > (64 << 30):
+        P //= 2
+    lay = moba.moba_bwd_plan(shape, B, k, P)
+    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(kk), torch.empty_like(v)
+    passes = list(range(0, Hkv, lay.kv_heads_per_pass))
+    log("bwd workspace %.1f GiB, %d pass(es) of %d kv heads" % (
+        lay.total_bytes / 2**30, len(passes), lay.kv_heads_per_pass))
+
+    def step(tm):
+        tm.run("seqtable", lambda: moba.moba_seqtable(cu, shape, B, lay, ws))
+        tm.run("meanpool", lambda: moba.moba_meanpool(kk, shape, B, lay, ws))
+        tm.run("delta", lambda: moba.moba_bwd_delta(out, dout, shape, B, k, lay, ws))
+        for g0 in passes:
+            tm.run("gate", lambda: moba.moba_gate(q, shape, B, k, lay, ws, g0))
+            tm.run("dispatch", lambda: moba.moba_dispatch(shape, B, k, lay, ws, g0))
+            tm.run("ktrans", lambda: moba.moba_ktrans(kk, shape, B, k, lay, ws, g0))
+            tm.run("dq_diag", lambda: moba.moba_attn_bwd_dq(q, kk, v, dout, lse, shape, B, k,
+                                                             lay, ws, g0, which=1))
+            tm.run("dq_hist", lambda: moba.moba_attn_bwd_dq(q, kk, v, dout, lse, shape, B, k,
+                                                             lay, ws, g0, which=2))
+            tm.run("dq_sum", lambda: moba.moba_attn_bwd_dq_sum(shape, B, k, lay, ws, dq, g0))
+            tm.run("dkdv", lambda: moba.moba_attn_bwd_dkdv(q, kk, v, dout, lse, shape, B, k, lay,
+                                                            ws, dk, dv, g0))
+
+    nbins = lay.kv_heads_per_pass * lay.num_blocks_bound
+    hist_rows = []
+    moba.moba_seqtable(cu, shape, B, lay, ws)
+    moba.moba_meanpool(kk, shape, B, lay, ws)
+    for g0 in passes:
+        moba.moba_gate(q, shape, B, k, lay, ws, g0)
+        moba.moba_dispatch(shape, B, k, lay, ws, g0)
+        torch.cuda.synchronize()
+        off = workspace_view(ws, lay.bins_offset + 4 * nbins, nbins + 1, torch.int32)
+        hist_rows.append(int(off[-1].item()) & 0xFFFFFFFF)
+
+    log("warmup %d step(s)" % args.warmup)
+    for _ in range(args.warmup):
+        step(Timer())
+    torch.cuda.synchronize()
+    log("timing %d step(s)" % args.steps)
+    tm = Timer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step(tm)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    totals = tm.totals()
+    stages = {n: tot / args.steps for n, (tot, cnt) in totals.items()}
+    log("bwd step %.2f ms; stages %s" % (ms, {n: round(x, 3) for n, x in stages.items()}))
+
+    d = HEAD_DIM
+    own_pairs = Hq * sum(int(((np.arange(L) % B) + 1).sum()) for L in w.lengths)
+    hist_pairs = B * float(sum(hist_rows))
+    eff = 10.0 * d * (own_pairs + hist_pairs)
+    # per-kernel algorithmic FLOP: dq = S, dP, dQ (6 d per pair); dk/dv = S, dP,
+    # dV, dK (8 d per pair)
+    kflop = {"dq_diag": 6.0 * d * own_pairs, "dq_hist": 6.0 * d * hist_pairs,
+             "dkdv": 8.0 * d * (own_pairs + hist_pairs)}
+    kernels = {}
+    for name, fl in kflop.items():
+        tot, cnt = totals[name]
+        kernels[name] = {"ms_per_step": round(tot / args.steps, 3),
+                         "avg_launch_ms": round(tot / cnt, 4),
+                         "TFLOP/s": round(fl / (tot / args.steps * 1e-3) / 1e12, 2),
+                         "frac": round(fl / (tot / args.steps * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                       4)}
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["TFLOP/s"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+                "traffic": None, "avg_launch_ms": kernels[dom]["avg_launch_ms"],
+                "launches_per_step": len(passes),
+                "flop_per_launch": kflop[dom] / len(passes)}
+    es = 2
+    n_hist = float(sum(hist_rows))
+    hbm_bytes = {"delta": 2 * T * Hq * d * es + T * Hq * 4,
+                 "ktrans": 2 * T * Hkv * d * es,
+                 "dq_sum": (n_hist + T * Hq) * d * 4 + T * Hq * k * 4 + T * Hq * d * es}
+    hbm = {n: {"ms": round(stages[n], 4), "GB/s": round(b / (stages[n] * 1e-3) / 1e9, 1),
+               "frac": round(b / (stages[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+           for n, b in hbm_bytes.items()}
+    res = {
+        "metric": "MoBA bwd ms + effective TFLOP/s (10*d per attended row-head-key), % MFMA peak",
+        "value": round(eff / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s (effective)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v/dO, per-block key offsets)",
+        "config": {"workload": w.name, "pass": "backward", "seq_lens": list(w.lengths),
+                   "total_tokens": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "block_size": B, "topk": k, "kv_heads_per_pass": lay.kv_heads_per_pass,
+                   "gate": {"kind": "mean"}, "parallelism": "single GPU"},
+        "effective_flop": eff,
+        "stage_ms": {n: round(x, 4) for n, x in stages.items()},
+        "kernels": kernels, "hbm": hbm, "roofline": roofline, "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
 

@@ -220,14 +220,28 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
 }
 
 // Shared checks of the stage entry points: the layout must be the plan of
-// these arguments (same pass size) and the workspace non-NULL.
+// these arguments (same pass size) and the workspace non-NULL. PLAN_FWD /
+// PLAN_BWD: the forward / backward plan; PLAN_ANY: either (the stages before
+// the attention use the regions both plans share).
+enum { PLAN_FWD = 1, PLAN_BWD = 2, PLAN_ANY = 3 };
 moba_status_t check_stage(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L,
-                          void *ws, moba_layout_t *fresh) {
+                          void *ws, moba_layout_t *fresh, int which = PLAN_FWD) {
   if (!L) return fail(MOBA_ERROR_INVALID_VALUE, "layout is NULL");
   moba_status_t st = plan_impl(sh, B, k, L->kv_heads_per_pass, fresh);
   if (st != MOBA_SUCCESS) return st;
-  if (fresh->total_bytes != L->total_bytes || fresh->kv_heads_per_pass != L->kv_heads_per_pass)
-    return fail(MOBA_ERROR_INVALID_VALUE, "layout does not match shape/block_size/topk");
+  bool ok = false;
+  if ((which & PLAN_FWD) && fresh->total_bytes == L->total_bytes &&
+      fresh->kv_heads_per_pass == L->kv_heads_per_pass)
+    ok = true;
+  if (!ok && (which & PLAN_BWD)) {
+    moba_layout_t b;
+    if ((st = bwd_plan_impl(sh, B, k, L->kv_heads_per_pass, &b)) != MOBA_SUCCESS) return st;
+    if (b.total_bytes == L->total_bytes && b.kv_heads_per_pass == L->kv_heads_per_pass) {
+      ok = true;
+      *fresh = b;
+    }
+  }
+  if (!ok) return fail(MOBA_ERROR_INVALID_VALUE, "layout does not match shape/block_size/topk");
   if (!ws && sh->total_tokens > 0) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
   return MOBA_SUCCESS;
 }
@@ -236,6 +250,44 @@ moba_status_t check_pass(const moba_shape_t *sh, const moba_layout_t *L, int32_t
   if (g0 < 0 || g0 >= sh->num_kv_heads || g0 % L->kv_heads_per_pass != 0)
     return fail(MOBA_ERROR_INVALID_VALUE, "kv_head_begin %d must be a multiple of %d below %d", g0,
                 L->kv_heads_per_pass, sh->num_kv_heads);
+  return MOBA_SUCCESS;
+}
+
+// Backward plan: its partial-dq and D regions, and the pooled gate's scratch
+// (lists at the start of the partial-dq region, at most (topk + 2) ints per
+// (row, head); the per-slot lse in its last T*Hp*topk floats) kept away from D.
+BwdWork carve_bwd(const Problem &pb, const moba_layout_t *L, void *ws, Work *w) {
+  BwdWork bw{(float *)((char *)ws + L->part_o_offset), (float *)((char *)ws + L->part_lse_offset)};
+  const int64_t slots = pb.T * pb.Hp * pb.k;
+  w->part_o = bw.dq_part;
+  w->part_lse = bw.dq_part + slots * (kHeadDim - 1);
+  return bw;
+}
+
+bool is_bwd_plan(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L) {
+  moba_layout_t f;
+  return plan_impl(sh, B, k, L->kv_heads_per_pass, &f) == MOBA_SUCCESS &&
+         f.total_bytes != L->total_bytes;
+}
+
+// Shared checks and set-up of the attention-gradient stages.
+moba_status_t bwd_stage(const void *q, const void *k, const void *v, const void *dout,
+                        const float *lse, const moba_shape_t *sh, int32_t B, int32_t topk,
+                        float scale, const moba_layout_t *L, void *ws, int32_t g0, Problem *pb,
+                        Work *w, BwdWork *bw, bool *nothing) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f, PLAN_BWD);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->dtype != MOBA_DTYPE_BF16) return fail(MOBA_ERROR_UNSUPPORTED, "backward pass: bf16 only");
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  *nothing = sh->total_tokens == 0;
+  if (*nothing) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q || !k || !v || !dout || !lse)
+    return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v, dout and lse must be non-NULL");
+  *pb = make_problem(sh, B, topk, scale, L);
+  *w = carve(*pb, L, ws);
+  *bw = carve_bwd(*pb, L, ws, w);
   return MOBA_SUCCESS;
 }
 
@@ -450,7 +502,7 @@ moba_status_t moba_meanpool(const void *k, const moba_shape_t *sh, int32_t B,
 moba_status_t moba_gate(const void *q, const moba_shape_t *sh, int32_t B, int32_t k,
                         const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
   moba_layout_t f;
-  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f, PLAN_ANY);
   if (st != MOBA_SUCCESS) return st;
   if (sh->total_tokens == 0) return MOBA_SUCCESS;
   if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
@@ -476,7 +528,7 @@ moba_status_t moba_minmaxpool(const void *k, const moba_shape_t *sh, int32_t B,
 moba_status_t moba_gate_window(const moba_shape_t *sh, int32_t B, int32_t k, int32_t n_sink,
                                const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
   moba_layout_t f;
-  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f, PLAN_ANY);
   if (st != MOBA_SUCCESS) return st;
   const moba_gate_t gate{MOBA_GATE_WINDOW, n_sink, 0, 0};
   if ((st = check_gate(&gate, k)) != MOBA_SUCCESS) return st;
@@ -492,7 +544,7 @@ moba_status_t moba_gate_pooled(const void *q, const moba_shape_t *sh, int32_t B,
                                int32_t extra_max, int32_t extra_min, const moba_layout_t *L,
                                void *ws, int32_t g0, hipStream_t s) {
   moba_layout_t f;
-  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f, PLAN_ANY);
   if (st != MOBA_SUCCESS) return st;
   const moba_gate_t gate{MOBA_GATE_POOLED, 0, extra_max, extra_min};
   if ((st = check_gate(&gate, k)) != MOBA_SUCCESS) return st;
@@ -501,6 +553,7 @@ moba_status_t moba_gate_pooled(const void *q, const moba_shape_t *sh, int32_t B,
   if (!q) return fail(MOBA_ERROR_INVALID_VALUE, "q is NULL");
   Problem pb = make_problem(sh, B, k, 0.f, L);
   Work w = carve(pb, L, ws);
+  if (is_bwd_plan(sh, B, k, L)) carve_bwd(pb, L, ws, &w);
   MOBA_HIP(launch_gate_pooled(pb, w, q, g0, extra_max, extra_min, s), "gate_pooled");
   return MOBA_SUCCESS;
 }
@@ -508,7 +561,7 @@ moba_status_t moba_gate_pooled(const void *q, const moba_shape_t *sh, int32_t B,
 moba_status_t moba_dispatch(const moba_shape_t *sh, int32_t B, int32_t k, const moba_layout_t *L,
                             void *ws, int32_t g0, hipStream_t s) {
   moba_layout_t f;
-  moba_status_t st = check_stage(sh, B, k, L, ws, &f);
+  moba_status_t st = check_stage(sh, B, k, L, ws, &f, PLAN_ANY);
   if (st != MOBA_SUCCESS) return st;
   if (sh->total_tokens == 0) return MOBA_SUCCESS;
   if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
@@ -663,15 +716,8 @@ moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *
   if (!ws) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
   Problem pb = make_problem(sh, B, topk, scale, &L);
   Work w = carve(pb, &L, ws);
-  BwdWork bw{(float *)((char *)ws + L.part_o_offset), (float *)((char *)ws + L.part_lse_offset)};
+  const BwdWork bw = carve_bwd(pb, &L, ws, &w);
   const BwdIo io{q, k, v, dout, lse, dq, dk, dv};
-  // the pooled gate keeps scratch lists in part_o and writes a per-slot lse
-  // in part_lse: both go to the partial-dq region (lists at its start, at
-  // most (topk + 2) ints per (row, head); the lse in its last slots floats),
-  // so D stays intact
-  const int64_t slots = pb.T * pb.Hp * topk;
-  w.part_o = bw.dq_part;
-  w.part_lse = bw.dq_part + slots * (kHeadDim - 1);
   MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
   if (gate->kind != MOBA_GATE_WINDOW) MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
   if (gate->kind == MOBA_GATE_POOLED) MOBA_HIP(launch_minmaxpool(pb, w, k, s), "minmaxpool");
@@ -687,10 +733,94 @@ moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *
     MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
     MOBA_HIP(launch_vtrans(k, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
              "ktrans");
-    MOBA_HIP(launch_bwd_dq(pb, w, bw, io, g0, s), "bwd_dq");
+    MOBA_HIP(launch_bwd_dq(pb, w, bw, io, g0, 3, s), "bwd_dq");
     MOBA_HIP(launch_bwd_dq_sum(pb, w, bw, io, g0, s), "bwd_dq_sum");
     MOBA_HIP(launch_bwd_dkdv(pb, w, bw, io, g0, s), "bwd_dkdv");
   }
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_bwd_delta(const void *out, const void *dout, const moba_shape_t *sh,
+                             int32_t B, int32_t topk, const moba_layout_t *L, void *ws,
+                             hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f, PLAN_BWD);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->dtype != MOBA_DTYPE_BF16) return fail(MOBA_ERROR_UNSUPPORTED, "backward pass: bf16 only");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if (!out || !dout) return fail(MOBA_ERROR_INVALID_VALUE, "out and dout must be non-NULL");
+  Problem pb = make_problem(sh, B, topk, 0.f, L);
+  Work w = carve(pb, L, ws);
+  const BwdWork bw = carve_bwd(pb, L, ws, &w);
+  MOBA_HIP(launch_bwd_delta(pb, out, dout, bw.delta, s), "bwd_delta");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_ktrans(const void *k, const moba_shape_t *sh, int32_t B, int32_t topk,
+                          const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f, PLAN_BWD);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!k) return fail(MOBA_ERROR_INVALID_VALUE, "k is NULL");
+  Problem pb = make_problem(sh, B, topk, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_vtrans(k, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+           "ktrans");
+  return MOBA_SUCCESS;
+}
+
+
+moba_status_t moba_attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
+                               const float *lse, const moba_shape_t *sh, int32_t B, int32_t topk,
+                               float scale, const moba_layout_t *L, void *ws, int32_t g0,
+                               int32_t which, hipStream_t s) {
+  Problem pb;
+  Work w;
+  BwdWork bw;
+  bool nothing = false;
+  moba_status_t st = bwd_stage(q, k, v, dout, lse, sh, B, topk, scale, L, ws, g0, &pb, &w, &bw,
+                               &nothing);
+  if (st != MOBA_SUCCESS || nothing) return st;
+  if (which < 1 || which > 3) return fail(MOBA_ERROR_INVALID_VALUE, "which must be 1, 2 or 3");
+  const BwdIo io{q, k, v, dout, lse, nullptr, nullptr, nullptr};
+  MOBA_HIP(launch_bwd_dq(pb, w, bw, io, g0, which, s), "bwd_dq");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_bwd_dq_sum(const moba_shape_t *sh, int32_t B, int32_t topk,
+                                   const moba_layout_t *L, void *ws, int32_t g0, void *dq,
+                                   hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f, PLAN_BWD);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->dtype != MOBA_DTYPE_BF16) return fail(MOBA_ERROR_UNSUPPORTED, "backward pass: bf16 only");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!dq) return fail(MOBA_ERROR_INVALID_VALUE, "dq is NULL");
+  Problem pb = make_problem(sh, B, topk, 0.f, L);
+  Work w = carve(pb, L, ws);
+  const BwdWork bw = carve_bwd(pb, L, ws, &w);
+  const BwdIo io{nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr, nullptr};
+  MOBA_HIP(launch_bwd_dq_sum(pb, w, bw, io, g0, s), "bwd_dq_sum");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
+                                 const float *lse, const moba_shape_t *sh, int32_t B,
+                                 int32_t topk, float scale, const moba_layout_t *L, void *ws,
+                                 int32_t g0, void *dk, void *dv, hipStream_t s) {
+  Problem pb;
+  Work w;
+  BwdWork bw;
+  bool nothing = false;
+  moba_status_t st = bwd_stage(q, k, v, dout, lse, sh, B, topk, scale, L, ws, g0, &pb, &w, &bw,
+                               &nothing);
+  if (st != MOBA_SUCCESS || nothing) return st;
+  if (!dk || !dv) return fail(MOBA_ERROR_INVALID_VALUE, "dk and dv must be non-NULL");
+  const BwdIo io{q, k, v, dout, lse, nullptr, dk, dv};
+  MOBA_HIP(launch_bwd_dkdv(pb, w, bw, io, g0, s), "bwd_dkdv");
   return MOBA_SUCCESS;
 }
 

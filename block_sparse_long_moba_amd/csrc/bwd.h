@@ -20,8 +20,9 @@ struct BwdIo {
 
 hipError_t launch_bwd_delta(const Problem &pb, const void *out, const void *dout, float *delta,
                             hipStream_t s);
+// which: 1 = own-block rows, 2 = earlier-block rows, 3 = both
 hipError_t launch_bwd_dq(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io,
-                         int g0, hipStream_t s);
+                         int g0, int which, hipStream_t s);
 hipError_t launch_bwd_dq_sum(const Problem &pb, const Work &w, const BwdWork &bw,
                              const BwdIo &io, int g0, hipStream_t s);
 hipError_t launch_bwd_dkdv(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io,

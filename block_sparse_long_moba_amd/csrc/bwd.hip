@@ -18,8 +18,8 @@
 //   comes pre-transposed per block, like V^T in the forward pass). Each
 //   (row, head, slot) gets an fp32 partial dQ; a sum over the slots follows.
 // - keys resident (bwd_dkdv_kernel): one workgroup per (kv head, block, chunk
-//   of 256 keys), 8 waves of 32 keys with K and V in registers as MFMA B
-//   operands. The block's own rows (for each query head of the kv head,
+//   of 256 keys), 8 waves of 32 keys with V in registers and K in LDS as
+//   MFMA B operands. The block's own rows (for each query head of the kv head,
 //   causally) and then the rows of its bin stream through LDS in tiles of 32
 //   rows, stored both row-major and transposed. Per tile S = Q K^T,
 //   dP = dO V^T, dS, dV^T += dO^T P and dK^T += Q^T dS; dK and dV are written
@@ -345,17 +345,21 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
 //
 // LDS per stage: Q and dO tiles row-major (32 rows of 256 B at a pitch of
 // 272 B), then Q^T and dO^T (128 rows (d) of 32 elements at a pitch of 80 B);
-// after both stages, per stage the 32 rows' lse (log2 units) and D. The
+// after both stages, per stage the 32 rows' lse (log2 units) and D; then the
+// waves' K rows. The
 // padding makes the 16 rows (or d rows) that 16 lanes read at one chunk
 // column fall in 16 different 16-byte bank groups, and every lane's operand
 // addresses a base plus compile-time offsets. Rows past the end of a tile
 // have q = dO = 0, lse = +inf and D = 0, so their probabilities and dS are
-// exactly 0.
+// exactly 0. Per tile: S, then P in place of S, then dP interleaved with the
+// dV products, then dS and the dK products; nothing the tile computes waits
+// for the next tile's rows, which are fetched into registers before it and
+// stored to LDS after it.
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int NP = 272, TP = 80;  // pitches of the row-major and transposed tiles
   constexpr int QN = 0, DN = 32 * NP, QT = 64 * NP, DTT = 64 * NP + 128 * TP;
-  constexpr int STAGE = 64 * NP + 256 * TP, LD = 2 * STAGE;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE + 2 * 256];
+  constexpr int STAGE = 64 * NP + 256 * TP, LD = 2 * STAGE, KW = LD + 2 * 256;
+  __shared__ __attribute__((aligned(1024))) char lds[KW + 8 * 32 * NP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
@@ -378,15 +382,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 
   // K and V rows of this lane's key as MFMA B operands (k = d); a lane past
   // the block's end takes the block's first row (its results are dropped)
-  bf16x8 kB[8], vB[8];
+  // K rows of this wave's keys in LDS (32 rows at pitch NP; each lane reads
+  // back what it wrote), V rows in registers, both as MFMA B operands (k = d)
+  char *const kw_lds = lds + KW + wave * 32 * NP;
+  bf16x8 vB[8];
   {
     const int64_t off = ((int64_t)(bi.y + (kvalid ? key : 0)) * a.Hkv + g) * kHeadDim + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      kB[kk] = *(const bf16x8 *)(a.k + off + 16 * kk);
+      *(bf16x8 *)(kw_lds + n * NP + (2 * kk + hh) * 16) = *(const bf16x8 *)(a.k + off + 16 * kk);
       vB[kk] = *(const bf16x8 *)(a.v + off + 16 * kk);
     }
   }
+  const int krd = n * NP + hh * 16;  // + 32 kk
   floatx16 dk[4], dv[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -402,35 +410,36 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 
   // loader: thread (row lr, chunk lc of 8 elements)
   const int lr = threadIdx.x & 31, lc = threadIdx.x >> 5;
+  // the item of this thread's row in tile `it`, clamped to an existing entry
+  // (own tiles and rows past the bin read one whose value goes unused): always
+  // a load, so its register is never written conditionally while a load may
+  // still be filling it
+  const uint32_t ilast = iend > 0 ? iend - 1 : 0u;
   auto item_of = [&](int it) -> uint32_t {
-    if (it < n_own || it >= ntiles) return 0u;
-    const uint32_t j = ibeg + (uint32_t)(it - n_own) * kKvRows + lr;
-    return a.items[j < iend ? j : iend - 1];
+    const uint32_t j = ibeg + (uint32_t)max(it - n_own, 0) * kKvRows + lr;
+    return a.items[j < ilast ? j : ilast];
   };
   bf16x8 sq, sdo;
   float sl = 0.f, sd = 0.f;
   bool sok = false;
   auto fetch = [&](int it, uint32_t item) {
-    int64_t t;
-    int h;
-    if (it < n_own) {
-      const int gi = it / own_per_head;
-      const int rl = k0 + (it - gi * own_per_head) * kKvRows + lr;
-      sok = rl < bi.z;
-      t = bi.y + (sok ? rl : k0);
-      h = a.h0 + p * a.G + gi;
-    } else {
-      const uint32_t j = ibeg + (uint32_t)(it - n_own) * kKvRows + lr;
-      sok = j < iend;
-      const int64_t row = (int64_t)item / a.topk;
-      t = row / a.Hp;
-      h = a.h0 + (int)(row % a.Hp);
-    }
+    // the item is decoded on every path (slots are below 2^32), so its load
+    // has completed before this tile's loads are issued
+    const uint32_t row_b = item / (uint32_t)a.topk;
+    const uint32_t t_b = row_b / (uint32_t)a.Hp;
+    const int h_b = a.h0 + (int)(row_b - t_b * (uint32_t)a.Hp);
+    const bool own = it < n_own;
+    const int gi = own ? it / own_per_head : 0;
+    const int rl = k0 + (it - gi * own_per_head) * kKvRows + lr;
+    const uint32_t j = ibeg + (uint32_t)max(it - n_own, 0) * kKvRows + lr;
+    sok = own ? rl < bi.z : j < iend;
+    const int64_t t = own ? (int64_t)bi.y + (rl < bi.z ? rl : k0) : (int64_t)t_b;
+    const int h = own ? a.h0 + p * a.G + gi : h_b;
     const int64_t off = (t * a.Hq + h) * kHeadDim + 8 * lc;
     sq = *(const bf16x8 *)(a.q + off);
     sdo = *(const bf16x8 *)(a.dout + off);
     if (lc == 0) {
-      sl = a.lse[(int64_t)h * a.T + t] * kLog2e;
+      sl = a.lse[(int64_t)h * a.T + t];
       sd = a.delta[(int64_t)h * a.T + t];
     }
   };
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
     if (lc == 0) {
       float *L = (float *)(lds + LD + stage * 256);
-      L[lr] = sok ? sl : INFINITY;
+      L[lr] = sok ? sl * kLog2e : INFINITY;
       L[32 + lr] = sok ? sd : 0.f;
     }
   };
@@ -476,33 +485,47 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = mfma(*(const bf16x8 *)(S_ + QN + qrd + 32 * kk), kB[kk], s);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) dp = mfma(*(const bf16x8 *)(S_ + DN + qrd + 32 * kk), vB[kk], dp);
-    bf16x8 pb[2], db[2];
+    for (int kk = 0; kk < 8; ++kk)
+      s = mfma(*(const bf16x8 *)(S_ + QN + qrd + 32 * kk), *(const bf16x8 *)(kw_lds + krd + 32 * kk),
+               s);
+    // probabilities in place of the scores
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      // accumulators 8c .. 8c+7 hold rows 16c + 8hh .. +7 of the tile
       const float4 l0 = *(const float4 *)(L + 16 * c + 8 * hh);
       const float4 l1 = *(const float4 *)(L + 16 * c + 8 * hh + 4);
-      const float4 d0 = *(const float4 *)(L + 32 + 16 * c + 8 * hh);
-      const float4 d1 = *(const float4 *)(L + 32 + 16 * c + 8 * hh + 4);
       const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-      const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * c + j;
         float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[j]));
         if (own && key > rt + 16 * c + 8 * hh + j) pv = 0.f;
-        pb[c][j] = (__bf16)pv;
-        db[c][j] = (__bf16)(pv * (dp[i] - dd[j]));
+        s[i] = pv;
       }
+    }
+    bf16x8 pb[2], db[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)s[8 * c + j];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) dp = mfma(*(const bf16x8 *)(S_ + DN + qrd + 32 * kk), vB[kk], dp);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        dv[dt] = mfma(*(const bf16x8 *)(S_ + DTT + trd + dt * 32 * TP + 32 * c), pb[c], dv[dt]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float4 d0 = *(const float4 *)(L + 32 + 16 * c + 8 * hh);
+      const float4 d1 = *(const float4 *)(L + 32 + 16 * c + 8 * hh + 4);
+      const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) db[c][j] = (__bf16)(s[8 * c + j] * (dp[8 * c + j] - dd[j]));
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dv[dt] = mfma(*(const bf16x8 *)(S_ + DTT + trd + dt * 32 * TP + 32 * c), pb[c], dv[dt]);
         dk[dt] = mfma(*(const bf16x8 *)(S_ + QT + trd + dt * 32 * TP + 32 * c), db[c], dk[dt]);
       }
   };
@@ -514,11 +537,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     uint32_t nxt = item_of(1);
     for (int it = 0; it < ntiles; ++it) {
       const int stage = it & 1;
-      const bool more = it + 1 < ntiles;
-      if (more) fetch(it + 1, nxt);
+      // every path issues the same loads (the last tile fetches itself again
+      // and drops it), so no wait inside the tile covers this tile's fetch
+      fetch(min(it + 1, ntiles - 1), nxt);
       nxt = item_of(it + 2);
       compute(it, stage);
-      if (more) stash(stage ^ 1);
+      if (it + 1 < ntiles) stash(stage ^ 1);
       __syncthreads();
     }
   }
@@ -573,16 +597,21 @@ hipError_t launch_bwd_delta(const Problem &pb, const void *out, const void *dout
 }
 
 hipError_t launch_bwd_dq(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io,
-                         int g0, hipStream_t s) {
+                         int g0, int which, hipStream_t s) {
   const BwdArgs a = make_args(pb, w, bw, io, g0);
-  const int64_t nq = (pb.B + kDqRows - 1) / kDqRows;
-  const int64_t gdiag = (pb.Hp * pb.NBb * nq + 7) / 8 * 8;
-  bwd_dq_kernel<BWD_DIAG><<<dim3((unsigned)gdiag), 512, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pb.k <= 1) return e;
-  const int64_t ghist = (w.max_tiles + 7) / 8 * 8;
-  bwd_dq_kernel<BWD_HIST><<<dim3((unsigned)ghist), 512, 0, s>>>(a);
-  return hipGetLastError();
+  if (which & 1) {
+    const int64_t nq = (pb.B + kDqRows - 1) / kDqRows;
+    const int64_t gdiag = (pb.Hp * pb.NBb * nq + 7) / 8 * 8;
+    bwd_dq_kernel<BWD_DIAG><<<dim3((unsigned)gdiag), 512, 0, s>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((which & 2) && pb.k > 1) {
+    const int64_t ghist = (w.max_tiles + 7) / 8 * 8;
+    bwd_dq_kernel<BWD_HIST><<<dim3((unsigned)ghist), 512, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_dq_sum(const Problem &pb, const Work &w, const BwdWork &bw,

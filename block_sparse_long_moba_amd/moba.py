@@ -23,7 +23,8 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_works
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
            "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
            "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
-           "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd",
+           "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd", "moba_bwd_delta",
+           "moba_ktrans", "moba_attn_bwd_dq", "moba_attn_bwd_dq_sum", "moba_attn_bwd_dkdv",
            "moba_dense_causal_workspace_size", "moba_dense_causal_fwd"]
 
 GATE_MEAN, GATE_WINDOW, GATE_POOLED = 0, 1, 2
@@ -111,6 +112,11 @@ def lib():
             "moba_bwd_workspace_size": ([S, I32, I32, I32], Z),
             "moba_bwd": ([P, P, P, P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, P,
                           Z, P], I32),
+            "moba_bwd_delta": ([P, P, S, I32, I32, LP, P, P], I32),
+            "moba_ktrans": ([P, S, I32, I32, LP, P, I32, P], I32),
+            "moba_attn_bwd_dq": ([P, P, P, P, P, S, I32, I32, F, LP, P, I32, I32, P], I32),
+            "moba_attn_bwd_dq_sum": ([S, I32, I32, LP, P, I32, P, P], I32),
+            "moba_attn_bwd_dkdv": ([P, P, P, P, P, S, I32, I32, F, LP, P, I32, P, P, P], I32),
             "moba_dense_causal_workspace_size": ([S], Z),
             "moba_dense_causal_fwd": ([P, P, P, P, S, F, P, P, P, Z, P], I32),
         }
@@ -325,6 +331,39 @@ def moba_bwd(q, k, v, out, lse, dout, cu_seqlens, block_size, topk, workspace, g
                           _ptr(dk), _ptr(dv), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(stream)))
     return dq, dk, dv
+
+
+def moba_bwd_delta(out, dout, shape, block_size, topk, layout, workspace, stream=None):
+    _check(lib().moba_bwd_delta(_ptr(out), _ptr(dout), ctypes.byref(shape), block_size, topk,
+                                ctypes.byref(layout), _ptr(workspace), _stream(stream)))
+
+
+def moba_ktrans(k, shape, block_size, topk, layout, workspace, kv_head_begin=0, stream=None):
+    _check(lib().moba_ktrans(_ptr(k), ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
+                             _ptr(workspace), kv_head_begin, _stream(stream)))
+
+
+def moba_attn_bwd_dq(q, k, v, dout, lse, shape, block_size, topk, layout, workspace,
+                     kv_head_begin=0, which=3, softmax_scale=0.0, stream=None):
+    _check(lib().moba_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                  ctypes.byref(shape), block_size, topk, softmax_scale,
+                                  ctypes.byref(layout), _ptr(workspace), kv_head_begin, which,
+                                  _stream(stream)))
+
+
+def moba_attn_bwd_dq_sum(shape, block_size, topk, layout, workspace, dq, kv_head_begin=0,
+                         stream=None):
+    _check(lib().moba_attn_bwd_dq_sum(ctypes.byref(shape), block_size, topk,
+                                      ctypes.byref(layout), _ptr(workspace), kv_head_begin,
+                                      _ptr(dq), _stream(stream)))
+
+
+def moba_attn_bwd_dkdv(q, k, v, dout, lse, shape, block_size, topk, layout, workspace, dk, dv,
+                       kv_head_begin=0, softmax_scale=0.0, stream=None):
+    _check(lib().moba_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                    ctypes.byref(shape), block_size, topk, softmax_scale,
+                                    ctypes.byref(layout), _ptr(workspace), kv_head_begin,
+                                    _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def moba_dense_causal_workspace_size(shape: Shape) -> int:

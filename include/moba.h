@@ -349,6 +349,41 @@ moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *
                        const moba_gate_t *gate, float softmax_scale, void *dq, void *dk,
                        void *dv, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Stages of moba_bwd, on a workspace laid out by moba_bwd_plan (moba_seqtable,
+ * moba_meanpool / moba_minmaxpool, the gate stages and moba_dispatch accept
+ * that plan too and run first, as in the forward pass). Per pass
+ * kv_head_begin: gate, dispatch, moba_ktrans, moba_attn_bwd_dq,
+ * moba_attn_bwd_dq_sum, moba_attn_bwd_dkdv; moba_bwd_delta once before. */
+
+/* D[h][t] = <dout[t][h], out[t][h]> (float32) into the part_lse region. */
+moba_status_t moba_bwd_delta(const void *out, const void *dout, const moba_shape_t *shape,
+                             int32_t block_size, int32_t topk, const moba_layout_t *layout,
+                             void *workspace, hipStream_t stream);
+/* K^T of every block of the pass's kv heads into the vt region. */
+moba_status_t moba_ktrans(const void *k, const moba_shape_t *shape, int32_t block_size,
+                          int32_t topk, const moba_layout_t *layout, void *workspace,
+                          int32_t kv_head_begin, hipStream_t stream);
+/* Partial dq of every (row, head, slot) of the pass: which = 1 the own block
+ * (causal), 2 the earlier blocks of the bins, 3 both. Needs the gate,
+ * dispatch, moba_ktrans and moba_bwd_delta. */
+moba_status_t moba_attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
+                               const float *lse, const moba_shape_t *shape, int32_t block_size,
+                               int32_t topk, float softmax_scale, const moba_layout_t *layout,
+                               void *workspace, int32_t kv_head_begin, int32_t which,
+                               hipStream_t stream);
+/* dq of the pass's query heads = sum of their slots' partials (own block
+ * first, then the earlier blocks in slot order). */
+moba_status_t moba_attn_bwd_dq_sum(const moba_shape_t *shape, int32_t block_size, int32_t topk,
+                                   const moba_layout_t *layout, void *workspace,
+                                   int32_t kv_head_begin, void *dq, hipStream_t stream);
+/* dk, dv of the pass's kv heads (own-block rows of their query heads, then
+ * the rows of the bins). Needs the gate, dispatch and moba_bwd_delta. */
+moba_status_t moba_attn_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout,
+                                 const float *lse, const moba_shape_t *shape, int32_t block_size,
+                                 int32_t topk, float softmax_scale, const moba_layout_t *layout,
+                                 void *workspace, int32_t kv_head_begin, void *dk, void *dv,
+                                 hipStream_t stream);
+
 /* ---- Dense causal attention on the same layout ("Standard Attention
  * Baseline" with a causal mask, per sequence): the full-attention reference
  * the pages compare MoBA against. workspace may be NULL (then scratch is

@@ -170,3 +170,47 @@ def test_decode_validation_and_sizes():
     empty = shape(T=0, S=0)
     assert L.moba_decode(None, None, None, ctypes.byref(empty), 4096, 12, 0.0, None, None, None,
                          moba.moba_decode_workspace_size(empty, 4096, 12), None) == 0
+
+
+def test_bwd_plan_and_validation():
+    L = moba.lib()
+    sh = shape(T=1 << 20)
+    f = moba.moba_plan(sh, 4096, 12, 1)
+    b = moba.moba_bwd_plan(sh, 4096, 12, 1)
+    # shared regions coincide; the partial-dq region holds fp32 rows
+    for name in ("table_offset", "kbar_offset", "vt_offset", "idx_offset", "bins_offset",
+                 "items_offset", "part_o_offset"):
+        assert getattr(f, name) == getattr(b, name), name
+    slots = (1 << 20) * 4 * 12
+    assert b.part_lse_offset - b.part_o_offset >= slots * 128 * 4
+    assert b.total_bytes - b.part_lse_offset >= (1 << 20) * 32 * 4
+    assert b.total_bytes == moba.moba_bwd_workspace_size(sh, 4096, 12, 1)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    null = None
+    n = b.total_bytes
+    # fp32 is unsupported
+    sh32 = shape(T=4096, dtype="fp32")
+    assert L.moba_bwd(fake, fake, fake, fake, fake, fake, fake, ctypes.byref(sh32), 4096, 12, null,
+                      0.0, fake, fake, fake, fake, 1 << 40, null) == 2
+    # missing gradients, too small a workspace
+    assert L.moba_bwd(fake, fake, fake, fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, null,
+                      0.0, null, fake, fake, fake, n, null) == 1
+    assert L.moba_bwd(fake, fake, fake, fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, null,
+                      0.0, fake, fake, fake, fake, 16, null) == 3
+    # stage entry points: a forward plan is not a backward plan, and vice versa
+    assert L.moba_attn_bwd_dkdv(fake, fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, 0.0,
+                                ctypes.byref(f), fake, 0, fake, fake, null) == 1
+    assert L.moba_attn_fwd_hist(fake, fake, ctypes.byref(sh), 4096, 12, 0.0, ctypes.byref(b),
+                                fake, 0, null) == 1
+    assert L.moba_attn_bwd_dq(fake, fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, 0.0,
+                              ctypes.byref(b), fake, 0, 4, null) == 1
+    # the gate and dispatch stages take either plan: the layout check passes and
+    # a kv_head_begin that is not a multiple of the pass size stops them before
+    # any launch
+    b2 = moba.moba_bwd_plan(sh, 4096, 12, 2)
+    assert L.moba_dispatch(ctypes.byref(sh), 4096, 12, ctypes.byref(b2), fake, 1, null) == 1
+    assert b"multiple" in L.moba_last_error()
+    empty = shape(T=0, S=0)
+    assert L.moba_bwd(null, null, null, null, null, null, null, ctypes.byref(empty), 4096, 12,
+                      null, 0.0, null, null, null, null,
+                      moba.moba_bwd_workspace_size(empty, 4096, 12, 0), null) == 0

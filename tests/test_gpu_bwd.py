@@ -162,3 +162,36 @@ def test_bwd_rejects_fp32_and_bad_arguments():
     with pytest.raises(moba.MobaError) as e:
         moba.moba_bwd(q, kk, v, q, torch.empty(4, 300, device="cuda"), q, cu, 64, 2, ws)
     assert e.value.status == 2
+
+
+def test_bwd_stages_match_one_call():
+    """The stage entry points, run in moba_bwd's order, give moba_bwd's
+    gradients (dq bit for bit; dk, dv up to the bin item order)."""
+    import torch
+    B, k = 128, 4
+    inp = synth.custom([1300, 700], 8, 2, 128, "bf16", B, k, 73)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    sh = moba.shape_of(q, kk, cu)
+    out, lse = moba.moba_fwd(q, kk, v, cu, B, k)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(9)).to(
+        torch.bfloat16).cuda()
+    lay = moba.moba_bwd_plan(sh, B, k, 1)
+    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    ref = moba.moba_bwd(q, kk, v, out, lse, dout, cu, B, k, ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(kk), torch.empty_like(v)
+    moba.moba_seqtable(cu, sh, B, lay, ws)
+    moba.moba_meanpool(kk, sh, B, lay, ws)
+    moba.moba_bwd_delta(out, dout, sh, B, k, lay, ws)
+    for g0 in range(0, 2, lay.kv_heads_per_pass):
+        moba.moba_gate(q, sh, B, k, lay, ws, g0)
+        moba.moba_dispatch(sh, B, k, lay, ws, g0)
+        moba.moba_ktrans(kk, sh, B, k, lay, ws, g0)
+        moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=1)
+        moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=2)
+        moba.moba_attn_bwd_dq_sum(sh, B, k, lay, ws, dq, g0)
+        moba.moba_attn_bwd_dkdv(q, kk, v, dout, lse, sh, B, k, lay, ws, dk, dv, g0)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, ref[0])
+    for x, y in ((dk, ref[1]), (dv, ref[2])):
+        diff = (x.float() - y.float()).abs().max().item()
+        assert diff <= 2.0 ** -7 * y.float().abs().max().item(), diff
