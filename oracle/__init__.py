@@ -55,6 +55,8 @@ def _load():
                                              i32, i32, i32, p, i64, p, p]
         lib.oracle_attend_bwd.argtypes = [p, p, p, p, i32, i64, i32, i32, i32, p, i32, i32, i32,
                                           p, dbl, p, p, p]
+        lib.oracle_attend_bwd_dq_rows.argtypes = [p, p, p, p, i32, i64, i32, i32, i32, p, i32,
+                                                  i32, i32, p, p, i64, dbl, p]
         lib.oracle_dense_causal.argtypes = [p, p, p, i32, i64, i32, i32, i32, p, i32, p, i64,
                                             dbl, p, p]
         for f in (lib.oracle_meanpool, lib.oracle_select, lib.oracle_attend, lib.oracle_moba,
@@ -214,6 +216,28 @@ def attend_bwd(q, k, v, dout, cu_seqlens, block_size, topk, sel, scale=None):
                               cu.size - 1, block_size, topk, _ptr(s), scale, _ptr(dq), _ptr(dk),
                               _ptr(dv))
     return dq, dk, dv
+
+
+def attend_bwd_dq_rows(q, k, v, dout_rows, cu_seqlens, block_size, topk, sel_rows, rows,
+                       scale=None):
+    """dq of the listed rows only (all heads), float64 [n][Hq][d]; dout_rows and
+    sel_rows hold those rows."""
+    bf = _check_inputs(q, k, v)
+    cu = _cu(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    n = r.size
+    s = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    assert s.shape == (n, Hq, topk)
+    go = np.ascontiguousarray(dout_rows, dtype=np.float64)
+    assert go.shape == (n, Hq, d)
+    dq = np.zeros((n, Hq, d))
+    _load().oracle_attend_bwd_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(go), bf, T, Hq, Hkv, d,
+                                      _ptr(cu), cu.size - 1, block_size, topk, _ptr(s), _ptr(r), n,
+                                      scale, _ptr(dq))
+    return dq
 
 
 def moba(q, k, v, cu_seqlens, block_size, topk, scale=None, rows=None):

@@ -480,6 +480,69 @@ void oracle_attend_bwd(const void *q, const void *k, const void *v, const double
   }
 }
 
+/* dq alone for a list of rows (all heads): the query-side half of
+ * oracle_attend_bwd, in the same order of operations, for sampled rows of
+ * inputs too large for the full gradient. sel and dout hold the listed rows:
+ * sel [n_rows][Hq][topk], dout [n_rows][Hq][d]; dq [n_rows][Hq][d]. */
+void oracle_attend_bwd_dq_rows(const void *q, const void *k, const void *v, const double *dout,
+                               int is_bf16, int64_t T, int Hq, int Hkv, int d, const int32_t *cu,
+                               int S, int B, int topk, const int32_t *sel, const int64_t *rows,
+                               int64_t n_rows, double scale, double *dq) {
+  const int G = Hq / Hkv;
+  const int64_t cap = (int64_t)topk * B + 1;
+  (void)T;
+#pragma omp parallel
+  {
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * cap);
+    double *z = (double *)malloc(sizeof(double) * cap);
+    double *dp = (double *)malloc(sizeof(double) * cap);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t w = 0; w < n_rows * Hq; ++w) {
+      const int64_t ri = w / Hq, t = rows[ri];
+      const int h = (int)(w % Hq), g = h / G;
+      int s = seq_of_row(cu, S, t);
+      int64_t a = cu[s], L = (int64_t)cu[s + 1] - cu[s], local = t - a, c = local / B;
+      const int32_t *my = sel + (ri * Hq + h) * (int64_t)topk;
+      int64_t nk = 0;
+      for (int i = 0; i < topk; ++i) {
+        int64_t j = my[i];
+        if (j < 0) continue;
+        int64_t r0 = j * B, r1 = (j == c) ? local + 1 : ((j + 1) * B < L ? (j + 1) * B : L);
+        for (int64_t r = r0; r < r1; ++r) keys[nk++] = a + r;
+      }
+      double m = -INFINITY;
+      for (int64_t i = 0; i < nk; ++i) {
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e)
+          acc += load_elem(q, (t * Hq + h) * (int64_t)d + e, is_bf16) *
+                 load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+        z[i] = scale * acc;
+        if (z[i] > m) m = z[i];
+      }
+      double l = 0.0;
+      for (int64_t i = 0; i < nk; ++i) { z[i] = exp(z[i] - m); l += z[i]; }
+      const double *go = dout + (ri * Hq + h) * (int64_t)d;
+      double D = 0.0;
+      for (int64_t i = 0; i < nk; ++i) {
+        z[i] /= l;
+        double acc = 0.0;
+        for (int e = 0; e < d; ++e)
+          acc += go[e] * load_elem(v, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+        dp[i] = acc;
+        D += z[i] * acc;
+      }
+      double *gq = dq + (ri * Hq + h) * (int64_t)d;
+      for (int e = 0; e < d; ++e) gq[e] = 0.0;
+      for (int64_t i = 0; i < nk; ++i) {
+        double ds = z[i] * (dp[i] - D);
+        for (int e = 0; e < d; ++e)
+          gq[e] += scale * ds * load_elem(k, (keys[i] * Hkv + g) * (int64_t)d + e, is_bf16);
+      }
+    }
+    free(keys); free(z); free(dp);
+  }
+}
+
 /* Full MoBA forward for a list of rows: meanpool, select, attend.
  * sel_out / near_tie_out may be NULL. */
 void oracle_moba(const void *q, const void *k, const void *v, int is_bf16,

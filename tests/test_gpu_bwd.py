@@ -195,3 +195,113 @@ def test_bwd_stages_match_one_call():
     for x, y in ((dk, ref[1]), (dv, ref[2])):
         diff = (x.float() - y.float()).abs().max().item()
         assert diff <= 2.0 ** -7 * y.float().abs().max().item(), diff
+
+
+FULL_BWD = ["gqa32x8_t32k_b512_k3_bf16", "gqa32x8_t128k_b4096_k12_bf16",
+            "gqa32x8_varlen4ragged_t256k_b4096_k12_bf16", "gqa32x8_t1m_b4096_k12_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL_BWD)
+def test_bwd_full_workload_sampled_rows_and_identities(name):
+    """Full-size backward pass in the benchmark's launch configuration (its
+    pass size and its seeded dO), staged as the benchmark runs it: dq of
+    sampled rows against the oracle, and for dk, dv (whose every key collects
+    from rows all over the sequence) the identities that hold at any size:
+      sum over keys of dk = 0 per kv head (sum_u dS_u = 0 per row and head),
+      sum over keys of dv = sum of dO over the kv head's query heads
+      (sum_u P_u = 1), sum <dq, q> = sum <dk, k> (both are sum dS_u z_u), and
+      sum <dv, v> = sum <dO, O>.
+    Each identity allows 8 times the spread that independent errors of
+    2^-8 relative per gradient element (rounding of P, dS and the outputs to
+    bf16) give to its sums."""
+    import torch
+    w = synth.WORKLOADS[name]
+    B, k, Hq, Hkv = w.block_size, w.topk, w.num_q_heads, w.num_kv_heads
+    T = w.total_tokens
+    note("bwd workload %s: generating inputs" % name)
+    inp = synth.generate(w)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    sh = moba.shape_of(q, kk, cu, max_seqlen=max(w.lengths))
+    P = Hkv
+    while P > 1 and moba.moba_fwd_workspace_size(sh, B, k, P) > (48 << 30):
+        P //= 2
+    fws = torch.empty(moba.moba_fwd_workspace_size(sh, B, k, P), dtype=torch.uint8, device="cuda")
+    out, lse = moba.moba_fwd_ex(q, kk, v, cu, B, k, fws, max_seqlen=max(w.lengths))
+    torch.cuda.synchronize()
+    del fws
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 5)
+    dout = torch.randn(q.shape, device="cuda", generator=gen).to(torch.bfloat16)
+    P = Hkv
+    while P > 1 and moba.moba_bwd_workspace_size(sh, B, k, P) > (64 << 30):
+        P //= 2
+    lay = moba.moba_bwd_plan(sh, B, k, P)
+    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    rows = check.sample_rows(w.cu_seqlens(), B, 2, w.seed)
+    rng = np.random.default_rng(w.seed + 3000)
+    rows = np.unique(np.concatenate([rng.choice(rows, min(len(rows), 48), replace=False),
+                                     w.cu_seqlens()[1:] - 1]))
+    note("bwd workload %s: pass of %d kv heads, %d sampled rows" % (name, P, len(rows)))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(kk), torch.empty_like(v)
+    Hp = lay.q_heads_per_pass
+    rows_t = torch.from_numpy(rows).cuda()
+    gsel = np.zeros((len(rows), Hq, k), np.int32)
+    moba.moba_seqtable(cu, sh, B, lay, ws)
+    moba.moba_meanpool(kk, sh, B, lay, ws)
+    moba.moba_bwd_delta(out, dout, sh, B, k, lay, ws)
+    for g0 in range(0, Hkv, P):
+        h0 = g0 * (Hq // Hkv)
+        moba.moba_gate(q, sh, B, k, lay, ws, g0)
+        idx = workspace_view(ws, lay.idx_offset, T * Hp * k, torch.int32).view(T, Hp, k)
+        gsel[:, h0:h0 + Hp] = idx[rows_t].cpu().numpy()
+        moba.moba_dispatch(sh, B, k, lay, ws, g0)
+        moba.moba_ktrans(kk, sh, B, k, lay, ws, g0)
+        moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=1)
+        moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=2)
+        moba.moba_attn_bwd_dq_sum(sh, B, k, lay, ws, dq, g0)
+        moba.moba_attn_bwd_dkdv(q, kk, v, dout, lse, sh, B, k, lay, ws, dk, dv, g0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+    # identities over every key, in float64, summed in chunks of rows
+    G = Hq // Hkv
+
+    def chunked(fn):
+        acc = None
+        for r0 in range(0, T, 1 << 16):
+            x = fn(slice(r0, min(T, r0 + (1 << 16))))
+            acc = x if acc is None else acc + x
+        return acc
+
+    f = lambda x: x.double()
+    stats = {}
+    sum_dk = chunked(lambda r: f(dk[r]).sum(dim=0))
+    spread = 2.0 ** -8 * chunked(lambda r: f(dk[r]).square().sum(dim=0)).sqrt()
+    stats["sum_dk/spread"] = (sum_dk.abs() / spread).max().item()
+    sum_do = chunked(lambda r: f(dout[r]).view(-1, Hkv, G, 128).sum(dim=(0, 2)))
+    err = (chunked(lambda r: f(dv[r]).sum(dim=0)) - sum_do).abs()
+    spread = 2.0 ** -8 * chunked(lambda r: f(dv[r]).square().sum(dim=0)).sqrt()
+    stats["sum_dv-sum_dO/spread"] = (err / spread).max().item()
+    for label, (x1, y1, x2, y2) in (("dq.q-dk.k/spread", (dq, q, dk, kk)),
+                                    ("dv.v-dO.O/spread", (dv, v, dout, out))):
+        s1 = chunked(lambda r: (f(x1[r]) * f(y1[r])).sum())
+        s2 = chunked(lambda r: (f(x2[r]) * f(y2[r])).sum())
+        q1 = chunked(lambda r: (f(x1[r]) * f(y1[r])).square().sum())
+        q2 = chunked(lambda r: (f(x2[r]) * f(y2[r])).square().sum())
+        stats[label] = ((s1 - s2).abs() / (2.0 ** -8 * (q1.sqrt() + q2.sqrt()))).item()
+    note("bwd workload %s: identities %s" % (name, stats))
+    for key_, val in stats.items():
+        assert val <= 8.0, (key_, stats)
+
+    # dq of the sampled rows against the oracle, over the GPU's selection once
+    # it is checked against the oracle's
+    kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+    sel, tie, scores = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows,
+                                     want_scores=True)
+    differs, _ = check.check_selection(gsel, sel, tie, scores, k)
+    dout_rows = to_host_f64(dout[rows_t])
+    note("bwd workload %s: oracle dq on %d rows" % (name, len(rows)))
+    ref = oracle.attend_bwd_dq_rows(inp.q, inp.k, inp.v, dout_rows, inp.cu_seqlens, B, k, gsel,
+                                    rows)
+    st = compare("dq", to_host_f64(dq[rows_t]), ref)
+    note("bwd workload %s: dq %s, selection differs in %d near ties" % (name, st,
+                                                                         int(differs.sum())))

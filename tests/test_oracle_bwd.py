@@ -94,3 +94,36 @@ def test_dense_gradients_match_torch_sdpa():
         np.testing.assert_allclose(dq[a:b], Q.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
         np.testing.assert_allclose(dk[a:b], K.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
         np.testing.assert_allclose(dv[a:b], V.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+
+
+def test_dq_rows_equals_full_gradient_rows():
+    """The row-subset dq follows the full gradient's arithmetic: equal on any
+    subset of rows."""
+    lengths, B, hq, hkv, d, topk = [70, 90], 16, 4, 2, 8, 3
+    q, k, v, cu = rand_inputs(lengths, hq, hkv, d, 11)
+    _, _, sel, _ = oracle.moba(q, k, v, cu, B, topk)
+    dout = np.random.default_rng(12).standard_normal(q.shape)
+    dq, _, _ = oracle.attend_bwd(q, k, v, dout, cu, B, topk, sel)
+    rows = np.array([0, 5, 69, 70, 71, 100, 159])
+    dq_r = oracle.attend_bwd_dq_rows(q, k, v, dout[rows], cu, B, topk, sel[rows], rows)
+    assert np.array_equal(dq_r, dq[rows])
+
+
+def test_gradient_identities():
+    """Identities of softmax attention that hold at any size (sum_u dS_u = 0
+    and sum_u P_u = 1 per row and head): sum over keys of dk is 0 per kv head;
+    sum over keys of dv is the sum of dO over the group's rows; sum <dq, q> =
+    sum <dk, k>; sum <dv, v> = sum over rows and heads of <dO, O>."""
+    lengths, B, hq, hkv, d, topk = [150, 77], 32, 4, 2, 8, 3
+    q, k, v, cu = rand_inputs(lengths, hq, hkv, d, 13)
+    out, _, sel, _ = oracle.moba(q, k, v, cu, B, topk)
+    dout = np.random.default_rng(14).standard_normal(q.shape)
+    dq, dk, dv = oracle.attend_bwd(q, k, v, dout, cu, B, topk, sel)
+    G = hq // hkv
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    scale_sum = np.abs(dk).sum()
+    assert np.abs(dk.sum(axis=0)).max() <= 1e-12 * scale_sum
+    dsum = dout.reshape(len(dout), hkv, G, d).sum(axis=(0, 2))
+    np.testing.assert_allclose(dv.sum(axis=0), dsum, rtol=0, atol=1e-10)
+    np.testing.assert_allclose((dq * q64).sum(), (dk * k64).sum(), rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose((dv * v64).sum(), (dout * out).sum(), rtol=1e-12, atol=1e-10)
