@@ -329,13 +329,23 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
   const int c = (int)((t - cu[s]) / B);
   const int nsel = min(k, c + 1);
   const float *base = dq_part + row * k * kHeadDim + lane * 4;
-  float4 acc = *(const float4 *)(base + (int64_t)(nsel - 1) * kHeadDim);
   const int32_t *sel = idx + row * k;
-  for (int i = 0; i < nsel - 1; ++i) {
-    const int j = sel[i];
-    if (j >= 0 && j < c) {
-      const float4 x = *(const float4 *)(base + (int64_t)i * kHeadDim);
-      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  float4 acc = *(const float4 *)(base + (int64_t)(nsel - 1) * kHeadDim);
+  // the earlier slots' rows are all loaded at once (16 per batch; a slot the
+  // dispatch did not route holds stale workspace bytes and is not added)
+  for (int i0 = 0; i0 < nsel - 1; i0 += 16) {
+    float4 x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      x[u] = i0 + u < nsel - 1 ? *(const float4 *)(base + (int64_t)(i0 + u) * kHeadDim)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (i0 + u >= nsel - 1) break;
+      const int j = sel[i0 + u];
+      if (j >= 0 && j < c) {
+        acc.x += x[u].x; acc.y += x[u].y; acc.z += x[u].z; acc.w += x[u].w;
+      }
     }
   }
   store_bf16x4(dq + (t * Hq + h0 + hl) * kHeadDim + lane * 4, acc.x, acc.y, acc.z, acc.w);

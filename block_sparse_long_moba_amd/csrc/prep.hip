@@ -305,14 +305,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
 #pragma unroll
   for (int j = 0; j < N; ++j) acc[j] = 0.f;
   const TO *po = part_o + row * k * kHeadDim + lane * N;
-  for (int i0 = 0; i0 < nsel; i0 += 4) {
-    uint4 raw[4];
+  // all slots of the row in flight at once (16 per batch)
+  for (int i0 = 0; i0 < nsel; i0 += 16) {
+    uint4 raw[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 16; ++u)
       raw[u] = i0 + u < nsel ? *(const uint4 *)(po + (int64_t)(i0 + u) * kHeadDim)
-                             : make_uint4(0, 0, 0, 0);  // in bounds; an empty slot's bytes are ignored
+                             : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 16; ++u) {
       if (i0 + u >= nsel) break;
       if (!(pl[i0 + u] > -INFINITY)) continue;
       const float wgt = __builtin_amdgcn_exp2f((pl[i0 + u] - L) * kLog2eF);
