@@ -146,16 +146,25 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const int L = cu[s + 1] - cu[s];
   if (L == 0 || j > (L - 1) / B) return;
   const int G = Hq / Hkv;
+  // query heads of the group that chose block j, in head order, with the
+  // slot of j in their selection (a head lists a block at most once): the
+  // first wave tests the G*k entries 64 at a time and compacts the matches
   __shared__ int heads[64], slots[64], nheads;
-  if (tid == 0) {
+  if (tid < 64) {
+    const int32_t *rows = idx + ((int64_t)s * Hq + g * G) * k;  // G rows of k, contiguous
     int n = 0;
-    for (int hl = 0; hl < G && n < 64; ++hl) {
-      const int h = g * G + hl;
-      const int32_t *row = idx + ((int64_t)s * Hq + h) * k;
-      for (int i = 0; i < k; ++i)
-        if (row[i] == j) { heads[n] = h; slots[n] = i; ++n; break; }
+    for (int base = 0; base < G * k && n < 64; base += 64) {
+      const int e = base + tid;
+      const bool hit = e < G * k && rows[e] == j;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(hit);
+      const int pos = n + __builtin_popcountll(mask & ((1ull << tid) - 1ull));
+      if (hit && pos < 64) {
+        heads[pos] = g * G + e / k;
+        slots[pos] = e % k;
+      }
+      n += __builtin_popcountll(mask);
     }
-    nheads = n;
+    if (tid == 0) nheads = min(n, 64);
   }
   __syncthreads();
   const int nh = nheads;
@@ -269,18 +278,27 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const float *__restri
   }
   const int n = min(k, (L - 1) / B + 1) * ns;  // parts of the selected blocks, in block order
   const int64_t base = ((int64_t)s * Hq + h) * k * ns;
+  const float *pl = part_lse + base;
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, part_lse[base + i]);
+  for (int i = 0; i < n; ++i) M = fmaxf(M, pl[i]);
   float sum = 0.f;
   for (int i = 0; i < n; ++i)
-    if (part_lse[base + i] > -INFINITY)
-      sum += __builtin_amdgcn_exp2f((part_lse[base + i] - M) * kLog2eDec);
+    if (pl[i] > -INFINITY) sum += __builtin_amdgcn_exp2f((pl[i] - M) * kLog2eDec);
   const float Lt = M + __logf(sum);
+  // part rows loaded 16 at a time, unconditionally (an empty part's row is
+  // written too), and added in part order
   float o = 0.f;
-  for (int i = 0; i < n; ++i)
-    if (part_lse[base + i] > -INFINITY)
-      o += __builtin_amdgcn_exp2f((part_lse[base + i] - Lt) * kLog2eDec) *
-           part_o[(base + i) * kHeadDim + e];
+  for (int i0 = 0; i0 < n; i0 += 16) {
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = i0 + u < n ? part_o[(base + i0 + u) * kHeadDim + e] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (i0 + u >= n) break;
+      if (pl[i0 + u] > -INFINITY)
+        o += __builtin_amdgcn_exp2f((pl[i0 + u] - Lt) * kLog2eDec) * x[u];
+    }
+  }
   dst[e] = (T)o;
   if (e == 0 && lse) lse[(int64_t)h * S + s] = Lt;
 }
