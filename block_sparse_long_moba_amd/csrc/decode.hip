@@ -26,12 +26,13 @@ constexpr float kLog2eDec = 1.4426950408889634f;
 constexpr float kLn2Dec = 0.6931471805599453f;
 constexpr int kDecKeyLanes = 16;                 // lanes per key row (8 dims each)
 constexpr int kDecGroups = 256 / kDecKeyLanes;   // key groups per workgroup
-constexpr int kDecMaxHeads = 8;                  // query heads per sweep over a block
+constexpr int kDecWaves = 4;                     // waves per workgroup
 
 template <typename T> struct Row8;
 template <> struct Row8<__bf16> {
-  __device__ static void load(const __bf16 *p, float *f) {
-    const uint4 u = *(const uint4 *)p;
+  using Raw = uint4;  // the 8 elements as loaded (half the registers of floats)
+  __device__ static Raw load_raw(const __bf16 *p) { return *(const uint4 *)p; }
+  __device__ static void unpack(const Raw &u, float *f) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -39,6 +40,7 @@ template <> struct Row8<__bf16> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ static void load(const __bf16 *p, float *f) { unpack(load_raw(p), f); }
   __device__ static void store(__bf16 *p, const float *f) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     bf16x8 v;
@@ -48,11 +50,15 @@ template <> struct Row8<__bf16> {
   }
 };
 template <> struct Row8<float> {
-  __device__ static void load(const float *p, float *f) {
-    const float4 a = ((const float4 *)p)[0], b = ((const float4 *)p)[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  struct Raw { float4 a, b; };
+  __device__ static Raw load_raw(const float *p) {
+    return Raw{((const float4 *)p)[0], ((const float4 *)p)[1]};
   }
+  __device__ static void unpack(const Raw &r, float *f) {
+    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+    f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
+  }
+  __device__ static void load(const float *p, float *f) { unpack(load_raw(p), f); }
   __device__ static void store(float *p, const float *f) {
     ((float4 *)p)[0] = make_float4(f[0], f[1], f[2], f[3]);
     ((float4 *)p)[1] = make_float4(f[4], f[5], f[6], f[7]);
@@ -136,7 +142,9 @@ __global__ __launch_bounds__(256) void decode_gate_kernel(const T *__restrict__ 
 // the block's rows (the own block up to the query's row) with an online
 // softmax per group, combined at the end through LDS. Writes the part of
 // slot (s, h, position of j in h's selection): o (fp32) and lse.
-template <typename T>
+// MH: query heads per sweep over the block (registers hold q and the output
+// accumulators of MH heads; 4 covers the 8B head shape's groups in one sweep)
+template <typename T, int MH>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ idx, int Hq, int Hkv, int B,
@@ -179,13 +187,16 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   const int64_t kstride = (int64_t)Hkv * kHeadDim;
   const T *kb = kc + (r0 * Hkv + g) * kHeadDim + 8 * li;
   const T *vb = vc + (r0 * Hkv + g) * kHeadDim + 8 * li;
-  __shared__ float gm[kDecGroups][kDecMaxHeads], gl[kDecGroups][kDecMaxHeads];
-  __shared__ float gacc[kDecGroups][kDecMaxHeads][kHeadDim];
-  for (int h0 = 0; h0 < nh; h0 += kDecMaxHeads) {
-    const int nq = min(kDecMaxHeads, nh - h0);
-    float qv[kDecMaxHeads][8], m[kDecMaxHeads], l[kDecMaxHeads], acc[kDecMaxHeads][8];
+  // per-wave states (the 4 key groups of a wave are merged with shuffles
+  // first), combined across the 4 waves through LDS
+  __shared__ float gm[kDecWaves][MH], gl[kDecWaves][MH];
+  __shared__ float gacc[kDecWaves][MH][kHeadDim];
+  const int wv = tid >> 6;
+  for (int h0 = 0; h0 < nh; h0 += MH) {
+    const int nq = min(MH, nh - h0);
+    float qv[MH][8], m[MH], l[MH], acc[MH][8];
 #pragma unroll
-    for (int qi = 0; qi < kDecMaxHeads; ++qi) {
+    for (int qi = 0; qi < MH; ++qi) {
       m[qi] = -INFINITY;
       l[qi] = 0.f;
 #pragma unroll
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     }
     auto consume = [&](const float (&kf)[8], const float (&vf)[8]) {
 #pragma unroll
-      for (int qi = 0; qi < kDecMaxHeads; ++qi) {
+      for (int qi = 0; qi < MH; ++qi) {
         if (qi >= nq) break;
         float d = 0.f;
 #pragma unroll
@@ -218,14 +229,19 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     constexpr int U = 4;
     int key = kg;
     for (; key + (U - 1) * kDecGroups < nk; key += U * kDecGroups) {
-      float kf[U][8], vf[U][8];
+      typename Row8<T>::Raw kr[U], vr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        Row8<T>::load(kb + (int64_t)(key + u * kDecGroups) * kstride, kf[u]);
-        Row8<T>::load(vb + (int64_t)(key + u * kDecGroups) * kstride, vf[u]);
+        kr[u] = Row8<T>::load_raw(kb + (int64_t)(key + u * kDecGroups) * kstride);
+        vr[u] = Row8<T>::load_raw(vb + (int64_t)(key + u * kDecGroups) * kstride);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) consume(kf[u], vf[u]);
+      for (int u = 0; u < U; ++u) {
+        float kf[8], vf[8];
+        Row8<T>::unpack(kr[u], kf);
+        Row8<T>::unpack(vr[u], vf);
+        consume(kf, vf);
+      }
     }
     for (; key < nk; key += kDecGroups) {
       float kf[8], vf[8];
@@ -234,19 +250,33 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
       consume(kf, vf);
     }
 #pragma unroll
-    for (int qi = 0; qi < kDecMaxHeads; ++qi) {
+    for (int qi = 0; qi < MH; ++qi) {
       if (qi >= nq) break;
+      // merge the online-softmax states of lanes li, li+16, li+32, li+48
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gacc[kg][qi][8 * li + e] = acc[qi][e];
-      if (li == 0) { gm[kg][qi] = m[qi]; gl[kg][qi] = l[qi]; }
+      for (int o = kDecKeyLanes; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(m[qi], o), l2 = __shfl_xor(l[qi], o);
+        const float M = fmaxf(m[qi], m2);
+        const float a1 = m[qi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qi] - M);
+        const float a2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+        l[qi] = l[qi] * a1 + l2 * a2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qi][e] = acc[qi][e] * a1 + __shfl_xor(acc[qi][e], o) * a2;
+        m[qi] = M;
+      }
+      if ((tid & 63) < kDecKeyLanes) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gacc[wv][qi][8 * li + e] = acc[qi][e];
+        if (li == 0) { gm[wv][qi] = m[qi]; gl[wv][qi] = l[qi]; }
+      }
     }
     __syncthreads();
     for (int x = tid; x < nq * kHeadDim; x += 256) {
       const int qi = x / kHeadDim, e = x % kHeadDim;
       float M = -INFINITY;
-      for (int gi = 0; gi < kDecGroups; ++gi) M = fmaxf(M, gm[gi][qi]);
+      for (int gi = 0; gi < kDecWaves; ++gi) M = fmaxf(M, gm[gi][qi]);
       float Ls = 0.f, o = 0.f;
-      for (int gi = 0; gi < kDecGroups; ++gi) {
+      for (int gi = 0; gi < kDecWaves; ++gi) {
         const float wgt = gm[gi][qi] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(gm[gi][qi] - M);
         Ls += gl[gi][qi] * wgt;
         o += gacc[gi][qi][e] * wgt;
@@ -325,17 +355,27 @@ hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const 
   if (pb.bf16) {
     decode_gate_kernel<__bf16><<<gg, 256, 0, s>>>((const __bf16 *)q, w.kbar, w.cu, w.blk_first,
                                                   pb.Hq, pb.Hkv, pb.B, pb.k, w.idx);
-    decode_attn_kernel<__bf16><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
-                                                  (const __bf16 *)vc, w.cu, w.idx, pb.Hq, pb.Hkv,
-                                                  pb.B, pb.k, ns, sl2, po, w.part_lse);
+    if (pb.G <= 4)
+      decode_attn_kernel<__bf16, 4><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
+                                                       (const __bf16 *)vc, w.cu, w.idx, pb.Hq,
+                                                       pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
+    else
+      decode_attn_kernel<__bf16, 8><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
+                                                       (const __bf16 *)vc, w.cu, w.idx, pb.Hq,
+                                                       pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
     decode_merge_kernel<__bf16><<<gg, 128, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
                                                    ns, (__bf16 *)out, lse);
   } else {
     decode_gate_kernel<float><<<gg, 256, 0, s>>>((const float *)q, w.kbar, w.cu, w.blk_first,
                                                  pb.Hq, pb.Hkv, pb.B, pb.k, w.idx);
-    decode_attn_kernel<float><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
-                                                 (const float *)vc, w.cu, w.idx, pb.Hq, pb.Hkv,
-                                                 pb.B, pb.k, ns, sl2, po, w.part_lse);
+    if (pb.G <= 4)
+      decode_attn_kernel<float, 4><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
+                                                      (const float *)vc, w.cu, w.idx, pb.Hq,
+                                                      pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
+    else
+      decode_attn_kernel<float, 8><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
+                                                      (const float *)vc, w.cu, w.idx, pb.Hq,
+                                                      pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
     decode_merge_kernel<float><<<gg, 128, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
                                                   ns, (float *)out, lse);
   }
