@@ -289,7 +289,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, w, args.cpu_rows)
+        cpu = cpu_baseline(inp, w, args.cpu_rows, args.gate, k, args.n_sink, args.extra_max,
+                           args.extra_min)
 
     res = {
         "metric": "MoBA fwd ms + effective TFLOP/s at 128K/1M tokens (8B heads), % MFMA peak",
@@ -424,6 +425,11 @@ def bwd_bench(args):
                 "traffic": None, "avg_launch_ms": kernels[dom]["avg_launch_ms"],
                 "launches_per_step": len(passes),
                 "flop_per_launch": kflop[dom] / len(passes)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_bwd(
+            inp, w, lambda rows: dout[torch.from_numpy(rows).cuda()].double().cpu().numpy(),
+            args.cpu_rows)
     es = 2
     n_hist = float(sum(hist_rows))
     hbm_bytes = {"delta": 2 * T * Hq * d * es + T * Hq * 4,
@@ -444,7 +450,7 @@ def bwd_bench(args):
                    "gate": {"kind": "mean"}, "parallelism": "single GPU"},
         "effective_flop": eff,
         "stage_ms": {n: round(x, 4) for n, x in stages.items()},
-        "kernels": kernels, "hbm": hbm, "roofline": roofline, "cpu_baseline": None,
+        "kernels": kernels, "hbm": hbm, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
@@ -466,7 +472,7 @@ def decode_bench(args):
     cu = inp.cu_seqlens
     qd = np.stack([inp.q[cu[s + 1] - 1] for s in range(S)])
     q, kc, vc, cud = (to_device(x) for x in (qd, inp.k, inp.v, cu))
-    del inp
+    inp_q_host, inp_k_host, inp_v_host = inp.q, inp.k, inp.v
     T = int(cu[-1])
     res = {}
     for name, topk in (("moba", k), ("dense", -(-L // B))):
@@ -506,6 +512,17 @@ def decode_bench(args):
                      "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log("%s decode: %.4f ms, %.1f GB/s" % (name, ms, res[name]["GB/s"]))
         del ws
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.asarray(cu[1:], dtype=np.int64) - 1  # the query is the last cache row
+        log("cpu baseline: oracle prefill result at the %d last rows" % S)
+        t0 = time.time()
+        oracle.moba(inp_q_host, inp_k_host, inp_v_host, cu, B, k, rows=rows)
+        dt = time.time() - t0
+        cpu = {"value": round(dt * 1e3, 3), "unit": "ms", "cores": _threads(), "kind": "oracle",
+               "sample": "the whole call: pooled keys of the cache's blocks, then selection "
+                         "and attention of the %d queries" % S}
     line = {
         "metric": "MoBA decode latency (one query per sequence over its KV cache)",
         "value": res["moba"]["ms"], "unit": "ms", "n_gpus": 1, "steps": args.steps,
@@ -519,40 +536,92 @@ def decode_bench(args):
         "dense_decode": res["dense"],
         "speedup_moba_vs_dense": round(res["dense"]["ms"] / res["moba"]["ms"], 3),
         "moba": res["moba"],
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(inp, w, n_rows):
-    """The fp64 oracle on a bounded sample of the same workload: pooled keys of
-    every block, then selection and attention for n sampled rows (all heads)."""
+def _threads():
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_baseline(inp, w, n_rows, gate="mean", k=None, n_sink=1, extra_max=1, extra_min=1):
+    """The fp64 oracle on a bounded sample of the same workload: the block
+    representations the gate needs (pooled keys of every block), then the
+    gate's selection and the attention for n sampled rows (all heads)."""
     import oracle
-    B, k, Hq = w.block_size, w.topk, w.num_q_heads
+    B, Hq = w.block_size, w.num_q_heads
+    k = w.topk if k is None else k
     rng = np.random.default_rng(w.seed + 77)
     T = w.total_tokens
     if n_rows <= 0:
         # about 15 s of attention work at ~1.5 GFLOP/s per thread (fp64, plain loops)
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         per_row = 4.0 * HEAD_DIM * Hq * (k * B)
-        n_rows = int(max(8, min(T, 15 * 1.5e9 * threads / per_row)))
+        n_rows = int(max(8, min(T, 15 * 1.5e9 * _threads() / per_row)))
     rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False)).astype(np.int64)
-    log("cpu baseline: oracle on %d sampled rows" % len(rows))
+    log("cpu baseline: oracle on %d sampled rows (%s gate)" % (len(rows), gate))
     t0 = time.time()
-    kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
-    sel, _, _ = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows)
+    if gate == "window":
+        sel = oracle.select_window(inp.cu_seqlens, B, k, n_sink, Hq, rows=rows, total_tokens=T)
+    else:
+        kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+        if gate == "pooled":
+            kmax, kmin = oracle.minmaxpool(inp.k, inp.cu_seqlens, B)
+            sel, _ = oracle.select_pooled(inp.q, kbar, kmax, kmin, inp.cu_seqlens, B, k,
+                                          extra_max, extra_min, rows=rows)
+        else:
+            sel, _, _ = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows)
     oracle.attend(inp.q, inp.k, inp.v, inp.cu_seqlens, B, k, sel, rows=rows)
     dt = time.time() - t0
-    cu = inp.cu_seqlens
+    flop = 4.0 * HEAD_DIM * float(attended_keys(inp.cu_seqlens, B, sel, rows).sum())
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s (effective)",
+            "cores": _threads(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "%d random rows x %d heads of %s (%s gate: block representations of all "
+                      "blocks, then selection and attention for the sampled rows)"
+                      % (len(rows), Hq, w.name, gate)}
+
+
+def attended_keys(cu, B, sel, rows):
+    """Keys attended per (sampled row, head) under selection sel[n][H][k]:
+    earlier chosen blocks in full, the own block up to the row."""
     seq = np.searchsorted(cu, rows, side="right") - 1
     local = rows - cu[seq]
     c = local // B
-    keys = (np.minimum(k, c + 1) - 1) * B + local % B + 1
-    flop = 4.0 * HEAD_DIM * Hq * float(keys.sum())
-    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s (effective)",
-            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "%d random rows x %d heads of %s (pooled keys of all blocks, then "
-                      "selection and attention for the sampled rows)" % (len(rows), Hq, w.name)}
+    L = cu[seq + 1] - cu[seq]
+    out = np.zeros(sel.shape[:2], dtype=np.int64)
+    for i in range(sel.shape[0]):
+        for h in range(sel.shape[1]):
+            for j in sel[i, h]:
+                if j < 0:
+                    continue
+                out[i, h] += (local[i] % B + 1) if j == c[i] else min(B, L[i] - j * B)
+    return out
+
+
+def cpu_baseline_bwd(inp, w, dout_rows_fn, n_rows):
+    """The fp64 oracle's gradient on a bounded sample: dq of n sampled rows
+    (all heads) over the oracle's selection; 6 d per attended (row, head, key)
+    (scores, dP and dq; the key-side gradients of a row cost the same again)."""
+    import oracle
+    B, k, Hq = w.block_size, w.topk, w.num_q_heads
+    rng = np.random.default_rng(w.seed + 78)
+    T = w.total_tokens
+    if n_rows <= 0:
+        per_row = 6.0 * HEAD_DIM * Hq * (k * B)
+        n_rows = int(max(8, min(T, 15 * 1.5e9 * _threads() / per_row)))
+    rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False)).astype(np.int64)
+    dout_rows = dout_rows_fn(rows)
+    log("cpu baseline: oracle dq on %d sampled rows" % len(rows))
+    t0 = time.time()
+    kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+    sel, _, _ = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows)
+    oracle.attend_bwd_dq_rows(inp.q, inp.k, inp.v, dout_rows, inp.cu_seqlens, B, k, sel, rows)
+    dt = time.time() - t0
+    flop = 6.0 * HEAD_DIM * float(attended_keys(inp.cu_seqlens, B, sel, rows).sum())
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s (6 d per attended pair)",
+            "cores": _threads(), "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "dq of %d random rows x %d heads of %s (pooled keys of all blocks, "
+                      "selection, scores, dP and dq for the sampled rows)" % (len(rows), Hq, w.name)}
 
 
 if __name__ == "__main__":
