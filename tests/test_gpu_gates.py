@@ -194,22 +194,30 @@ def test_pooled_gate_every_row(case):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("name", ["gqa32x8_t128k_b4096_k12_bf16", "gqa32x8_t1m_b4096_k12_bf16"])
 @pytest.mark.parametrize("kind", ["window", "pooled"])
-def test_gates_on_the_128k_workload_sampled_rows(kind):
+def test_gates_on_full_workloads_sampled_rows(kind, name):
+    """128K and 1M tokens, in the benchmark's launch configuration (its pass
+    size; the pooled gate with one extra block per pooling on top of k = 12)."""
     import torch
-    w = synth.WORKLOADS["gqa32x8_t128k_b4096_k12_bf16"]
+    w = synth.WORKLOADS[name]
     inp = synth.generate(w)
     B = w.block_size
     topk = 12 if kind == "window" else 14
     gate = moba.gate_window(1) if kind == "window" else moba.gate_pooled(1, 1)
-    note("128K %s gate: GPU run" % kind)
-    q, kk, v, cu, sh, lay, ws = setup(inp, B, topk, kv_heads_per_pass=2)
+    P = w.num_kv_heads
+    full = moba.make_shape(w.total_tokens, len(w.lengths), w.num_q_heads, w.num_kv_heads, 128,
+                           w.dtype)
+    while P > 1 and moba.moba_fwd_workspace_size(full, B, topk, P) > (48 << 30):
+        P //= 2
+    note("%s %s gate: GPU run, pass of %d kv heads" % (name, kind, P))
+    q, kk, v, cu, sh, lay, ws = setup(inp, B, topk, kv_heads_per_pass=P)
     out, lse = moba.moba_fwd_gated(q, kk, v, cu, B, topk, gate, ws)
     torch.cuda.synchronize()
     rows = check.sample_rows(inp.cu_seqlens, B, 4, w.seed)
     rng = np.random.default_rng(w.seed + 3000)
     out_rows = np.unique(np.concatenate([rng.choice(rows, 96, replace=False), [0, len(inp.q) - 1]]))
-    note("128K %s gate: oracle on %d rows" % (kind, len(out_rows)))
+    note("%s %s gate: oracle on %d rows" % (name, kind, len(out_rows)))
     if kind == "window":
         use = oracle.select_window(inp.cu_seqlens, B, topk, 1, w.num_q_heads, rows=out_rows)
     else:
