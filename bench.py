@@ -120,7 +120,7 @@ def main():
                     help="time decode instead: S sequences with KV caches of L tokens each "
                     "(e.g. 1x1048576 or 32x32768), one new query per sequence")
     ap.add_argument("--bwd", action="store_true",
-                    help="time the backward pass (dq, dk, dv; mean gate) instead of the forward")
+                    help="time the backward pass (dq, dk, dv; with --gate) instead of the forward")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows the CPU oracle times (0 = sized for about 15 s)")
     args = ap.parse_args()
@@ -332,6 +332,10 @@ def bwd_bench(args):
     w = synth.WORKLOADS[args.workload]
     assert w.dtype == "bf16", "the backward pass is bf16 only"
     B, k, Hq, Hkv = w.block_size, w.topk, w.num_q_heads, w.num_kv_heads
+    if args.gate == "pooled":
+        k += args.extra_max + args.extra_min
+    gate = {"mean": moba.gate_mean(), "window": moba.gate_window(args.n_sink),
+            "pooled": moba.gate_pooled(args.extra_max, args.extra_min)}[args.gate]
     T = w.total_tokens
     log("bwd, workload %s: generating seeded inputs" % w.name)
     inp = synth.generate(w)
@@ -343,7 +347,7 @@ def bwd_bench(args):
         P //= 2
     fws = torch.empty(moba.moba_fwd_workspace_size(shape, B, k, P), dtype=torch.uint8,
                       device="cuda")
-    out, lse = moba.moba_fwd_ex(q, kk, v, cu, B, k, fws, max_seqlen=max(w.lengths))
+    out, lse = moba.moba_fwd_gated(q, kk, v, cu, B, k, gate, fws, max_seqlen=max(w.lengths))
     torch.cuda.synchronize()
     del fws
     gen = torch.Generator(device="cuda").manual_seed(w.seed + 5)
@@ -358,12 +362,26 @@ def bwd_bench(args):
     log("bwd workspace %.1f GiB, %d pass(es) of %d kv heads" % (
         lay.total_bytes / 2**30, len(passes), lay.kv_heads_per_pass))
 
+    def run_gate(g0):
+        if args.gate == "window":
+            moba.moba_gate_window(shape, B, k, args.n_sink, lay, ws, g0)
+        elif args.gate == "pooled":
+            moba.moba_gate_pooled(q, shape, B, k, args.extra_max, args.extra_min, lay, ws, g0)
+        else:
+            moba.moba_gate(q, shape, B, k, lay, ws, g0)
+
+    def pools():
+        if args.gate != "window":
+            moba.moba_meanpool(kk, shape, B, lay, ws)
+        if args.gate == "pooled":
+            moba.moba_minmaxpool(kk, shape, B, lay, ws)
+
     def step(tm):
         tm.run("seqtable", lambda: moba.moba_seqtable(cu, shape, B, lay, ws))
-        tm.run("meanpool", lambda: moba.moba_meanpool(kk, shape, B, lay, ws))
+        tm.run("meanpool", pools)
         tm.run("delta", lambda: moba.moba_bwd_delta(out, dout, shape, B, k, lay, ws))
         for g0 in passes:
-            tm.run("gate", lambda: moba.moba_gate(q, shape, B, k, lay, ws, g0))
+            tm.run("gate", lambda: run_gate(g0))
             tm.run("dispatch", lambda: moba.moba_dispatch(shape, B, k, lay, ws, g0))
             tm.run("ktrans", lambda: moba.moba_ktrans(kk, shape, B, k, lay, ws, g0))
             tm.run("dq_diag", lambda: moba.moba_attn_bwd_dq(q, kk, v, dout, lse, shape, B, k,
@@ -377,9 +395,9 @@ def bwd_bench(args):
     nbins = lay.kv_heads_per_pass * lay.num_blocks_bound
     hist_rows = []
     moba.moba_seqtable(cu, shape, B, lay, ws)
-    moba.moba_meanpool(kk, shape, B, lay, ws)
+    pools()
     for g0 in passes:
-        moba.moba_gate(q, shape, B, k, lay, ws, g0)
+        run_gate(g0)
         moba.moba_dispatch(shape, B, k, lay, ws, g0)
         torch.cuda.synchronize()
         off = workspace_view(ws, lay.bins_offset + 4 * nbins, nbins + 1, torch.int32)
@@ -429,7 +447,7 @@ def bwd_bench(args):
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_bwd(
             inp, w, lambda rows: dout[torch.from_numpy(rows).cuda()].double().cpu().numpy(),
-            args.cpu_rows)
+            args.cpu_rows, args.gate, k, args.n_sink, args.extra_max, args.extra_min)
     es = 2
     n_hist = float(sum(hist_rows))
     hbm_bytes = {"delta": 2 * T * Hq * d * es + T * Hq * 4,
@@ -447,7 +465,11 @@ def bwd_bench(args):
         "config": {"workload": w.name, "pass": "backward", "seq_lens": list(w.lengths),
                    "total_tokens": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "block_size": B, "topk": k, "kv_heads_per_pass": lay.kv_heads_per_pass,
-                   "gate": {"kind": "mean"}, "parallelism": "single GPU"},
+                   "gate": {"mean": {"kind": "mean"},
+                            "window": {"kind": "window", "n_sink": args.n_sink},
+                            "pooled": {"kind": "pooled", "extra_max": args.extra_max,
+                                       "extra_min": args.extra_min}}[args.gate],
+                   "parallelism": "single GPU"},
         "effective_flop": eff,
         "stage_ms": {n: round(x, 4) for n, x in stages.items()},
         "kernels": kernels, "hbm": hbm, "roofline": roofline, "cpu_baseline": cpu,
@@ -598,12 +620,14 @@ def attended_keys(cu, B, sel, rows):
     return out
 
 
-def cpu_baseline_bwd(inp, w, dout_rows_fn, n_rows):
+def cpu_baseline_bwd(inp, w, dout_rows_fn, n_rows, gate="mean", k=None, n_sink=1, extra_max=1,
+                     extra_min=1):
     """The fp64 oracle's gradient on a bounded sample: dq of n sampled rows
-    (all heads) over the oracle's selection; 6 d per attended (row, head, key)
+    (all heads) over the gate's selection; 6 d per attended (row, head, key)
     (scores, dP and dq; the key-side gradients of a row cost the same again)."""
     import oracle
-    B, k, Hq = w.block_size, w.topk, w.num_q_heads
+    B, Hq = w.block_size, w.num_q_heads
+    k = w.topk if k is None else k
     rng = np.random.default_rng(w.seed + 78)
     T = w.total_tokens
     if n_rows <= 0:
@@ -611,17 +635,26 @@ def cpu_baseline_bwd(inp, w, dout_rows_fn, n_rows):
         n_rows = int(max(8, min(T, 15 * 1.5e9 * _threads() / per_row)))
     rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False)).astype(np.int64)
     dout_rows = dout_rows_fn(rows)
-    log("cpu baseline: oracle dq on %d sampled rows" % len(rows))
+    log("cpu baseline: oracle dq on %d sampled rows (%s gate)" % (len(rows), gate))
     t0 = time.time()
-    kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
-    sel, _, _ = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows)
+    if gate == "window":
+        sel = oracle.select_window(inp.cu_seqlens, B, k, n_sink, Hq, rows=rows, total_tokens=T)
+    else:
+        kbar = oracle.meanpool(inp.k, inp.cu_seqlens, B)
+        if gate == "pooled":
+            kmax, kmin = oracle.minmaxpool(inp.k, inp.cu_seqlens, B)
+            sel, _ = oracle.select_pooled(inp.q, kbar, kmax, kmin, inp.cu_seqlens, B, k,
+                                          extra_max, extra_min, rows=rows)
+        else:
+            sel, _, _ = oracle.select(inp.q, kbar, inp.cu_seqlens, B, k, rows=rows)
     oracle.attend_bwd_dq_rows(inp.q, inp.k, inp.v, dout_rows, inp.cu_seqlens, B, k, sel, rows)
     dt = time.time() - t0
     flop = 6.0 * HEAD_DIM * float(attended_keys(inp.cu_seqlens, B, sel, rows).sum())
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s (6 d per attended pair)",
             "cores": _threads(), "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "dq of %d random rows x %d heads of %s (pooled keys of all blocks, "
-                      "selection, scores, dP and dq for the sampled rows)" % (len(rows), Hq, w.name)}
+            "sample": "dq of %d random rows x %d heads of %s (%s gate: block representations "
+                      "of all blocks, selection, scores, dP and dq for the sampled rows)"
+                      % (len(rows), Hq, w.name, gate)}
 
 
 if __name__ == "__main__":
