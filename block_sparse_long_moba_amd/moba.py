@@ -380,3 +380,60 @@ def moba_dense_causal_fwd(q, k, v, cu_seqlens, out=None, lse=None, softmax_scale
                                        ctypes.byref(sh), softmax_scale, _ptr(out), _ptr(lse),
                                        _ptr(workspace), nbytes, _stream(stream)))
     return out, lse
+
+
+def _autograd_function():
+    """torch.autograd.Function over moba_fwd_gated and moba_bwd (built on first
+    use so that importing this module does not import torch)."""
+    import torch
+
+    class MobaAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, cu_seqlens, block_size, topk, gate, softmax_scale, max_seqlen):
+            gate = gate_mean() if gate is None else gate
+            sh = shape_of(q, k, cu_seqlens, max_seqlen)
+            # the largest pass (a divisor of Hkv) whose workspace fits the limit
+            P = sh.num_kv_heads
+            limit = int(float(os.environ.get("MOBA_WORKSPACE_LIMIT_GIB", "48")) * (1 << 30))
+            while P > 1 and moba_fwd_workspace_size(sh, block_size, topk, P) > limit:
+                P -= 1
+            ws = torch.empty(moba_fwd_workspace_size(sh, block_size, topk, P), dtype=torch.uint8,
+                             device=q.device)
+            out, lse = moba_fwd_gated(q, k, v, cu_seqlens, block_size, topk, gate, ws,
+                                      softmax_scale=softmax_scale, max_seqlen=max_seqlen)
+            ctx.save_for_backward(q, k, v, cu_seqlens, out, lse)
+            ctx.args = (block_size, topk, gate, softmax_scale, max_seqlen)
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, cu_seqlens, out, lse = ctx.saved_tensors
+            block_size, topk, gate, softmax_scale, max_seqlen = ctx.args
+            sh = shape_of(q, k, cu_seqlens, max_seqlen)
+            limit = int(float(os.environ.get("MOBA_WORKSPACE_LIMIT_GIB", "48")) * (1 << 30))
+            P = sh.num_kv_heads
+            while P > 1 and moba_bwd_workspace_size(sh, block_size, topk, P) > limit:
+                P -= 1
+            ws = torch.empty(moba_bwd_workspace_size(sh, block_size, topk, P), dtype=torch.uint8,
+                             device=q.device)
+            dq, dk, dv = moba_bwd(q, k, v, out, lse, dout.contiguous(), cu_seqlens, block_size,
+                                  topk, ws, gate=gate, softmax_scale=softmax_scale,
+                                  max_seqlen=max_seqlen)
+            return dq, dk, dv, None, None, None, None, None, None
+
+    return MobaAttention
+
+
+_MobaAttention = None
+
+
+def moba_attention(q, k, v, cu_seqlens, block_size, topk, gate=None, softmax_scale=0.0,
+                   max_seqlen=0):
+    """Differentiable MoBA attention (bf16 for gradients): out = moba_fwd_gated(...),
+    and autograd calls moba_bwd for dq, dk, dv. The workspaces are allocated
+    per call (a pass size that fits MOBA_WORKSPACE_LIMIT_GIB, default 48)."""
+    global _MobaAttention
+    if _MobaAttention is None:
+        _MobaAttention = _autograd_function()
+    return _MobaAttention.apply(q, k, v, cu_seqlens, block_size, topk, gate, softmax_scale,
+                                max_seqlen)

@@ -305,3 +305,31 @@ def test_bwd_full_workload_sampled_rows_and_identities(name):
     st = compare("dq", to_host_f64(dq[rows_t]), ref)
     note("bwd workload %s: dq %s, selection differs in %d near ties" % (name, st,
                                                                          int(differs.sum())))
+
+
+def test_autograd_function_matches_the_entry_points():
+    """moba_attention (torch.autograd) runs moba_fwd_gated forward and moba_bwd
+    backward: its out and gradients equal those of the direct calls."""
+    import torch
+    B, k = 128, 4
+    inp = synth.custom([900, 400], 8, 2, 128, "bf16", B, k, 74)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    for gate in (None, moba.gate_window(1)):
+        qa, ka, va = (x.clone().requires_grad_() for x in (q, kk, v))
+        out = moba.moba_attention(qa, ka, va, cu, B, k, gate=gate)
+        dout = torch.randn(out.shape, generator=torch.Generator().manual_seed(3)).to(
+            torch.bfloat16).cuda()
+        out.backward(dout)
+        sh = moba.shape_of(q, kk, cu)
+        fws = torch.empty(moba.moba_fwd_workspace_size(sh, B, k, 0), dtype=torch.uint8,
+                          device="cuda")
+        o2, l2 = moba.moba_fwd_gated(q, kk, v, cu, B, k, gate or moba.gate_mean(), fws)
+        bws = torch.empty(moba.moba_bwd_workspace_size(sh, B, k, 0), dtype=torch.uint8,
+                          device="cuda")
+        dq, dk, dv = moba.moba_bwd(q, kk, v, o2, l2, dout, cu, B, k, bws, gate=gate)
+        torch.cuda.synchronize()
+        assert torch.equal(out.detach(), o2)
+        assert torch.equal(qa.grad, dq)
+        for a_, b_ in ((ka.grad, dk), (va.grad, dv)):
+            diff = (a_.float() - b_.float()).abs().max().item()
+            assert diff <= 2.0 ** -7 * b_.float().abs().max().item(), diff
