@@ -135,3 +135,25 @@ def custom(lengths, hq, hkv, d, dtype, block_size, topk, seed, name="custom") ->
     """Inputs for an ad-hoc shape with the same recipe (used by tests)."""
     return generate(Workload(name, tuple(int(x) for x in lengths), hq, hkv, d, dtype, block_size,
                              topk, seed))
+
+
+def ramped(inp: Inputs, q_scale: float, k_lo: float, k_hi: float) -> Inputs:
+    """A copy of `inp` with the queries multiplied by q_scale and each key row
+    by a factor that grows linearly from k_lo to k_hi across its block (local
+    position / block size). Later keys of a block then score ever higher, so
+    the running maximum of an online softmax keeps moving inside a block.
+    Values are rounded back to the workload's dtype."""
+    w = inp.workload
+    bf16 = w.dtype == "bf16"
+
+    def f32(x):
+        return bf16_bits_to_f32(x) if bf16 else np.asarray(x, dtype=np.float32)
+
+    def back(x):
+        return f32_to_bf16_bits(x) if bf16 else x.astype(np.float32)
+
+    pos = np.concatenate([np.arange(n) % w.block_size for n in w.lengths]).astype(np.float32)
+    fac = np.float32(k_lo) + np.float32(k_hi - k_lo) * pos / np.float32(w.block_size)
+    q = back(f32(inp.q) * np.float32(q_scale))
+    k = back(f32(inp.k) * fac[:, None, None])
+    return Inputs(w, q, k, inp.v.copy(), inp.cu_seqlens)
