@@ -21,9 +21,9 @@
 //   of 256 keys), 8 waves of 32 keys with V in registers and K in LDS as
 //   MFMA B operands. The block's own rows (for each query head of the kv head,
 //   causally) and then the rows of its bin stream through LDS in tiles of 32
-//   rows, stored both row-major and transposed. Per tile S = Q K^T,
-//   dP = dO V^T, dS, dV^T += dO^T P and dK^T += Q^T dS; dK and dV are written
-//   once.
+//   rows, stored row-major; the transposed operands come from the same tiles
+//   through the LDS transpose read. Per tile S = Q K^T, dP = dO V^T, dS,
+//   dV^T += dO^T P and dK^T += Q^T dS; dK and dV are written once.
 // Lane layouts: v_mfma_f32_32x32x16_bf16, lane l holds A[m = l%32][k = 8(l/32)
 // .. +7] and B[k = 8(l/32) .. +7][n = l%32]; accumulator i of lane l is
 // C[8(i/4) + 4(l/32) + i%4][l%32]. Feeding M-row m from source row perm(m)
@@ -71,6 +71,26 @@ __device__ __forceinline__ floatx16 mfma(const bf16x8 &a, const bf16x8 &b, const
 
 __device__ __forceinline__ int perm32(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// dK/dV tiles: M row (or K index) 16 c + 8 a + 4 b + e (a, b in {0, 1},
+// e < 4) takes tile row 16 c + 4 e + 2 b + a, so that accumulator i = 8 c + j
+// of lane half hh holds row 16 c + 4 (j % 4) + 2 hh + j / 4: its 8 rows are
+// the K slice the lane passes on, read 4 rows apart by the transpose reads.
+__device__ __forceinline__ int perm_tr(int m) {
+  return (m & 16) | ((m & 3) << 2) | (((m >> 2) & 1) << 1) | ((m >> 3) & 1);
+}
+// Inverse: the position 16 c + 8 b + 4 a + e that tile row 16 c + 4 e + 2 b + a
+// takes in that order.
+__device__ __forceinline__ int perm_tr_pos(int r) {
+  return (r & 16) | (((r >> 1) & 1) << 3) | ((r & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t *lds_short4_t;
+// ds_read_b64_tr_b16 at an 8-byte-aligned LDS address
+__device__ __forceinline__ bf16x4 tr_read(const char *p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t)p));
 }
 
 // Raw buffer descriptor from wave-uniform values; offsets past `bytes` read 0.
@@ -354,21 +374,25 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
 // ---- dK, dV: keys resident, rows streamed.
 //
 // LDS per stage: Q and dO tiles row-major (32 rows of 256 B at a pitch of
-// 272 B), then Q^T and dO^T (128 rows (d) of 32 elements at a pitch of 80 B);
-// after both stages, per stage the 32 rows' lse (log2 units) and D; then the
-// waves' K rows. The
-// padding makes the 16 rows (or d rows) that 16 lanes read at one chunk
-// column fall in 16 different 16-byte bank groups, and every lane's operand
-// addresses a base plus compile-time offsets. Rows past the end of a tile
+// 272 B); after both stages, per stage the 32 rows' lse (log2 units) and D;
+// then the waves' K rows. The padding puts row r at bank group 4r mod 64, so
+// the 16 rows that 16 lanes read at one chunk column fall in 16 different
+// 16-byte bank groups. The transposed operands (Q^T, dO^T as A operands of
+// dK^T and dV^T) come from the same tiles through ds_read_b64_tr_b16: in each
+// 16-lane group, output lane 4p+q receives as element j element q of the
+// 8 bytes that lane 4j+p addressed. Row r of a tile feeds the MFMAs' M row
+// (or K index) perm_tr so that one transpose read takes rows 4 apart, whose
+// bank groups are 16 apart: conflict-free. Every lane's operand addresses a
+// base plus compile-time offsets. Rows past the end of a tile
 // have q = dO = 0, lse = +inf and D = 0, so their probabilities and dS are
 // exactly 0. Per tile: S, then P in place of S, then dP interleaved with the
 // dV products, then dS and the dK products; nothing the tile computes waits
 // for the next tile's rows, which are fetched into registers before it and
 // stored to LDS after it.
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int NP = 272, TP = 80;  // pitches of the row-major and transposed tiles
-  constexpr int QN = 0, DN = 32 * NP, QT = 64 * NP, DTT = 64 * NP + 128 * TP;
-  constexpr int STAGE = 64 * NP + 256 * TP, LD = 2 * STAGE, KW = LD + 2 * 256;
+  constexpr int NP = 272;  // pitch of a tile row
+  constexpr int QN = 0, DN = 32 * NP;
+  constexpr int STAGE = 64 * NP, LD = 2 * STAGE, KW = LD + 2 * 256;
   __shared__ __attribute__((aligned(1024))) char lds[KW + 8 * 32 * NP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -420,6 +444,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 
   // loader: thread (row lr, chunk lc of 8 elements)
   const int lr = threadIdx.x & 31, lc = threadIdx.x >> 5;
+  const int lr_pos = perm_tr_pos(lr);
   // the item of this thread's row in tile `it`, clamped to an existing entry
   // (own tiles and rows past the bin read one whose value goes unused): always
   // a load, so its register is never written conditionally while a load may
@@ -461,24 +486,29 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     }
     *(bf16x8 *)(S_ + QN + lr * NP + lc * 16) = sq;
     *(bf16x8 *)(S_ + DN + lr * NP + lc * 16) = sdo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int off = (8 * lc + e) * TP + lr * 2;
-      *(__bf16 *)(S_ + QT + off) = sq[e];
-      *(__bf16 *)(S_ + DTT + off) = sdo[e];
-    }
     if (lc == 0) {
+      // row lr's values go where the lane that holds its scores reads them
       float *L = (float *)(lds + LD + stage * 256);
-      L[lr] = sok ? sl * kLog2e : INFINITY;
-      L[32 + lr] = sok ? sd : 0.f;
+      const int pos = lr_pos;
+      L[pos] = sok ? sl * kLog2e : INFINITY;
+      L[32 + pos] = sok ? sd : 0.f;
     }
   };
 
-  // LDS read offsets: Q / dO rows as A operands of S and dP (row perm(n));
-  // Q^T / dO^T rows (d = 32 dt + n) as A operands of dK^T and dV^T
-  const int qrd = perm32(n) * NP + hh * 16;  // + 32 kk: chunk 2 kk + hh
-  const int trd = n * TP + hh * 16;          // + 2560 dt + 32 c: rows 16 c + 8 hh ..
+  // LDS read offsets: Q / dO rows as A operands of S and dP (row perm_tr(n));
+  // transpose reads of Q^T / dO^T as A operands of dK^T and dV^T: for MFMA
+  // (dt, c) read h of lane s takes the 8 bytes at row 16 c + 4 ((s % 16) / 4)
+  // + 2 (s / 32) + h, columns 32 dt + 16 ((s / 16) % 2) + 4 (s % 4) .. +3,
+  // which hands lane l the rows of its K indices 8 hh + 4 h .. +3 at column
+  // 32 dt + l % 32
+  const int qrd = perm_tr(n) * NP + hh * 16;  // + 32 kk: chunk 2 kk + hh
+  const int trl = (4 * ((lane & 15) >> 2) + 2 * hh) * NP + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
   const float c2 = a.c2;
+  auto tr_a = [&](const char *tile, int dt, int c) {
+    const bf16x4 lo = tr_read(tile + trl + 16 * c * NP + 64 * dt);
+    const bf16x4 hi = tr_read(tile + trl + (16 * c + 1) * NP + 64 * dt);
+    return (bf16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
 
   auto compute = [&](int it, int stage) {
     if (kw >= bi.z) return;  // every key of this wave is past the block's end
@@ -508,7 +538,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * c + j;
         float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[j]));
-        if (own && key > rt + 16 * c + 8 * hh + j) pv = 0.f;
+        if (own && key > rt + 16 * c + 4 * (j & 3) + 2 * hh + (j >> 2)) pv = 0.f;
         s[i] = pv;
       }
     }
@@ -523,7 +553,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        dv[dt] = mfma(*(const bf16x8 *)(S_ + DTT + trd + dt * 32 * TP + 32 * c), pb[c], dv[dt]);
+        dv[dt] = mfma(tr_a(S_ + DN, dt, c), pb[c], dv[dt]);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const float4 d0 = *(const float4 *)(L + 32 + 16 * c + 8 * hh);
@@ -536,7 +566,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dk[dt] = mfma(*(const bf16x8 *)(S_ + QT + trd + dt * 32 * TP + 32 * c), db[c], dk[dt]);
+        dk[dt] = mfma(tr_a(S_ + QN, dt, c), db[c], dk[dt]);
       }
   };
 

@@ -126,6 +126,35 @@ def test_bwd_matches_oracle_on_every_element(case):
     note("stats %s selection_differs_in_near_ties=%d" % (stats, n_diff))
 
 
+def test_bwd_with_a_moving_maximum():
+    """Keys that grow across each block (scores of tens of log2 units, close
+    to one-hot rows): the backward pass recomputes P from lse at those
+    magnitudes. Every element against the oracle."""
+    import torch
+    lengths, hq, hkv, B, k, seed = [2048, 600], 8, 2, 256, 3, 69
+    inp = synth.ramped(synth.custom(lengths, hq, hkv, 128, "bf16", B, k, seed), 3.0, 0.25, 4.0)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    sh = moba.shape_of(q, kk, cu)
+    fwd_ws = torch.empty(moba.moba_fwd_workspace_size(sh, B, k, 0), dtype=torch.uint8,
+                         device="cuda")
+    out, lse = moba.moba_fwd_ex(q, kk, v, cu, B, k, fwd_ws)
+    T = inp.q.shape[0]
+    rng = np.random.default_rng(seed + 1000)
+    dout = torch.from_numpy(rng.standard_normal((T, hq, 128), dtype=np.float32)).to(
+        torch.bfloat16).cuda()
+    lay = moba.moba_bwd_plan(sh, B, k, 0)
+    ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = moba.moba_bwd(q, kk, v, out, lse, dout, cu, B, k, ws)
+    torch.cuda.synchronize()
+    gidx = workspace_view(ws, lay.idx_offset, T * hq * k, torch.int32).view(T, hq, k).cpu().numpy()
+    sel, n_diff = checked_selection(inp, B, k, "mean", gidx)
+    ref = oracle.attend_bwd(inp.q, inp.k, inp.v, to_host_f64(dout), inp.cu_seqlens, B, k,
+                            np.ascontiguousarray(sel))
+    stats = {name: compare(name, to_host_f64(got), r)
+             for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)}
+    note("stats %s selection_differs_in_near_ties=%d" % (stats, n_diff))
+
+
 def test_bwd_pass_sizes_agree_and_repeat():
     """One pass of all kv heads and passes of one kv head give the same
     gradients; dq and dk/dv do not depend on the bin item order beyond
