@@ -164,6 +164,7 @@ moba_status_t bwd_plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_
   off = align_up(off + sizeof(float) * (size_t)slots * kHeadDim);
   L->part_lse_offset = off;
   off = align_up(off + sizeof(float) * (size_t)T * sh->num_q_heads);
+  off = align_up(off + kBwdZeroBytes);
   L->total_bytes = off;
   return MOBA_SUCCESS;
 }
@@ -257,7 +258,8 @@ moba_status_t check_pass(const moba_shape_t *sh, const moba_layout_t *L, int32_t
 // (lists at the start of the partial-dq region, at most (topk + 2) ints per
 // (row, head); the per-slot lse in its last T*Hp*topk floats) kept away from D.
 BwdWork carve_bwd(const Problem &pb, const moba_layout_t *L, void *ws, Work *w) {
-  BwdWork bw{(float *)((char *)ws + L->part_o_offset), (float *)((char *)ws + L->part_lse_offset)};
+  BwdWork bw{(float *)((char *)ws + L->part_o_offset), (float *)((char *)ws + L->part_lse_offset),
+             (char *)ws + L->total_bytes - align_up(kBwdZeroBytes)};
   const int64_t slots = pb.T * pb.Hp * pb.k;
   w->part_o = bw.dq_part;
   w->part_lse = bw.dq_part + slots * (kHeadDim - 1);

@@ -63,6 +63,7 @@ struct BwdArgs {
   const int4 *tile_rec;
   float *dq_part;
   __bf16 *dk, *dv;
+  const void *zeros;  // 256 zero bytes: the rows past the end of a dK/dV tile
 };
 
 __device__ __forceinline__ floatx16 mfma(const bf16x8 &a, const bf16x8 &b, const floatx16 &c) {
@@ -105,6 +106,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base,
 
 // Wait for every vector memory load of the wave (and its LDS accesses).
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x70); }
+// Wait until at most N vector memory loads of this wave are outstanding (and
+// for its LDS accesses).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(N | 0x70);
+}
+
+typedef __attribute__((address_space(1))) const void *global_ptr_t;
+
+// Workgroup barrier that orders LDS only: this wave's LDS accesses complete,
+// then s_barrier. Unlike __syncthreads it does not wait for the wave's
+// outstanding vector memory loads, so direct-to-LDS loads of later tiles
+// stay in flight; every wave waits for its own loads of the next tile before
+// it. The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void store_bf16x4(__bf16 *p, float a, float b, float c, float d) {
   bf16x4 v;
@@ -373,27 +395,47 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
 
 // ---- dK, dV: keys resident, rows streamed.
 //
-// LDS per stage: Q and dO tiles row-major (32 rows of 256 B at a pitch of
-// 272 B); after both stages, per stage the 32 rows' lse (log2 units) and D;
-// then the waves' K rows. The padding puts row r at bank group 4r mod 64, so
-// the 16 rows that 16 lanes read at one chunk column fall in 16 different
-// 16-byte bank groups. The transposed operands (Q^T, dO^T as A operands of
-// dK^T and dV^T) come from the same tiles through ds_read_b64_tr_b16: in each
-// 16-lane group, output lane 4p+q receives as element j element q of the
-// 8 bytes that lane 4j+p addressed. Row r of a tile feeds the MFMAs' M row
-// (or K index) perm_tr so that one transpose read takes rows 4 apart, whose
-// bank groups are 16 apart: conflict-free. Every lane's operand addresses a
-// base plus compile-time offsets. Rows past the end of a tile
-// have q = dO = 0, lse = +inf and D = 0, so their probabilities and dS are
-// exactly 0. Per tile: S, then P in place of S, then dP interleaved with the
-// dV products, then dS and the dK products; nothing the tile computes waits
-// for the next tile's rows, which are fetched into registers before it and
-// stored to LDS after it.
+// LDS: three stages of {Q tile, dO tile}, each 32 rows of 256 B at a pitch
+// of 272 B, as three separate arrays; four slots of the 32 rows' lse (log2
+// units) and D; two slots of the rows' (token, head); the waves' K rows
+// (pitch 272 B). The padding puts row r at bank group 4r mod 64, so the 16
+// rows that 16 lanes read at one chunk column fall in 16 different 16-byte
+// bank groups. The transposed operands (Q^T, dO^T as A operands of dK^T and
+// dV^T) come from the same tiles through ds_read_b64_tr_b16: in each 16-lane
+// group, output lane 4p+q receives as element j element q of the 8 bytes that
+// lane 4j+p addressed. Row r of a tile feeds the MFMAs' M row (or K index)
+// perm_tr so that one transpose read takes rows 4 apart, whose bank groups
+// are 16 apart: conflict-free. Every lane's operand addresses a base plus
+// compile-time offsets.
+//
+// The Q and dO tiles of a stage are 2 x 32 x 17 slots of 16 B (the 17th slot
+// of a row is padding), filled by 17 wave-wide direct loads of 64 slots,
+// three each on waves 0, 2 and 3 and two each on waves 4..7. A row past the
+// end of the
+// tile loads from a zeroed 256-byte area and gets lse = +inf and D = 0, so its
+// probabilities and dS are exactly 0. Tile x's rows are fetched two tiles
+// ahead: in the body of tile x - 2, wave 1 (lanes 0..31, one row each) loads
+// the items of tile x + 1 and the lse and D of tile x into registers; every
+// wave issues tile x's Q and dO loads from the (token, head) slot; at the end
+// of the body wave 1 stores the lse and D and decodes the items into
+// (token, head); wave 1 issues no direct loads, so that nothing it waits for
+// is a tile load. A body ends when each wave's loads of the next tile have
+// landed, with a barrier that leaves the loads of the tile after in flight.
+// The loop is unrolled by the three stages so that every access names its
+// stage array: the compiler then sees that a body's direct loads and its LDS
+// reads never overlap and adds no waits between them.
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int NP = 272;  // pitch of a tile row
-  constexpr int QN = 0, DN = 32 * NP;
-  constexpr int STAGE = 64 * NP, LD = 2 * STAGE, KW = LD + 2 * 256;
-  __shared__ __attribute__((aligned(1024))) char lds[KW + 8 * 32 * NP];
+  constexpr int NP = 272;                   // pitch of a tile row
+  constexpr int SLOTS = 17;                 // 16-byte slots per tile row
+  constexpr int QN = 0, DN = kKvRows * NP;  // Q and dO tiles of a stage
+  constexpr int STAGE = 2 * kKvRows * NP;
+  static_assert(2 * kKvRows * SLOTS == 17 * 64, "17 direct loads per tile");
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
+  __shared__ __attribute__((aligned(16))) float lse_d[4][2 * kKvRows];  // [slot][lse 32, D 32]
+  __shared__ __attribute__((aligned(16))) int2 rinfo[2][kKvRows];       // (token, head)
+  __shared__ __attribute__((aligned(1024))) char klds[8 * 32 * NP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
@@ -414,11 +456,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int key = kw + n;
   const bool kvalid = key < bi.z;
 
-  // K and V rows of this lane's key as MFMA B operands (k = d); a lane past
-  // the block's end takes the block's first row (its results are dropped)
   // K rows of this wave's keys in LDS (32 rows at pitch NP; each lane reads
-  // back what it wrote), V rows in registers, both as MFMA B operands (k = d)
-  char *const kw_lds = lds + KW + wave * 32 * NP;
+  // back what it wrote), V rows in registers, both as MFMA B operands (k = d);
+  // a lane past the block's end takes the block's first row (its results are
+  // dropped)
+  char *const kw_lds = klds + wave * 32 * NP;
   bf16x8 vB[8];
   {
     const int64_t off = ((int64_t)(bi.y + (kvalid ? key : 0)) * a.Hkv + g) * kHeadDim + 8 * hh;
@@ -442,56 +484,63 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const uint32_t ibeg = a.bin_off[b], iend = a.bin_off[b + 1];
   const int ntiles = n_own + (int)((iend - ibeg + kKvRows - 1) / kKvRows);
 
-  // loader: thread (row lr, chunk lc of 8 elements)
-  const int lr = threadIdx.x & 31, lc = threadIdx.x >> 5;
-  const int lr_pos = perm_tr_pos(lr);
-  // the item of this thread's row in tile `it`, clamped to an existing entry
-  // (own tiles and rows past the bin read one whose value goes unused): always
-  // a load, so its register is never written conditionally while a load may
-  // still be filling it
+  // ---- row staging (wave 1, lanes 0..31: row n of a tile)
+  const bool stager = wave == 1 && lane < kKvRows;
   const uint32_t ilast = iend > 0 ? iend - 1 : 0u;
-  auto item_of = [&](int it) -> uint32_t {
-    const uint32_t j = ibeg + (uint32_t)max(it - n_own, 0) * kKvRows + lr;
+  // the item of row n of tile x, clamped to an existing entry (own tiles and
+  // rows past the bin read one whose value goes unused)
+  auto item_load = [&](int x) -> uint32_t {
+    const uint32_t j = ibeg + (uint32_t)max(x - n_own, 0) * kKvRows + n;
     return a.items[j < ilast ? j : ilast];
   };
-  bf16x8 sq, sdo;
-  float sl = 0.f, sd = 0.f;
-  bool sok = false;
-  auto fetch = [&](int it, uint32_t item) {
-    // the item is decoded on every path (slots are below 2^32), so its load
-    // has completed before this tile's loads are issued
-    const uint32_t row_b = item / (uint32_t)a.topk;
-    const uint32_t t_b = row_b / (uint32_t)a.Hp;
-    const int h_b = a.h0 + (int)(row_b - t_b * (uint32_t)a.Hp);
-    const bool own = it < n_own;
-    const int gi = own ? it / own_per_head : 0;
-    const int rl = k0 + (it - gi * own_per_head) * kKvRows + lr;
-    const uint32_t j = ibeg + (uint32_t)max(it - n_own, 0) * kKvRows + lr;
-    sok = own ? rl < bi.z : j < iend;
-    const int64_t t = own ? (int64_t)bi.y + (rl < bi.z ? rl : k0) : (int64_t)t_b;
-    const int h = own ? a.h0 + p * a.G + gi : h_b;
-    const int64_t off = (t * a.Hq + h) * kHeadDim + 8 * lc;
-    sq = *(const bf16x8 *)(a.q + off);
-    sdo = *(const bf16x8 *)(a.dout + off);
-    if (lc == 0) {
-      sl = a.lse[(int64_t)h * a.T + t];
-      sd = a.delta[(int64_t)h * a.T + t];
+  // (token, head) of row n of tile x; token -1 past the tile's end
+  auto row_of = [&](int x, uint32_t item) -> int2 {
+    if (x < n_own) {
+      const int gi = x / own_per_head;
+      const int rl = k0 + (x - gi * own_per_head) * kKvRows + n;
+      return rl < bi.z ? make_int2(bi.y + rl, a.h0 + p * a.G + gi) : make_int2(-1, 0);
     }
+    const uint32_t j = ibeg + (uint32_t)(x - n_own) * kKvRows + n;
+    if (x >= ntiles || j >= iend) return make_int2(-1, 0);
+    // the divisors pass through an empty asm so that the compiler does not
+    // keep their reciprocals in vector registers for the whole loop
+    uint32_t dk_ = (uint32_t)a.topk, dh_ = (uint32_t)a.Hp;
+    asm volatile("" : "+s"(dk_), "+s"(dh_));
+    const uint32_t th = item / dk_;
+    const uint32_t t = th / dh_;
+    return make_int2((int)t, a.h0 + (int)(th - t * dh_));
   };
-  auto stash = [&](int stage) {
-    char *S_ = lds + stage * STAGE;
-    if (!sok) {
+  const int npos = perm_tr_pos(n);  // where row n's lse and D go in a slot
+  auto lse_store = [&](int x, int2 rw, float l, float d) {
+    float *L = lse_d[x & 3];
+    L[npos] = rw.x >= 0 ? l * kLog2e : INFINITY;
+    L[kKvRows + npos] = rw.x >= 0 ? d : 0.f;
+  };
+  auto lse_off = [&](int2 rw) { return rw.x >= 0 ? (int64_t)rw.y * a.T + rw.x : (int64_t)0; };
+
+  // ---- direct loads of the Q and dO tiles: this wave's loads are slots
+  // 64 ld + lane for ld = ld0 .. ld0 + nld - 1
+  const int wv = wave == 0 ? 0 : wave - 1;  // 0..6 over the loading waves
+  const int nld = wave == 1 ? 0 : wv < 3 ? 3 : 2;
+  const int ld0 = wv < 3 ? 3 * wv : 9 + 2 * (wv - 3);
+  auto issue = [&](char *st, int x) {
+    const int2 *ri = rinfo[x & 1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { sq[e] = (__bf16)0.f; sdo[e] = (__bf16)0.f; }
-    }
-    *(bf16x8 *)(S_ + QN + lr * NP + lc * 16) = sq;
-    *(bf16x8 *)(S_ + DN + lr * NP + lc * 16) = sdo;
-    if (lc == 0) {
-      // row lr's values go where the lane that holds its scores reads them
-      float *L = (float *)(lds + LD + stage * 256);
-      const int pos = lr_pos;
-      L[pos] = sok ? sl * kLog2e : INFINITY;
-      L[32 + pos] = sok ? sd : 0.f;
+    for (int u = 0; u < 3; ++u) {
+      if (u >= nld) break;
+      const int ld = ld0 + u;
+      const int sx = 64 * ld + lane;
+      const bool is_do = sx >= kKvRows * SLOTS;
+      const int y = is_do ? sx - kKvRows * SLOTS : sx;
+      const int row = y / SLOTS;
+      const int chunk = min(y - row * SLOTS, 15);  // the padding slot repeats chunk 15
+      const int2 rw = ri[row];
+      const __bf16 *src = is_do ? a.dout : a.q;
+      const void *gp = rw.x >= 0
+                           ? (const void *)(src + ((int64_t)rw.x * a.Hq + rw.y) * kHeadDim +
+                                            8 * chunk)
+                           : (const void *)((const char *)a.zeros + 16 * chunk);
+      __builtin_amdgcn_global_load_lds((global_ptr_t)gp, (lds_ptr_t)(st + 1024 * ld), 16, 0, 0);
     }
   };
 
@@ -510,7 +559,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     return (bf16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
-  auto compute = [&](int it, int stage) {
+  auto compute = [&](const char *S_, int it) {
     if (kw >= bi.z) return;  // every key of this wave is past the block's end
     const bool own = it < n_own;
     int rt = 0;  // local position of the tile's first row (own tiles)
@@ -519,8 +568,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       rt = k0 + (it - gi * own_per_head) * kKvRows;
       if (rt + kKvRows - 1 < kw) return;  // every row precedes every key of this wave
     }
-    const char *S_ = lds + stage * STAGE;
-    const float *L = (const float *)(lds + LD + stage * 256);
+    const float *L = lse_d[it & 3];
     floatx16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
@@ -556,8 +604,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
         dv[dt] = mfma(tr_a(S_ + DN, dt, c), pb[c], dv[dt]);
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const float4 d0 = *(const float4 *)(L + 32 + 16 * c + 8 * hh);
-      const float4 d1 = *(const float4 *)(L + 32 + 16 * c + 8 * hh + 4);
+      const float4 d0 = *(const float4 *)(L + kKvRows + 16 * c + 8 * hh);
+      const float4 d1 = *(const float4 *)(L + kKvRows + 16 * c + 8 * hh + 4);
       const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) db[c][j] = (__bf16)(s[8 * c + j] * (dp[8 * c + j] - dd[j]));
@@ -570,21 +618,63 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       }
   };
 
-  if (ntiles > 0) {
-    fetch(0, item_of(0));
-    stash(0);
-    __syncthreads();
-    uint32_t nxt = item_of(1);
-    for (int it = 0; it < ntiles; ++it) {
-      const int stage = it & 1;
-      // every path issues the same loads (the last tile fetches itself again
-      // and drops it), so no wait inside the tile covers this tile's fetch
-      fetch(min(it + 1, ntiles - 1), nxt);
-      nxt = item_of(it + 2);
-      compute(it, stage);
-      if (it + 1 < ntiles) stash(stage ^ 1);
-      __syncthreads();
+  // body of tile it: cur is its stage, nx2 the stage of tile it + 2
+  auto body = [&](char *cur, char *nx2, int it) {
+    // assigned and read on the stager lanes only
+    uint32_t st_item;
+    int2 st_rw;
+    float st_l, st_d;
+    if (stager) {
+      st_item = item_load(it + 3);
+      st_rw = rinfo[it & 1][n];  // tile it + 2's rows
+      const int64_t o = lse_off(st_rw);
+      st_l = a.lse[o];
+      st_d = a.delta[o];
     }
+    issue(nx2, it + 2);
+    compute(cur, it);
+    // this wave's loads from before this body's Q/dO loads have landed:
+    // tile it + 1's (issued a body ago)
+    if (nld == 3) wait_vm<3>(); else if (nld == 2) wait_vm<2>(); else wait_vm<0>();
+    if (stager) {
+      // the staged values are first touched here, after the compute (the
+      // empty asm keeps the compiler from converting them right after
+      // their loads, which would wait for the loads there)
+      asm volatile("" : "+v"(st_l), "+v"(st_d), "+v"(st_item));
+      lse_store(it + 2, st_rw, st_l, st_d);
+      rinfo[(it + 3) & 1][n] = row_of(it + 3, st_item);
+    }
+    lds_barrier();
+  };
+
+  if (ntiles > 0) {
+    // prologue: rows of tiles 0 and 1 with their lse and D, their loads, then
+    // the rows of tile 2
+    if (stager) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int2 rw = row_of(x, item_load(x));
+        rinfo[x][n] = rw;
+        const int64_t o = lse_off(rw);
+        lse_store(x, rw, a.lse[o], a.delta[o]);
+      }
+    }
+    __syncthreads();
+    issue(stage0, 0);
+    issue(stage1, 1);
+    __syncthreads();  // every wave has read both row slots
+    if (stager) rinfo[0][n] = row_of(2, item_load(2));
+    wait_all_loads();
+    __syncthreads();
+    int it = 0;
+    for (; it + 3 <= ntiles; it += 3) {
+      body(stage0, stage2, it);
+      body(stage1, stage0, it + 1);
+      body(stage2, stage1, it + 2);
+    }
+    if (it < ntiles) body(stage0, stage2, it);
+    if (it + 1 < ntiles) body(stage1, stage0, it + 1);
+    wait_all_loads();  // the last bodies' prefetches (rows past the end)
   }
 
   if (!kvalid) return;
@@ -622,6 +712,7 @@ BwdArgs make_args(const Problem &pb, const Work &w, const BwdWork &bw, const Bwd
   a.dq_part = bw.dq_part;
   a.dk = (__bf16 *)io.dk;
   a.dv = (__bf16 *)io.dv;
+  a.zeros = bw.zeros;
   return a;
 }
 
@@ -669,6 +760,8 @@ hipError_t launch_bwd_dkdv(const Problem &pb, const Work &w, const BwdWork &bw, 
   const BwdArgs a = make_args(pb, w, bw, io, g0);
   const int64_t nch = (pb.B + kKvKeys - 1) / kKvKeys;
   const int64_t grid = (a.nbins + 7) / 8 * 8 * nch;
+  hipError_t e = launch_fill_u32((uint32_t *)bw.zeros, 0u, kBwdZeroBytes / 4, s);
+  if (e != hipSuccess) return e;
   bwd_dkdv_kernel<<<dim3((unsigned)grid), 512, 0, s>>>(a);
   return hipGetLastError();
 }
