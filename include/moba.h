@@ -335,7 +335,8 @@ moba_status_t moba_decode(const void *q, const void *k_cache, const void *v_cach
  * heads; see moba_plan): the forward plan's regions, except that the vt
  * region holds K^T per block, part_o_offset is the fp32 partial dq of each
  * (row, head, slot) ([T][Hp][topk][d]) and part_lse_offset is D ([Hq][T]
- * float32). */
+ * float32); the last 256 bytes are a zero area that moba_attn_bwd_dkdv
+ * clears and reads. */
 moba_status_t moba_bwd_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
                             int32_t kv_heads_per_pass, moba_layout_t *layout);
 /* Bytes of workspace moba_bwd needs for the given pass size; 0 if invalid. */
