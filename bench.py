@@ -383,7 +383,6 @@ def bwd_bench(args):
         for g0 in passes:
             tm.run("gate", lambda: run_gate(g0))
             tm.run("dispatch", lambda: moba.moba_dispatch(shape, B, k, lay, ws, g0))
-            tm.run("ktrans", lambda: moba.moba_ktrans(kk, shape, B, k, lay, ws, g0))
             tm.run("dq_diag", lambda: moba.moba_attn_bwd_dq(q, kk, v, dout, lse, shape, B, k,
                                                              lay, ws, g0, which=1))
             tm.run("dq_hist", lambda: moba.moba_attn_bwd_dq(q, kk, v, dout, lse, shape, B, k,
@@ -451,7 +450,6 @@ def bwd_bench(args):
     es = 2
     n_hist = float(sum(hist_rows))
     hbm_bytes = {"delta": 2 * T * Hq * d * es + T * Hq * 4,
-                 "ktrans": 2 * T * Hkv * d * es,
                  "dq_sum": (n_hist + T * Hq) * d * 4 + T * Hq * k * 4 + T * Hq * d * es}
     hbm = {n: {"ms": round(stages[n], 4), "GB/s": round(b / (stages[n] * 1e-3) / 1e9, 1),
                "frac": round(b / (stages[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}

@@ -733,8 +733,6 @@ moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *
     else
       MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
     MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
-    MOBA_HIP(launch_vtrans(k, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
-             "ktrans");
     MOBA_HIP(launch_bwd_dq(pb, w, bw, io, g0, 3, s), "bwd_dq");
     MOBA_HIP(launch_bwd_dq_sum(pb, w, bw, io, g0, s), "bwd_dq_sum");
     MOBA_HIP(launch_bwd_dkdv(pb, w, bw, io, g0, s), "bwd_dkdv");
@@ -755,21 +753,6 @@ moba_status_t moba_bwd_delta(const void *out, const void *dout, const moba_shape
   Work w = carve(pb, L, ws);
   const BwdWork bw = carve_bwd(pb, L, ws, &w);
   MOBA_HIP(launch_bwd_delta(pb, out, dout, bw.delta, s), "bwd_delta");
-  return MOBA_SUCCESS;
-}
-
-moba_status_t moba_ktrans(const void *k, const moba_shape_t *sh, int32_t B, int32_t topk,
-                          const moba_layout_t *L, void *ws, int32_t g0, hipStream_t s) {
-  moba_layout_t f;
-  moba_status_t st = check_stage(sh, B, topk, L, ws, &f, PLAN_BWD);
-  if (st != MOBA_SUCCESS) return st;
-  if (sh->total_tokens == 0) return MOBA_SUCCESS;
-  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
-  if (!k) return fail(MOBA_ERROR_INVALID_VALUE, "k is NULL");
-  Problem pb = make_problem(sh, B, topk, 0.f, L);
-  Work w = carve(pb, L, ws);
-  MOBA_HIP(launch_vtrans(k, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
-           "ktrans");
   return MOBA_SUCCESS;
 }
 

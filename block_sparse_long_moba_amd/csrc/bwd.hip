@@ -15,8 +15,8 @@
 //   256 query rows of one head per workgroup, causal; earlier blocks: a tile of
 //   up to 256 gathered rows of one bin), keys streamed through LDS in tiles of
 //   64. Per tile S^T = K Q^T, dP^T = V dO^T, dS, and dQ^T += K^T dS^T (K^T
-//   comes pre-transposed per block, like V^T in the forward pass). Each
-//   (row, head, slot) gets an fp32 partial dQ; a sum over the slots follows.
+//   read from the K tile through the LDS transpose read). Each (row, head,
+//   slot) gets an fp32 partial dQ; a sum over the slots follows.
 // - keys resident (bwd_dkdv_kernel): one workgroup per (kv head, block, chunk
 //   of 256 keys), 8 waves of 32 keys with V in registers and K in LDS as
 //   MFMA B operands. The block's own rows (for each query head of the kv head,
@@ -51,7 +51,7 @@ constexpr int kKvRows = 32;               // rows per dK/dV tile
 enum { BWD_HIST = 0, BWD_DIAG = 1 };
 
 struct BwdArgs {
-  const __bf16 *q, *k, *v, *kt, *dout;
+  const __bf16 *q, *k, *v, *dout;
   const float *lse, *delta;  // [Hq][T]
   int64_t T;
   int Hq, Hkv, G, B, topk;
@@ -160,14 +160,28 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16 *__restrict
 
 // ---- dQ: rows resident, keys streamed.
 //
-// LDS: two stages of {K tile, V tile, K^T tile}, 16 KiB each. K and V tiles
-// are 64 rows x 16 chunks of 16 B, chunk c of row r at position c ^ (r & 15);
-// the K^T tile is 128 rows (d) x 8 chunks (of 8 keys), chunk c of row r at
-// c ^ ((r >> 1) & 7). Every wave fills 2 KiB of each with direct loads.
+// LDS: three stages of {K tile, V tile}, 16 KiB each, as three separate
+// arrays: 64 rows x 16 chunks of 16 B, chunk c of row r at position
+// c ^ swz(r) with swz(r) = 4 (r % 4) + (r / 4) % 4. Every wave fills 2 KiB of
+// each with direct loads, two tiles ahead. K^T, the A operand of
+// dQ^T += K^T dS^T, comes from the K tile through ds_read_b64_tr_b16: for
+// 16-lane group G and read h, lane s addresses key 16 c + 8 (s / 32) + 4 h +
+// (s % 16) / 4 (of a 32-key half), columns 32 dt + 16 G%2 + 4 (s % 4) .. +3,
+// and lane l receives the keys of its K slice 8 hh + 4 h .. +3 at column
+// 32 dt + l % 32. The four keys of a read differ in swz by 4 each and the
+// four chunks a half-wave reads in swz's low bits, so the 32 lanes hit 64
+// different banks. A body ends when each wave's loads of the next tile have
+// landed, with an LDS-only barrier that leaves the tile after in flight; the
+// loop is unrolled by the stages so that the compiler sees that a body's
+// direct loads and its LDS reads never overlap.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
-  constexpr int TILE = 16384, STAGE = 3 * TILE, LPW = 2;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  constexpr int TILE = 16384, STAGE = 2 * TILE, LPW = 2;
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
@@ -238,44 +252,45 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
   const float Dr = a.delta[(int64_t)hq * a.T + t];
   const float c2 = a.c2;
 
-  // direct-load sources (byte offsets from the tile base): K and V regions
-  // are 4 rows, K^T regions 8 rows
+  // direct-load sources (byte offsets from the tile base): regions of 4 rows
   const int64_t kstride = (int64_t)a.Hkv * kHeadDim;
-  uint32_t kso[LPW], tso[LPW];
+  uint32_t kso[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int region = wave * LPW + j;
-    const int krow = region * 4 + (lane >> 4);
-    kso[j] = (uint32_t)krow * (uint32_t)kstride * 2u + (uint32_t)(((lane & 15) ^ (krow & 15)) * 16);
-    const int trow = region * 8 + (lane >> 3);
-    tso[j] = (uint32_t)trow * (uint32_t)a.B * 2u + (uint32_t)(((lane & 7) ^ ((trow >> 1) & 7)) * 16);
+    const int krow = (wave * LPW + j) * 4 + (lane >> 4);
+    kso[j] = (uint32_t)krow * (uint32_t)kstride * 2u + (uint32_t)(((lane & 15) ^ swz(krow)) * 16);
   }
-  char *const lds_w = lds + wave * LPW * 1024;
+  const int lw = wave * LPW * 1024;  // this wave's share of a tile
   const __bf16 *kt0 = a.k + kbeg * kstride + (int64_t)g * kHeadDim;
   const __bf16 *vt0 = a.v + kbeg * kstride + (int64_t)g * kHeadDim;
-  const __bf16 *tt0 = a.kt + ((int64_t)p * a.NBb + gb) * kHeadDim * a.B;
   const int64_t span = (a.T - kbeg) * kstride * 2;  // bytes to the end of the tensor (upper bound)
   const __amdgpu_buffer_rsrc_t krs = uniform_rsrc(kt0, span);
   const __amdgpu_buffer_rsrc_t vrs = uniform_rsrc(vt0, span);
-  const __amdgpu_buffer_rsrc_t trs = uniform_rsrc(tt0, (int64_t)kHeadDim * a.B * 2);
-  auto issue = [&](int kt, int stage) {
+  auto issue = [&](char *st, int kt) {
     const uint32_t soff = (uint32_t)kt * kKeyTile * (uint32_t)kstride * 2u;
-    const uint32_t toff = (uint32_t)kt * kKeyTile * 2u;
-    char *base = lds_w + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(base + j * 1024), 16, kso[j], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(base + TILE + j * 1024), 16, kso[j], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (lds_ptr_t)(base + 2 * TILE + j * 1024), 16, tso[j], toff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(st + lw + j * 1024), 16, kso[j], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(st + TILE + lw + j * 1024), 16, kso[j], soff, 0, 0);
     }
   };
-  // LDS read offsets of this lane's A operands
+  // LDS read offsets of this lane's A operands: K and V rows (perm32) for S
+  // and dP; the transpose reads of K^T per (dt, h)
   const int pr = perm32(n);
-  uint32_t krd[8], trd[4];
+  uint32_t krd[8], trk[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) krd[kk] = pr * 256 + (((2 * kk + hh) ^ (pr & 15)) * 16);
+  for (int kk = 0; kk < 8; ++kk) krd[kk] = pr * 256 + (((2 * kk + hh) ^ swz(pr)) * 16);
+  {
+    const int jq = (lane & 15) >> 2, gq = (lane >> 4) & 1;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) trd[c] = n * 128 + (((2 * c + hh) ^ ((n >> 1) & 7)) * 16);
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 8 * hh + 4 * h + jq;  // + 32 st + 16 c, which leave swz unchanged
+        const int chunk = 4 * dt + 2 * gq + ((lane & 3) >> 1);
+        trk[2 * dt + h] = key * 256 + ((chunk ^ swz(key)) * 16) + 8 * (lane & 1);
+      }
+  }
 
   floatx16 dq[4];
 #pragma unroll
@@ -283,10 +298,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[dt][i] = 0.f;
 
-  auto compute = [&](int kt, int stage) {
-    const char *Ks = lds + stage * STAGE;
+  auto compute = [&](const char *Ks, int kt) {
     const char *Vs = Ks + TILE;
-    const char *Ts = Ks + 2 * TILE;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       floatx16 sc, dp;
@@ -308,30 +321,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const BwdArgs a) {
           if (MODE == BWD_DIAG && kt * kKeyTile + 32 * st + 16 * c + 8 * hh + j > qpos) pv = 0.f;
           b[j] = (__bf16)(pv * (dp[i] - Dr));
         }
+        const char *kb = Ks + (32 * st + 16 * c) * 256;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          dq[dt] = mfma(*(const bf16x8 *)(Ts + dt * 4096 + trd[2 * st + c]), b, dq[dt]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x4 lo = tr_read(kb + trk[2 * dt]);
+          const bf16x4 hi = tr_read(kb + trk[2 * dt + 1]);
+          dq[dt] = mfma((bf16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), b, dq[dt]);
+        }
       }
       // keep the two halves apart: interleaving them costs registers
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // body of key tile kt (stage cur), loading tile kt + 2 into stage nx2
+  auto body = [&](const char *cur, char *nx2, int kt) {
+    // the last two bodies load the last tile again into a stage nobody reads,
+    // so that every body issues the same loads
+    issue(nx2, min(kt + 2, nkt - 1));
+    compute(cur, kt);
+    // this wave's loads of tile kt + 1 (issued a body ago) have landed
+    wait_vm<2 * LPW>();
+    lds_barrier();
+  };
 
-  issue(0, 0);
+  issue(stage0, 0);
+  issue(stage1, min(1, nkt - 1));
   wait_all_loads();
   __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    if (kt + 1 < nkt) issue(kt + 1, 1);
-    compute(kt, 0);
-    wait_all_loads();
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      if (kt + 2 < nkt) issue(kt + 2, 0);
-      compute(kt + 1, 1);
-      wait_all_loads();
-      __syncthreads();
-    }
+  int kt = 0;
+  for (; kt + 3 <= nkt; kt += 3) {
+    body(stage0, stage2, kt);
+    body(stage1, stage0, kt + 1);
+    body(stage2, stage1, kt + 2);
   }
+  if (kt < nkt) body(stage0, stage2, kt);
+  if (kt + 1 < nkt) body(stage1, stage0, kt + 1);
+  wait_all_loads();  // the last bodies' repeated loads
 
   if (r >= nrows) return;
   float *dst = a.dq_part + slot * kHeadDim + 4 * hh;
@@ -696,7 +721,6 @@ BwdArgs make_args(const Problem &pb, const Work &w, const BwdWork &bw, const Bwd
   a.q = (const __bf16 *)io.q;
   a.k = (const __bf16 *)io.k;
   a.v = (const __bf16 *)io.v;
-  a.kt = (const __bf16 *)w.vt;
   a.dout = (const __bf16 *)io.dout;
   a.lse = io.lse;
   a.delta = bw.delta;

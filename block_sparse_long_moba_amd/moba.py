@@ -24,7 +24,7 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_works
            "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
            "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
            "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd", "moba_bwd_delta",
-           "moba_ktrans", "moba_attn_bwd_dq", "moba_attn_bwd_dq_sum", "moba_attn_bwd_dkdv",
+           "moba_attn_bwd_dq", "moba_attn_bwd_dq_sum", "moba_attn_bwd_dkdv",
            "moba_dense_causal_workspace_size", "moba_dense_causal_fwd"]
 
 GATE_MEAN, GATE_WINDOW, GATE_POOLED = 0, 1, 2
@@ -113,7 +113,6 @@ def lib():
             "moba_bwd": ([P, P, P, P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, P,
                           Z, P], I32),
             "moba_bwd_delta": ([P, P, S, I32, I32, LP, P, P], I32),
-            "moba_ktrans": ([P, S, I32, I32, LP, P, I32, P], I32),
             "moba_attn_bwd_dq": ([P, P, P, P, P, S, I32, I32, F, LP, P, I32, I32, P], I32),
             "moba_attn_bwd_dq_sum": ([S, I32, I32, LP, P, I32, P, P], I32),
             "moba_attn_bwd_dkdv": ([P, P, P, P, P, S, I32, I32, F, LP, P, I32, P, P, P], I32),
@@ -336,11 +335,6 @@ def moba_bwd(q, k, v, out, lse, dout, cu_seqlens, block_size, topk, workspace, g
 def moba_bwd_delta(out, dout, shape, block_size, topk, layout, workspace, stream=None):
     _check(lib().moba_bwd_delta(_ptr(out), _ptr(dout), ctypes.byref(shape), block_size, topk,
                                 ctypes.byref(layout), _ptr(workspace), _stream(stream)))
-
-
-def moba_ktrans(k, shape, block_size, topk, layout, workspace, kv_head_begin=0, stream=None):
-    _check(lib().moba_ktrans(_ptr(k), ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
-                             _ptr(workspace), kv_head_begin, _stream(stream)))
 
 
 def moba_attn_bwd_dq(q, k, v, dout, lse, shape, block_size, topk, layout, workspace,

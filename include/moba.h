@@ -333,7 +333,7 @@ moba_status_t moba_decode(const void *q, const void *k_cache, const void *v_cach
 
 /* Host only. Workspace plan of the backward pass for a pass size (0 = all kv
  * heads; see moba_plan): the forward plan's regions, except that the vt
- * region holds K^T per block, part_o_offset is the fp32 partial dq of each
+ * region is unused, part_o_offset is the fp32 partial dq of each
  * (row, head, slot) ([T][Hp][topk][d]) and part_lse_offset is D ([Hq][T]
  * float32); the last 256 bytes are a zero area that moba_attn_bwd_dkdv
  * clears and reads. */
@@ -353,20 +353,16 @@ moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *
 /* Stages of moba_bwd, on a workspace laid out by moba_bwd_plan (moba_seqtable,
  * moba_meanpool / moba_minmaxpool, the gate stages and moba_dispatch accept
  * that plan too and run first, as in the forward pass). Per pass
- * kv_head_begin: gate, dispatch, moba_ktrans, moba_attn_bwd_dq,
- * moba_attn_bwd_dq_sum, moba_attn_bwd_dkdv; moba_bwd_delta once before. */
+ * kv_head_begin: gate, dispatch, moba_attn_bwd_dq, moba_attn_bwd_dq_sum,
+ * moba_attn_bwd_dkdv; moba_bwd_delta once before. */
 
 /* D[h][t] = <dout[t][h], out[t][h]> (float32) into the part_lse region. */
 moba_status_t moba_bwd_delta(const void *out, const void *dout, const moba_shape_t *shape,
                              int32_t block_size, int32_t topk, const moba_layout_t *layout,
                              void *workspace, hipStream_t stream);
-/* K^T of every block of the pass's kv heads into the vt region. */
-moba_status_t moba_ktrans(const void *k, const moba_shape_t *shape, int32_t block_size,
-                          int32_t topk, const moba_layout_t *layout, void *workspace,
-                          int32_t kv_head_begin, hipStream_t stream);
 /* Partial dq of every (row, head, slot) of the pass: which = 1 the own block
  * (causal), 2 the earlier blocks of the bins, 3 both. Needs the gate,
- * dispatch, moba_ktrans and moba_bwd_delta. */
+ * dispatch and moba_bwd_delta. */
 moba_status_t moba_attn_bwd_dq(const void *q, const void *k, const void *v, const void *dout,
                                const float *lse, const moba_shape_t *shape, int32_t block_size,
                                int32_t topk, float softmax_scale, const moba_layout_t *layout,

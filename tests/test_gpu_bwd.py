@@ -214,7 +214,6 @@ def test_bwd_stages_match_one_call():
     for g0 in range(0, 2, lay.kv_heads_per_pass):
         moba.moba_gate(q, sh, B, k, lay, ws, g0)
         moba.moba_dispatch(sh, B, k, lay, ws, g0)
-        moba.moba_ktrans(kk, sh, B, k, lay, ws, g0)
         moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=1)
         moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=2)
         moba.moba_attn_bwd_dq_sum(sh, B, k, lay, ws, dq, g0)
@@ -283,7 +282,6 @@ def test_bwd_full_workload_sampled_rows_and_identities(name):
         idx = workspace_view(ws, lay.idx_offset, T * Hp * k, torch.int32).view(T, Hp, k)
         gsel[:, h0:h0 + Hp] = idx[rows_t].cpu().numpy()
         moba.moba_dispatch(sh, B, k, lay, ws, g0)
-        moba.moba_ktrans(kk, sh, B, k, lay, ws, g0)
         moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=1)
         moba.moba_attn_bwd_dq(q, kk, v, dout, lse, sh, B, k, lay, ws, g0, which=2)
         moba.moba_attn_bwd_dq_sum(sh, B, k, lay, ws, dq, g0)
