@@ -123,6 +123,12 @@ def main():
                     help="time the backward pass (dq, dk, dv; with --gate) instead of the forward")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows the CPU oracle times (0 = sized for about 15 s)")
+    ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
+                    help="write a 512 MiB buffer between timed forward steps, outside the "
+                    "steps' events, so that no step finds its inputs in L2 / MALL (auto: on "
+                    "when q, k and v together are below 4 GiB)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy and GEMM ceilings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: there is no multi-GPU path (the forward pass would "
@@ -204,16 +210,25 @@ def main():
     for _ in range(args.warmup):
         step(Timer())
     torch.cuda.synchronize()
-    log("timing %d step(s)" % args.steps)
+    es = 2 if w.dtype == "bf16" else 4
+    qkv_bytes = T * (Hq + 2 * Hkv) * HEAD_DIM * es
+    flush = args.flush == "on" or (args.flush == "auto" and qkv_bytes < (4 << 30))
+    fbuf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if flush else None
+    log("timing %d step(s)%s" % (args.steps, " with a cache flush between steps" if flush else ""))
     tm = Timer()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spans = []
     torch.cuda.synchronize()
-    start.record()
     for i in range(args.steps):
+        if fbuf is not None:
+            fbuf.fill_(i & 255)  # between the steps' events: not timed
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         step(tm)
-    end.record()
+        b.record()
+        spans.append((a, b))
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = sum(a.elapsed_time(b) for a, b in spans) / args.steps
+    del fbuf
     stages = {n: (tot / args.steps, cnt) for n, (tot, cnt) in tm.totals().items()}
     log("step %.2f ms; stages %s" % (ms, {n: round(v[0], 3) for n, v in stages.items()}))
 
@@ -223,7 +238,6 @@ def main():
         own = sum(int(((np.arange(L) % B) + 1).sum()) for L in w.lengths)
         eff = 4.0 * HEAD_DIM * (B * float(sum(hist_rows)) + Hq * own)
     value = eff / (ms * 1e-3) / 1e12
-    es = 2 if w.dtype == "bf16" else 4
     # dominant kernel: earlier-block attention, MFMA bound
     hist_ms_total, hist_launches = tm.totals()["attn_hist"]
     hist_flop_per_step = 4.0 * HEAD_DIM * B * sum(hist_rows)
@@ -291,6 +305,20 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, w, args.cpu_rows, args.gate, k, args.n_sink, args.extra_max,
                            args.extra_min)
+        # the whole pass on the CPU, extrapolated from the sample by effective FLOP
+        cpu["extrapolated_full_pass_s"] = round(eff / (cpu["value"] * 1e12), 1)
+
+    # the least any forward pass must move: q, k, v read and out, lse written
+    io_bytes = qkv_bytes + T * Hq * HEAD_DIM * es + T * Hq * 4
+    minimal_io = {"bytes": io_bytes,
+                  "ms_at_hbm_peak": round(io_bytes / (PEAK_HBM_GBS * 1e9) * 1e3, 3)}
+
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measured_ceilings(torch)
+        ceilings["attn_hist_frac_of_gemm"] = round(achieved / ceilings["bf16_gemm_TFLOP/s"], 4)
+        ceilings["hbm_stages_frac_of_copy"] = {
+            n: round(x["GB/s"] / ceilings["hbm_copy_GB/s"], 4) for n, x in hbm.items()}
 
     res = {
         "metric": "MoBA fwd ms + effective TFLOP/s at 128K/1M tokens (8B heads), % MFMA peak",
@@ -313,6 +341,8 @@ def main():
         "hbm": hbm,
         "dense_causal": dense,
         "roofline": roofline,
+        "minimal_io": minimal_io,
+        "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -563,6 +593,38 @@ def decode_bench(args):
 
 def _threads():
     return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def measured_ceilings(torch):
+    """Practical ceilings on this GPU, measured with torch (a measuring
+    instrument here, not part of the path): HBM by a 4 GiB float32 copy
+    (negation: every byte read once and written once), bf16 matrix-core
+    throughput by an 8192^3 GEMM (hipBLASLt). Best of a few runs each."""
+    def best_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return min(out)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    copy_ms = best_ms(lambda: torch.neg(src, out=dst), 3)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    gemm_ms = best_ms(lambda: torch.mm(a, b), 5)
+    del a, b
+    return {"hbm_copy_GB/s": round(2 * 4 * n / (copy_ms * 1e-3) / 1e9, 1),
+            "bf16_gemm_TFLOP/s": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "how": "4 GiB float32 negation (torch); 8192^3 bf16 torch.mm (hipBLASLt)"}
 
 
 def cpu_baseline(inp, w, n_rows, gate="mean", k=None, n_sink=1, extra_max=1, extra_min=1):
