@@ -1,4 +1,5 @@
-// C ABI of the MoBA forward pass: argument checks, workspace plan, and the
+// C ABI of MoBA (forward pass and its stages, gate variants, backward pass,
+// decode, dense causal baseline): argument checks, workspace plans, and the
 // order in which the stages are enqueued. Declared in include/moba.h.
 #include <math.h>
 #include <stdarg.h>

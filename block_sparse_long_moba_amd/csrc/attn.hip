@@ -6,8 +6,9 @@
 // log-sum-exp; "Causality Enforcement" mechanism 2 for the own block. The same
 // tile engine runs dense causal attention ("Standard Attention Baseline").
 //
-// Workgroup: 4 waves, 128 query rows (32 per wave), one kv head. Keys stream
-// through LDS in tiles of 64 (double buffered). Each wave computes the
+// Workgroup: waves of 32 query rows of one kv head (bf16: 8 waves, 256 rows;
+// fp32: 4 waves, 128 rows). Keys stream through LDS in tiles of 64 (double
+// buffered). Each wave computes the
 // transposed score tile S^T = K Q^T (keys on the MFMA's M side, queries on N)
 // so a lane holds 16 scores of a single query: row max and row sum need no
 // cross-lane work except one exchange with the lane 32 away. The K rows are

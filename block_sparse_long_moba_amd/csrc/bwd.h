@@ -8,7 +8,7 @@ namespace moba {
 constexpr size_t kBwdZeroBytes = 256;  // zero area at the end of a backward workspace
 
 // Extra buffers of the backward pass, next to the forward-pass Work of the
-// same plan (the vt region holds K^T per block instead of V^T).
+// same plan (its vt region is unused).
 struct BwdWork {
   float *dq_part;  // [T*Hp*k][d] fp32 partial dQ of each (row, head, slot), scale applied
   float *delta;    // [Hq][T] D = <dO, O> of each (row, head)

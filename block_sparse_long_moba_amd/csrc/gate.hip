@@ -7,12 +7,15 @@
 // are never candidates). Review page (paperhub.cn), authors' rebuttal W1:
 // each query head selects on its own.
 //
-// One workgroup = 64 consecutive rows of one block x 4 query heads (one wave
-// per head, one lane per row). Every row of the workgroup has the same own
-// block c, so the candidate list 0..c-1 is uniform across the workgroup and
-// the pooled-key rows are wave-uniform reads. Scores are fp32 dot products
-// (q upcast exactly from bf16, kbar fp32), so a selection can differ from an
-// exact one only where the k-th and (k+1)-th scores agree to ~1e-6.
+// Two implementations of the mean gate: the matrix-core gate below (bf16
+// inputs, GQA groups of a multiple of 4 query heads) and this vector gate
+// (every other shape). Vector gate: one workgroup = 64 consecutive rows of
+// one block x 4 query heads (one wave per head, one lane per row). Every row
+// of the workgroup has the same own block c, so the candidate list 0..c-1 is
+// uniform across the workgroup and the pooled-key rows are wave-uniform
+// reads. Scores are fp32 dot products (q upcast exactly from bf16, kbar
+// fp32), so a selection can differ from an exact one only where the k-th and
+// (k+1)-th scores agree to ~1e-6.
 #include <limits.h>
 
 #include "moba_internal.h"
