@@ -349,9 +349,9 @@ def main():
 
 
 def bwd_bench(args):
-    """Backward pass of the workload (mean gate): D = <dO, O>, then per pass
-    the gate and dispatch again, K^T per block, partial dq (own block, earlier
-    blocks), their sum, and dk/dv; each stage bracketed by HIP events. The
+    """Backward pass of the workload (gate as --gate): D = <dO, O>, then per
+    pass the gate and dispatch again, partial dq (own block, earlier blocks),
+    their sum, and dk/dv; each stage bracketed by HIP events. The
     forward pass that produced out and lse runs once, untimed. Effective
     FLOP = 10*d per attended (row, head, key): the five products of the
     attention gradient (S recomputed, dP, dV, dK, dQ)."""
