@@ -15,6 +15,7 @@ traffic when that measurement belongs to the current kernel sources;
 "cpu_baseline" times the CPU oracle on a bounded sample of the same workload.
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -317,6 +318,8 @@ def main():
     if not args.no_ceilings:
         ceilings = measured_ceilings(torch)
         ceilings["attn_hist_frac_of_gemm"] = round(achieved / ceilings["bf16_gemm_TFLOP/s"], 4)
+        ceilings["attn_hist_frac_of_mfma_loop"] = round(
+            achieved / ceilings["bf16_mfma_loop_TFLOP/s"], 4)
         ceilings["hbm_stages_frac_of_copy"] = {
             n: round(x["GB/s"] / ceilings["hbm_copy_GB/s"], 4) for n, x in hbm.items()}
 
@@ -622,9 +625,27 @@ def measured_ceilings(torch):
     b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
     gemm_ms = best_ms(lambda: torch.mm(a, b), 5)
     del a, b
+    # pure MFMA loop (libmoba_probe.so): 8 waves per CU, 4 independent chains
+    probe = ctypes.CDLL(os.path.join(ROOT, "block_sparse_long_moba_amd", "libmoba_probe.so"))
+    probe.moba_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 100000
+    pout = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run_probe():
+        rc = probe.moba_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(pout.data_ptr()),
+                                        ctypes.c_void_p(stream))
+        assert rc == 0, "MFMA probe launch failed (%d)" % rc
+    mfma_ms = best_ms(run_probe, 3)
+    mfma_flop = blocks * 4.0 * iters * 4 * 32768
     return {"hbm_copy_GB/s": round(2 * 4 * n / (copy_ms * 1e-3) / 1e9, 1),
             "bf16_gemm_TFLOP/s": round(2.0 * m ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
-            "how": "4 GiB float32 negation (torch); 8192^3 bf16 torch.mm (hipBLASLt)"}
+            "bf16_mfma_loop_TFLOP/s": round(mfma_flop / (mfma_ms * 1e-3) / 1e12, 1),
+            "how": "4 GiB float32 negation (torch); 8192^3 bf16 torch.mm (hipBLASLt); "
+                   "a loop of independent 32x32x16 bf16 MFMAs, 8 waves per CU "
+                   "(libmoba_probe.so)"}
 
 
 def cpu_baseline(inp, w, n_rows, gate="mean", k=None, n_sink=1, extra_max=1, extra_min=1):

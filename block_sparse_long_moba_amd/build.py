@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoba.so")
+PROBE_LIB = os.path.join(HERE, "libmoba_probe.so")  # the benchmark's MFMA-rate probe
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "prep.hip", "gate.hip", "dispatch.hip", "attn.hip", "decode.hip", "bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,11 +42,12 @@ def build(verbose: bool = False) -> str:
             print(out, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(min(len(SOURCES) + 1, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + ["probe.hip"]))
+    for lib, parts in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + parts)
+        os.replace(tmp, lib)
     return LIB
 
 
