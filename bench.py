@@ -44,8 +44,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "dd1dbb1a97ebd7f47d3a11ab1b9a4e9e24b2bd40a7b05c6b49558a98ec694f54",
-    "fetch_kib": 18382821.3, "write_kib": 25358787.8,
+    "sha256": "4efdd82a6acf564a74f649058ada19e27b66fa5b18ad2e6f98bcbc6346ad872f",
+    "fetch_kib": 20448034.6, "write_kib": 25360275.6,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 
