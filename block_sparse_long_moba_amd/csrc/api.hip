@@ -165,8 +165,9 @@ moba_status_t bwd_plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_
   off = align_up(off + sizeof(float) * (size_t)slots * kHeadDim);
   L->part_lse_offset = off;
   off = align_up(off + sizeof(float) * (size_t)T * sh->num_q_heads);
-  off = align_up(off + kBwdZeroBytes);
-  L->total_bytes = off;
+  const int64_t nbins = (int64_t)L->kv_heads_per_pass * L->num_blocks_bound;
+  const DkdvSplit sp = dkdv_split(T, L->q_heads_per_pass, k, B);
+  L->total_bytes = bwd_extra(off, nbins, sp).end;
   return MOBA_SUCCESS;
 }
 
@@ -259,8 +260,11 @@ moba_status_t check_pass(const moba_shape_t *sh, const moba_layout_t *L, int32_t
 // (lists at the start of the partial-dq region, at most (topk + 2) ints per
 // (row, head); the per-slot lse in its last T*Hp*topk floats) kept away from D.
 BwdWork carve_bwd(const Problem &pb, const moba_layout_t *L, void *ws, Work *w) {
-  BwdWork bw{(float *)((char *)ws + L->part_o_offset), (float *)((char *)ws + L->part_lse_offset),
-             (char *)ws + L->total_bytes - align_up(kBwdZeroBytes)};
+  const size_t base = align_up(L->part_lse_offset + sizeof(float) * (size_t)pb.T * pb.Hq);
+  const BwdExtra x = bwd_extra(base, (int64_t)pb.P * pb.NBb, dkdv_split(pb.T, pb.Hp, pb.k, pb.B));
+  char *b = (char *)ws;
+  BwdWork bw{(float *)(b + L->part_o_offset), (float *)(b + L->part_lse_offset), b + x.zeros,
+             (uint32_t *)(b + x.ext_off), (uint32_t *)(b + x.slot_off), (float *)(b + x.part)};
   const int64_t slots = pb.T * pb.Hp * pb.k;
   w->part_o = bw.dq_part;
   w->part_lse = bw.dq_part + slots * (kHeadDim - 1);

@@ -31,6 +31,7 @@
 // 16(i/8) + 8hh + i%8: two runs of 8 consecutive rows, exactly the 8-wide K
 // slices the next product takes from the same lane.
 #include <math.h>
+#include <stdlib.h>
 
 #include "bwd.h"
 
@@ -45,7 +46,6 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr int kDqRows = kRowsBf16;        // query rows per dQ workgroup (8 waves x 32)
-constexpr int kKvKeys = 256;              // keys per dK/dV workgroup (8 waves x 32)
 constexpr int kKvRows = 32;               // rows per dK/dV tile
 
 enum { BWD_HIST = 0, BWD_DIAG = 1 };
@@ -64,6 +64,10 @@ struct BwdArgs {
   float *dq_part;
   __bf16 *dk, *dv;
   const void *zeros;  // 256 zero bytes: the rows past the end of a dK/dV tile
+  // bin segments of the dK/dV stage
+  const uint32_t *ext_off, *slot_off;
+  float *part;
+  int64_t seg_rows, extra_wg, part_half;  // part_half: floats of the dK half of part
 };
 
 __device__ __forceinline__ floatx16 mfma(const bf16x8 &a, const bf16x8 &b, const floatx16 &c) {
@@ -465,12 +469,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int nch = (a.B + kKvKeys - 1) / kKvKeys;
-  // workgroup x: bin 8 * ((x / 8) / nch) + x % 8, chunk (x / 8) % nch; every
-  // XCD takes every 8th bin, the chunks of one bin back to back
-  const int64_t xg = blockIdx.x >> 3;
-  const int64_t b = (xg / nch) * 8 + (blockIdx.x & 7);
-  const int kc = (int)(xg % nch);
-  if (b >= a.nbins) return;
+  // The first extra_wg workgroups take the segments beyond the first of the
+  // split bins (extra segment e = 8 * ((x / 8) / nch) + x % 8, chunk
+  // (x / 8) % nch), the others the first segment of every bin (bin
+  // 8 * ((x' / 8) / nch) + x' % 8 with x' = x - extra_wg): every XCD takes
+  // every 8th bin or segment, the chunks of one back to back.
+  int64_t b;
+  int kc, seg;
+  if ((int64_t)blockIdx.x < a.extra_wg) {
+    const int64_t xg = blockIdx.x >> 3;
+    const int64_t se = (xg / nch) * 8 + (blockIdx.x & 7);
+    kc = (int)(xg % nch);
+    if (se >= (int64_t)a.ext_off[a.nbins]) return;
+    int64_t lo = 0, hi = a.nbins - 1;  // the bin whose extra segments include se
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if ((int64_t)a.ext_off[mid] <= se) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    seg = (int)(se - a.ext_off[b]) + 1;
+  } else {
+    const int64_t x = blockIdx.x - a.extra_wg;
+    const int64_t xg = x >> 3;
+    b = (xg / nch) * 8 + (x & 7);
+    kc = (int)(xg % nch);
+    seg = 0;
+    if (b >= a.nbins) return;
+  }
+  const int nseg = (int)(a.ext_off[b + 1] - a.ext_off[b]) + 1;
   const int p = (int)(b / a.NBb);
   const int64_t gb = b % a.NBb;
   const int4 bi = a.info[gb];
@@ -502,11 +528,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.f; dv[dt][i] = 0.f; }
 
-  // tiles: the own block's rows from k0 on, per query head of the kv head,
-  // then the bin's items
+  // tiles: the own block's rows from k0 on, per query head of the kv head
+  // (first segment only), then the segment's items of the bin
   const int own_per_head = (bi.z - k0 + kKvRows - 1) / kKvRows;
-  const int n_own = a.G * own_per_head;
-  const uint32_t ibeg = a.bin_off[b], iend = a.bin_off[b + 1];
+  const int n_own = seg == 0 ? a.G * own_per_head : 0;
+  const uint32_t ibeg = a.bin_off[b] + (uint32_t)(seg * a.seg_rows);
+  const uint32_t iend = (uint32_t)min((int64_t)a.bin_off[b + 1], (int64_t)ibeg + a.seg_rows);
   const int ntiles = n_own + (int)((iend - ibeg + kKvRows - 1) / kKvRows);
 
   // ---- row staging (wave 1, lanes 0..31: row n of a tile)
@@ -703,8 +730,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   }
 
   if (!kvalid) return;
-  const int64_t o = ((int64_t)(bi.y + key) * a.Hkv + g) * kHeadDim + 4 * hh;
   const float sc = a.scale;
+  if (nseg > 1) {
+    // fp32 partial of this segment, summed with the bin's other segments by
+    // bwd_dkdv_sum_kernel
+    const int64_t slot = a.slot_off[b] + seg;
+    float *pk = a.part + ((slot * nch + kc) * kKvKeys + (key - k0)) * kHeadDim + 4 * hh;
+    float *pv = pk + a.part_half;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        *(float4 *)(pk + 32 * dt + 8 * aa) =
+            make_float4(dk[dt][4 * aa] * sc, dk[dt][4 * aa + 1] * sc, dk[dt][4 * aa + 2] * sc,
+                        dk[dt][4 * aa + 3] * sc);
+        *(float4 *)(pv + 32 * dt + 8 * aa) =
+            make_float4(dv[dt][4 * aa], dv[dt][4 * aa + 1], dv[dt][4 * aa + 2], dv[dt][4 * aa + 3]);
+      }
+    return;
+  }
+  const int64_t o = ((int64_t)(bi.y + key) * a.Hkv + g) * kHeadDim + 4 * hh;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -714,6 +759,101 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       store_bf16x4(a.dv + o + 32 * dt + 8 * aa, dv[dt][4 * aa], dv[dt][4 * aa + 1],
                    dv[dt][4 * aa + 2], dv[dt][4 * aa + 3]);
     }
+}
+
+// Exclusive scans over the bins of a pass: ext_off (segments beyond the
+// first, ceil(rows / seg_rows) - 1 per bin) and slot_off (partial slots: all
+// segments of a split bin, none for a bin of one segment).
+__global__ __launch_bounds__(1024) void dkdv_seg_scan_kernel(const uint32_t *__restrict__ bin_off,
+                                                             int64_t nbins, int64_t seg_rows,
+                                                             uint32_t *__restrict__ ext_off,
+                                                             uint32_t *__restrict__ slot_off) {
+  __shared__ uint32_t wsum[2][16];
+  __shared__ uint32_t carry[2];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) { carry[0] = 0; carry[1] = 0; }
+  __syncthreads();
+  for (int64_t base = 0; base < nbins; base += 1024) {
+    const int64_t bb = base + threadIdx.x;
+    uint32_t x[2] = {0u, 0u};
+    if (bb < nbins) {
+      const int64_t rows = (int64_t)bin_off[bb + 1] - bin_off[bb];
+      const int64_t nseg = rows > seg_rows ? (rows + seg_rows - 1) / seg_rows : 1;
+      x[0] = (uint32_t)(nseg - 1);
+      x[1] = nseg > 1 ? (uint32_t)nseg : 0u;
+    }
+    uint32_t incl[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      uint32_t y = x[v];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(y, o);
+        if (lane >= o) y += t;
+      }
+      if (lane == 63) wsum[v][w] = y;
+      incl[v] = y;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        uint32_t y = lane < 16 ? wsum[v][lane] : 0u;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const uint32_t t = __shfl_up(y, o);
+          if (lane >= o) y += t;
+        }
+        if (lane < 16) wsum[v][lane] = y;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 2; ++v) incl[v] += (w > 0 ? wsum[v][w - 1] : 0u) + carry[v];
+    if (bb < nbins) {
+      ext_off[bb] = incl[0] - x[0];
+      slot_off[bb] = incl[1] - x[1];
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) { carry[0] = incl[0]; carry[1] = incl[1]; }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    ext_off[nbins] = carry[0];
+    slot_off[nbins] = carry[1];
+  }
+}
+
+// dK, dV of the keys of a split bin: the sum of its segments' partials in
+// segment order, rounded to bf16. One workgroup per (bin, key chunk); 8
+// rows of 32 lanes (4 dims each) at a time.
+__global__ __launch_bounds__(256) void bwd_dkdv_sum_kernel(const BwdArgs a) {
+  const int nch = (a.B + kKvKeys - 1) / kKvKeys;
+  const int64_t b = blockIdx.x / nch;
+  const int kc = (int)(blockIdx.x % nch);
+  if (b >= a.nbins) return;
+  const int nseg = (int)(a.ext_off[b + 1] - a.ext_off[b]) + 1;
+  if (nseg == 1) return;
+  const int p = (int)(b / a.NBb);
+  const int4 bi = a.info[b % a.NBb];
+  const int k0 = kc * kKvKeys;
+  if (bi.x < 0 || k0 >= bi.z) return;
+  const int g = a.g0 + p;
+  const int e = (threadIdx.x & 31) * 4;
+  const int64_t slot0 = a.slot_off[b];
+  for (int kl = threadIdx.x >> 5; kl < min(kKvKeys, bi.z - k0); kl += 8) {
+    float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+    for (int sg = 0; sg < nseg; ++sg) {
+      const float *pk = a.part + (((slot0 + sg) * nch + kc) * kKvKeys + kl) * kHeadDim + e;
+      const float4 x = *(const float4 *)pk;
+      const float4 y = *(const float4 *)(pk + a.part_half);
+      sk.x += x.x; sk.y += x.y; sk.z += x.z; sk.w += x.w;
+      sv.x += y.x; sv.y += y.y; sv.z += y.z; sv.w += y.w;
+    }
+    const int64_t o = ((int64_t)(bi.y + k0 + kl) * a.Hkv + g) * kHeadDim + e;
+    store_bf16x4(a.dk + o, sk.x, sk.y, sk.z, sk.w);
+    store_bf16x4(a.dv + o, sv.x, sv.y, sv.z, sv.w);
+  }
 }
 
 BwdArgs make_args(const Problem &pb, const Work &w, const BwdWork &bw, const BwdIo &io, int g0) {
@@ -737,10 +877,43 @@ BwdArgs make_args(const Problem &pb, const Work &w, const BwdWork &bw, const Bwd
   a.dk = (__bf16 *)io.dk;
   a.dv = (__bf16 *)io.dv;
   a.zeros = bw.zeros;
+  a.ext_off = bw.ext_off;
+  a.slot_off = bw.slot_off;
+  a.part = bw.part;
+  const DkdvSplit sp = dkdv_split(pb.T, pb.Hp, pb.k, pb.B);
+  a.seg_rows = sp.seg_rows;
+  a.extra_wg = (sp.extra_bound + 7) / 8 * 8 * sp.nch;
+  a.part_half = 2 * sp.extra_bound * sp.nch * kKvKeys * kHeadDim;
   return a;
 }
 
 }  // namespace
+
+DkdvSplit dkdv_split(int64_t T, int Hp, int k, int B) {
+  DkdvSplit sp;
+  int64_t seg = 262144;
+  if (const char *env = getenv("MOBA_DKDV_SEGMENT_ROWS")) {
+    const long long v = atoll(env);
+    if (v >= kKvRows) seg = v / kKvRows * kKvRows;
+  }
+  sp.seg_rows = seg;
+  sp.extra_bound = T * Hp * (int64_t)(k > 1 ? k - 1 : 0) / seg;  // dispatched rows / seg
+  sp.nch = (B + kKvKeys - 1) / kKvKeys;
+  return sp;
+}
+
+BwdExtra bwd_extra(size_t base, int64_t nbins, const DkdvSplit &sp) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  BwdExtra x;
+  size_t off = al(base);
+  x.zeros = off;    off = al(off + kBwdZeroBytes);
+  x.ext_off = off;  off = al(off + sizeof(uint32_t) * (size_t)(nbins + 1));
+  x.slot_off = off; off = al(off + sizeof(uint32_t) * (size_t)(nbins + 1));
+  x.part = off;
+  off = al(off + sizeof(float) * 2 * (size_t)(2 * sp.extra_bound) * sp.nch * kKvKeys * kHeadDim);
+  x.end = off;
+  return x;
+}
 
 hipError_t launch_bwd_delta(const Problem &pb, const void *out, const void *dout, float *delta,
                             hipStream_t s) {
@@ -786,8 +959,16 @@ hipError_t launch_bwd_dkdv(const Problem &pb, const Work &w, const BwdWork &bw, 
   const int64_t grid = (a.nbins + 7) / 8 * 8 * nch;
   hipError_t e = launch_fill_u32((uint32_t *)bw.zeros, 0u, kBwdZeroBytes / 4, s);
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<<<dim3((unsigned)grid), 512, 0, s>>>(a);
-  return hipGetLastError();
+  dkdv_seg_scan_kernel<<<1, 1024, 0, s>>>(a.bin_off, a.nbins, a.seg_rows, bw.ext_off,
+                                          bw.slot_off);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bwd_dkdv_kernel<<<dim3((unsigned)(a.extra_wg + grid)), 512, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.extra_wg > 0) {
+    bwd_dkdv_sum_kernel<<<dim3((unsigned)(a.nbins * nch)), 256, 0, s>>>(a);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace moba

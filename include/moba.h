@@ -335,8 +335,11 @@ moba_status_t moba_decode(const void *q, const void *k_cache, const void *v_cach
  * heads; see moba_plan): the forward plan's regions, except that the vt
  * region is unused, part_o_offset is the fp32 partial dq of each
  * (row, head, slot) ([T][Hp][topk][d]) and part_lse_offset is D ([Hq][T]
- * float32); the last 256 bytes are a zero area that moba_attn_bwd_dkdv
- * clears and reads. */
+ * float32), followed by the dk/dv stage's own areas: 256 bytes it zeroes and
+ * reads, two per-bin prefix arrays, and fp32 partials for bins it splits into
+ * segments of MOBA_DKDV_SEGMENT_ROWS rows (environment variable, a multiple
+ * of 32; default 262144; read by the plan and by the stage, which must agree).
+ * */
 moba_status_t moba_bwd_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
                             int32_t kv_heads_per_pass, moba_layout_t *layout);
 /* Bytes of workspace moba_bwd needs for the given pass size; 0 if invalid. */

@@ -155,6 +155,52 @@ def test_bwd_with_a_moving_maximum():
     note("stats %s selection_differs_in_near_ties=%d" % (stats, n_diff))
 
 
+@pytest.mark.parametrize("kind", ["mean", "window1"])
+def test_bwd_with_split_bins(kind, monkeypatch):
+    """Bins processed in segments (MOBA_DKDV_SEGMENT_ROWS forces segments of
+    64 rows, so every bin of this shape splits into many): dk and dv are the
+    segments' fp32 partials summed in segment order. Every element against
+    the oracle, and against the same call with bins in one piece."""
+    import torch
+    lengths, hq, hkv, B, k, seed = [2048, 600], 8, 2, 256, 3, 81
+    inp = synth.custom(lengths, hq, hkv, 128, "bf16", B, k, seed)
+    q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
+    sh = moba.shape_of(q, kk, cu)
+    gate = make_gate(kind)
+    fwd_ws = torch.empty(moba.moba_fwd_workspace_size(sh, B, k, 0), dtype=torch.uint8,
+                         device="cuda")
+    out, lse = moba.moba_fwd_gated(q, kk, v, cu, B, k, gate or moba.gate_mean(), fwd_ws)
+    T = inp.q.shape[0]
+    rng = np.random.default_rng(seed + 1000)
+    dout = torch.from_numpy(rng.standard_normal((T, hq, 128), dtype=np.float32)).to(
+        torch.bfloat16).cuda()
+    results = {}
+    for seg in ("64", None):
+        if seg is None:
+            monkeypatch.delenv("MOBA_DKDV_SEGMENT_ROWS", raising=False)
+        else:
+            monkeypatch.setenv("MOBA_DKDV_SEGMENT_ROWS", seg)
+        lay = moba.moba_bwd_plan(sh, B, k, 0)
+        ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
+        results[seg] = moba.moba_bwd(q, kk, v, out, lse, dout, cu, B, k, ws, gate=gate)
+        torch.cuda.synchronize()
+        if seg is not None:
+            gidx = workspace_view(ws, lay.idx_offset, T * hq * k, torch.int32).view(
+                T, hq, k).cpu().numpy()
+    monkeypatch.delenv("MOBA_DKDV_SEGMENT_ROWS", raising=False)
+    sel, n_diff = checked_selection(inp, B, k, kind, gidx)
+    ref = oracle.attend_bwd(inp.q, inp.k, inp.v, to_host_f64(dout), inp.cu_seqlens, B, k,
+                            np.ascontiguousarray(sel))
+    stats = {name: compare(name, to_host_f64(got), r)
+             for name, got, r in zip(("dq", "dk", "dv"), results["64"], ref)}
+    note("split stats %s" % (stats,))
+    # dq does not depend on the split; dk and dv differ by the order of fp32 sums only
+    assert torch.equal(results["64"][0], results[None][0])
+    for x, y in zip(results["64"][1:], results[None][1:]):
+        diff = (x.float() - y.float()).abs().max().item()
+        assert diff <= 2.0 ** -7 * y.float().abs().max().item(), diff
+
+
 def test_bwd_pass_sizes_agree_and_repeat():
     """One pass of all kv heads and passes of one kv head give the same
     gradients; dq and dk/dv do not depend on the bin item order beyond
