@@ -637,10 +637,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int i = 8 * c + j;
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[j]));
-        if (own && key > rt + 16 * c + 4 * (j & 3) + 2 * hh + (j >> 2)) pv = 0.f;
-        s[i] = pv;
+        s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[j]));
       }
+    }
+    if (own) {
+      // causal mask of the own block: key > row, with row = rt + 16 c +
+      // 4 (j % 4) + 2 hh + j / 4 for score 8 c + j of this lane
+      const int kr = key - rt - 2 * hh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kr > 16 * (i >> 3) + 4 * (i & 3) + ((i >> 2) & 1)) s[i] = 0.f;
     }
     bf16x8 pb[2], db[2];
 #pragma unroll
