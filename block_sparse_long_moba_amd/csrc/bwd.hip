@@ -440,15 +440,15 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
 // The Q and dO tiles of a stage are 2 x 32 x 17 slots of 16 B (the 17th slot
 // of a row is padding), filled by 17 wave-wide direct loads of 64 slots,
 // three each on waves 0, 2 and 3 and two each on waves 4..7. A row past the
-// end of the
-// tile loads from a zeroed 256-byte area and gets lse = +inf and D = 0, so its
-// probabilities and dS are exactly 0. Tile x's rows are fetched two tiles
-// ahead: in the body of tile x - 2, wave 1 (lanes 0..31, one row each) loads
-// the items of tile x + 1 and the lse and D of tile x into registers; every
-// wave issues tile x's Q and dO loads from the (token, head) slot; at the end
-// of the body wave 1 stores the lse and D and decodes the items into
-// (token, head); wave 1 issues no direct loads, so that nothing it waits for
-// is a tile load. A body ends when each wave's loads of the next tile have
+// end of the tile loads from a zeroed 256-byte area and gets lse = +inf and
+// D = 0, so its probabilities and dS are exactly 0. Tile x's rows are fetched
+// two tiles ahead: in the body of tile x - 2, wave 1 (lanes 0..31, one row
+// each) loads the items of tile x + 1 and the lse and D of tile x into
+// registers; every wave issues tile x's Q and dO loads from the row addresses
+// in LDS; at the end of the body wave 1 stores the lse and D, decodes the
+// items into (token, head) and stores the addresses of those rows' Q and dO;
+// wave 1 issues no direct loads, so that nothing it waits for is a tile
+// load. A body ends when each wave's loads of the next tile have
 // landed, with a barrier that leaves the loads of the tile after in flight.
 // The loop is unrolled by the three stages so that every access names its
 // stage array: the compiler then sees that a body's direct loads and its LDS
@@ -463,7 +463,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
   __shared__ __attribute__((aligned(1024))) char stage2[STAGE];
   __shared__ __attribute__((aligned(16))) float lse_d[4][2 * kKvRows];  // [slot][lse 32, D 32]
-  __shared__ __attribute__((aligned(16))) int2 rinfo[2][kKvRows];       // (token, head)
+  // addresses of the Q and dO rows of a tile (the zeroed area past its end)
+  __shared__ __attribute__((aligned(16))) const char *raddr[2][2][kKvRows];  // [slot][Q, dO][row]
   __shared__ __attribute__((aligned(1024))) char klds[8 * 32 * NP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -569,6 +570,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     L[kKvRows + npos] = rw.x >= 0 ? d : 0.f;
   };
   auto lse_off = [&](int2 rw) { return rw.x >= 0 ? (int64_t)rw.y * a.T + rw.x : (int64_t)0; };
+  auto raddr_store = [&](int x, int2 rw) {
+    const int64_t o = ((int64_t)rw.x * a.Hq + rw.y) * kHeadDim;
+    raddr[x & 1][0][n] = rw.x >= 0 ? (const char *)(a.q + o) : (const char *)a.zeros;
+    raddr[x & 1][1][n] = rw.x >= 0 ? (const char *)(a.dout + o) : (const char *)a.zeros;
+  };
 
   // ---- direct loads of the Q and dO tiles: this wave's loads are slots
   // 64 ld + lane for ld = ld0 .. ld0 + nld - 1
@@ -576,23 +582,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   const int nld = wave == 1 ? 0 : wv < 3 ? 3 : 2;
   const int ld0 = wv < 3 ? 3 * wv : 9 + 2 * (wv - 3);
   auto issue = [&](char *st, int x) {
-    const int2 *ri = rinfo[x & 1];
+    const char *const *ra = &raddr[x & 1][0][0];
+    const char *gp[3];
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       if (u >= nld) break;
-      const int ld = ld0 + u;
-      const int sx = 64 * ld + lane;
+      const int sx = 64 * (ld0 + u) + lane;
       const bool is_do = sx >= kKvRows * SLOTS;
       const int y = is_do ? sx - kKvRows * SLOTS : sx;
       const int row = y / SLOTS;
       const int chunk = min(y - row * SLOTS, 15);  // the padding slot repeats chunk 15
-      const int2 rw = ri[row];
-      const __bf16 *src = is_do ? a.dout : a.q;
-      const void *gp = rw.x >= 0
-                           ? (const void *)(src + ((int64_t)rw.x * a.Hq + rw.y) * kHeadDim +
-                                            8 * chunk)
-                           : (const void *)((const char *)a.zeros + 16 * chunk);
-      __builtin_amdgcn_global_load_lds((global_ptr_t)gp, (lds_ptr_t)(st + 1024 * ld), 16, 0, 0);
+      gp[u] = ra[(is_do ? kKvRows : 0) + row] + 16 * chunk;
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      if (u >= nld) break;
+      __builtin_amdgcn_global_load_lds((global_ptr_t)gp[u], (lds_ptr_t)(st + 1024 * (ld0 + u)), 16,
+                                       0, 0);
     }
   };
 
@@ -677,14 +683,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
   };
 
   // body of tile it: cur is its stage, nx2 the stage of tile it + 2
+  int2 st_rw;  // stager lanes: row n of tile it + 2 at the start of body it
   auto body = [&](char *cur, char *nx2, int it) {
     // assigned and read on the stager lanes only
     uint32_t st_item;
-    int2 st_rw;
     float st_l, st_d;
     if (stager) {
       st_item = item_load(it + 3);
-      st_rw = rinfo[it & 1][n];  // tile it + 2's rows
       const int64_t o = lse_off(st_rw);
       st_l = a.lse[o];
       st_d = a.delta[o];
@@ -700,7 +705,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
       // their loads, which would wait for the loads there)
       asm volatile("" : "+v"(st_l), "+v"(st_d), "+v"(st_item));
       lse_store(it + 2, st_rw, st_l, st_d);
-      rinfo[(it + 3) & 1][n] = row_of(it + 3, st_item);
+      st_rw = row_of(it + 3, st_item);
+      raddr_store(it + 3, st_rw);
     }
     lds_barrier();
   };
@@ -712,7 +718,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int2 rw = row_of(x, item_load(x));
-        rinfo[x][n] = rw;
+        raddr_store(x, rw);
         const int64_t o = lse_off(rw);
         lse_store(x, rw, a.lse[o], a.delta[o]);
       }
@@ -720,8 +726,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const BwdArgs a) {
     __syncthreads();
     issue(stage0, 0);
     issue(stage1, 1);
-    __syncthreads();  // every wave has read both row slots
-    if (stager) rinfo[0][n] = row_of(2, item_load(2));
+    __syncthreads();  // every wave has read both address slots
+    if (stager) {
+      st_rw = row_of(2, item_load(2));
+      raddr_store(2, st_rw);
+    }
     wait_all_loads();
     __syncthreads();
     int it = 0;
