@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
 //
 // LDS: three stages of {Q tile, dO tile}, each 32 rows of 256 B at a pitch
 // of 272 B, as three separate arrays; four slots of the 32 rows' lse (log2
-// units) and D; two slots of the rows' (token, head); the waves' K rows
+// units) and D; two slots of the rows' Q and dO addresses; the waves' K rows
 // (pitch 272 B). The padding puts row r at bank group 4r mod 64, so the 16
 // rows that 16 lanes read at one chunk column fall in 16 different 16-byte
 // bank groups. The transposed operands (Q^T, dO^T as A operands of dK^T and
