@@ -92,11 +92,14 @@ BWD = [
     ([900],                  4,  4, 128, 16, "mean",     66),  # topk covers every block: dense
     ([1000, 700],            4,  2, 128,  4, "window1",  67),  # window gate with a sink
     ([1500],                 8,  2, 128,  5, "pooled11", 68),  # pooled gate
+    # 1100 sequences of up to three blocks
+    ([int(x) for x in np.random.default_rng(72).integers(0, 140, 1100)], 4, 2, 64, 3, "mean", 70),
 ]
 
 
 @pytest.mark.parametrize("case", BWD, ids=lambda c: "L%s_h%d_%d_B%d_k%d_%s" % (
-    "-".join(map(str, c[0])), c[1], c[2], c[3], c[4], c[5]))
+    "-".join(map(str, c[0])) if len(c[0]) <= 8 else "S%d-T%d" % (len(c[0]), sum(c[0])),
+    c[1], c[2], c[3], c[4], c[5]))
 def test_bwd_matches_oracle_on_every_element(case):
     import torch
     lengths, hq, hkv, B, k, kind, seed = case

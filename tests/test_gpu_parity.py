@@ -58,6 +58,17 @@ def gpu_rows(out, lse, rows):
     return o, l
 
 
+def many_lengths(n, hi, seed):
+    """n sequence lengths drawn uniformly from [0, hi) (empty ones included)."""
+    return [int(x) for x in np.random.default_rng(seed).integers(0, hi, n)]
+
+
+def lengths_id(lengths):
+    if len(lengths) <= 8:
+        return "-".join(map(str, lengths))
+    return "S%d-T%d" % (len(lengths), sum(lengths))
+
+
 SMALL = [
     # lengths,              Hq, Hkv, dtype,  B,   k, seed
     ([1000],                 4,  2, "bf16", 128,  3, 11),  # ragged tail, several tiles
@@ -68,11 +79,13 @@ SMALL = [
     ([1500],                 4,  4, "bf16", 256, 16, 16),  # topk covers all blocks: dense
     ([3000, 1000],          16,  2, "bf16", 192,  5, 17),  # block size 3*64, G = 8
     ([777, 1234],            2,  1, "fp32",  64,  6, 18),  # fp32, G = 2, many small blocks
+    # 1500 sequences (the sequence-table scan carries past 1024 of them)
+    (many_lengths(1500, 80, 71), 4, 2, "bf16",  64,  2, 19),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "L%s_h%d_%d_%s_B%d_k%d" % (
-    "-".join(map(str, c[0])), c[1], c[2], c[3], c[4], c[5]))
+    lengths_id(c[0]), c[1], c[2], c[3], c[4], c[5]))
 def test_moba_fwd_matches_oracle_on_every_row(case):
     import torch
     lengths, hq, hkv, dtype, B, k, seed = case
