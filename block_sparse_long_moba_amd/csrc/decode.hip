@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_gate_kernel(const T *__restrict__ 
   const int g = h / (Hq / Hkv);
   __shared__ float qs[kHeadDim];
   __shared__ float sc[kLdsBins];
-  __shared__ uint8_t chosen[kLdsBins];
+  __shared__ int wcnt[4];
   if (tid < kHeadDim) {
     float f[8];
     if ((tid & 7) == 0) {
@@ -99,37 +99,61 @@ __global__ __launch_bounds__(256) void decode_gate_kernel(const T *__restrict__ 
     }
   }
   __syncthreads();
+  // scores: 16 lanes per block (8 dimensions each, a coalesced 512-byte row),
+  // 128 blocks per round
   const float *kb0 = kbar + ((int64_t)blk_first[s] * Hkv + g) * kHeadDim;
   const int64_t kstride = (int64_t)Hkv * kHeadDim;
-  for (int j = tid; j < c; j += 256) {
-    const float *kb = kb0 + j * kstride;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < kHeadDim; e += 4) {
-      const float4 kv = *(const float4 *)(kb + e);
-      a0 = fmaf(qs[e], kv.x, a0);
-      a1 = fmaf(qs[e + 1], kv.y, a1);
-      a2 = fmaf(qs[e + 2], kv.z, a2);
-      a3 = fmaf(qs[e + 3], kv.w, a3);
+  const int sub = tid & 15, grp = tid >> 4;
+  float qv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] = qs[8 * sub + i];
+  for (int j0 = 0; j0 < c; j0 += 128) {
+    float dsum[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + 16 * u + grp, c - 1);
+      const float4 x0 = *(const float4 *)(kb0 + j * kstride + 8 * sub);
+      const float4 x1 = *(const float4 *)(kb0 + j * kstride + 8 * sub + 4);
+      dsum[u] = ((qv[0] * x0.x + qv[1] * x0.y) + (qv[2] * x0.z + qv[3] * x0.w)) +
+                ((qv[4] * x1.x + qv[5] * x1.y) + (qv[6] * x1.z + qv[7] * x1.w));
     }
-    sc[j] = (a0 + a1) + (a2 + a3);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float v = dsum[u];
+      v += __shfl_xor(v, 8, 16);
+      v += __shfl_xor(v, 4, 16);
+      v += __shfl_xor(v, 2, 16);
+      v += __shfl_xor(v, 1, 16);
+      const int j = j0 + 16 * u + grp;
+      if (sub == 0 && j < c) sc[j] = v;
+    }
   }
   __syncthreads();
-  for (int j = tid; j < c; j += 256) {
-    const float sj = sc[j];
-    int rank = 0;
-    for (int i = 0; i < c; ++i) {
-      const float si = sc[i];
-      rank += (si > sj) || (si == sj && i < j);
+  // block j is chosen iff fewer than pick candidates rank above it; the
+  // chosen blocks are written in ascending order (positions by ballot)
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;
+  for (int j0 = 0; j0 < c; j0 += 256) {
+    const int j = j0 + tid;
+    bool f = false;
+    if (j < c) {
+      const float sj = sc[j];
+      int rank = 0;
+      for (int i = 0; i < c; ++i) {
+        const float si = sc[i];
+        rank += (si > sj) || (si == sj && i < j);
+      }
+      f = rank < pick;
     }
-    chosen[j] = rank < pick;
-  }
-  __syncthreads();
-  for (int j = tid; j < c; j += 256) {
-    if (!chosen[j]) continue;
-    int pos = 0;
-    for (int i = 0; i < j; ++i) pos += chosen[i];
-    dst[pos] = j;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wcnt[w];
+    if (f) dst[off + __popcll(m & below)] = j;
+    base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();
   }
   if (tid == 0) {
     dst[pick] = c;
@@ -289,48 +313,78 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
   }
 }
 
-// Merge: one workgroup of 128 threads per (sequence, query head): the
+// Merge: one workgroup of 256 threads per (sequence, query head): the
 // log-sum-exp combination of its min(k, c+1) parts in ascending block order.
+// The part lse values are reduced by all threads; wave w adds the rows of
+// parts w, w + 4, ... (two elements per lane, eight rows in flight), and the
+// four waves' sums are added in wave order.
 template <typename T>
-__global__ __launch_bounds__(128) void decode_merge_kernel(const float *__restrict__ part_o,
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restrict__ part_o,
                                                            const float *__restrict__ part_lse,
                                                            const int32_t *__restrict__ cu,
                                                            int S, int Hq, int B, int k, int ns,
                                                            T *__restrict__ out,
                                                            float *__restrict__ lse) {
-  const int s = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
+  const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int L = cu[s + 1] - cu[s];
   T *dst = out + ((int64_t)s * Hq + h) * kHeadDim;
   if (L == 0) {
-    dst[e] = (T)0.f;
-    if (e == 0 && lse) lse[(int64_t)h * S + s] = -INFINITY;
+    if (tid < kHeadDim) dst[tid] = (T)0.f;
+    if (tid == 0 && lse) lse[(int64_t)h * S + s] = -INFINITY;
     return;
   }
+  __shared__ float red[4];
+  __shared__ float2 wsum[4][kHeadDim / 2];
   const int n = min(k, (L - 1) / B + 1) * ns;  // parts of the selected blocks, in block order
   const int64_t base = ((int64_t)s * Hq + h) * k * ns;
   const float *pl = part_lse + base;
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, pl[i]);
+  for (int i = tid; i < n; i += 256) M = fmaxf(M, pl[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
   float sum = 0.f;
-  for (int i = 0; i < n; ++i)
+  for (int i = tid; i < n; i += 256)
     if (pl[i] > -INFINITY) sum += __builtin_amdgcn_exp2f((pl[i] - M) * kLog2eDec);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  sum = (red[0] + red[1]) + (red[2] + red[3]);
   const float Lt = M + __logf(sum);
-  // part rows loaded 16 at a time, unconditionally (an empty part's row is
-  // written too), and added in part order
-  float o = 0.f;
-  for (int i0 = 0; i0 < n; i0 += 16) {
-    float x[16];
+  // part rows (written for every part, empty ones too) loaded unconditionally
+  float2 o = make_float2(0.f, 0.f);
+  for (int i0 = wave; i0 < n; i0 += 32) {
+    float2 x[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) x[u] = i0 + u < n ? part_o[(base + i0 + u) * kHeadDim + e] : 0.f;
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + 4 * u, n - 1);
+      x[u] = *(const float2 *)(part_o + (base + i) * kHeadDim + 2 * lane);
+    }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      if (i0 + u >= n) break;
-      if (pl[i0 + u] > -INFINITY)
-        o += __builtin_amdgcn_exp2f((pl[i0 + u] - Lt) * kLog2eDec) * x[u];
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 4 * u;
+      if (i < n && pl[i] > -INFINITY) {
+        const float wt = __builtin_amdgcn_exp2f((pl[i] - Lt) * kLog2eDec);
+        o.x += wt * x[u].x;
+        o.y += wt * x[u].y;
+      }
     }
   }
-  dst[e] = (T)o;
-  if (e == 0 && lse) lse[(int64_t)h * S + s] = Lt;
+  wsum[wave][lane] = o;
+  __syncthreads();
+  if (tid < kHeadDim / 2) {
+    float2 r = wsum[0][tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) { r.x += wsum[w][tid].x; r.y += wsum[w][tid].y; }
+    dst[2 * tid] = (T)r.x;
+    dst[2 * tid + 1] = (T)r.y;
+  }
+  if (tid == 0 && lse) lse[(int64_t)h * S + s] = Lt;
 }
 
 }  // namespace
@@ -363,7 +417,7 @@ hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const 
       decode_attn_kernel<__bf16, 8><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
                                                        (const __bf16 *)vc, w.cu, w.idx, pb.Hq,
                                                        pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
-    decode_merge_kernel<__bf16><<<gg, 128, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
+    decode_merge_kernel<__bf16><<<gg, 256, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
                                                    ns, (__bf16 *)out, lse);
   } else {
     decode_gate_kernel<float><<<gg, 256, 0, s>>>((const float *)q, w.kbar, w.cu, w.blk_first,
@@ -376,7 +430,7 @@ hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const 
       decode_attn_kernel<float, 8><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
                                                       (const float *)vc, w.cu, w.idx, pb.Hq,
                                                       pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
-    decode_merge_kernel<float><<<gg, 128, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
+    decode_merge_kernel<float><<<gg, 256, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
                                                   ns, (float *)out, lse);
   }
   return hipGetLastError();
