@@ -23,7 +23,9 @@
 //   causally) and then the rows of its bin stream through LDS in tiles of 32
 //   rows, stored row-major; the transposed operands come from the same tiles
 //   through the LDS transpose read. Per tile S = Q K^T, dP = dO V^T, dS,
-//   dV^T += dO^T P and dK^T += Q^T dS; dK and dV are written once.
+//   dV^T += dO^T P and dK^T += Q^T dS; dK and dV are written once (a bin
+//   too large for one workgroup is split into segments whose fp32 partials
+//   a second kernel adds in segment order).
 // Lane layouts: v_mfma_f32_32x32x16_bf16, lane l holds A[m = l%32][k = 8(l/32)
 // .. +7] and B[k = 8(l/32) .. +7][n = l%32]; accumulator i of lane l is
 // C[8(i/4) + 4(l/32) + i%4][l%32]. Feeding M-row m from source row perm(m)
