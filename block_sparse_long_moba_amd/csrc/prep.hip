@@ -294,32 +294,45 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
   const int nsel = min(k, c + 1);
   // a slot whose lse is -inf holds no block (a gate that picked fewer blocks
   // than it had slots) and is skipped
+  // the row's lanes load its slots' lse values together (slot i0 + lane),
+  // then reduce them with shuffles inside the row's lane group
   const float *pl = part_lse + row * k;
   float m = -INFINITY;
-  for (int i = 0; i < nsel; ++i) m = fmaxf(m, pl[i]);
+  for (int i0 = 0; i0 < nsel; i0 += LANES)
+    m = fmaxf(m, i0 + lane < nsel ? pl[i0 + lane] : -INFINITY);
+#pragma unroll
+  for (int o = LANES / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, LANES));
   float sum = 0.f;
-  for (int i = 0; i < nsel; ++i)
-    if (pl[i] > -INFINITY) sum += __builtin_amdgcn_exp2f((pl[i] - m) * kLog2eF);
+  for (int i0 = 0; i0 < nsel; i0 += LANES) {
+    const float x = i0 + lane < nsel ? pl[i0 + lane] : -INFINITY;
+    if (x > -INFINITY) sum += __builtin_amdgcn_exp2f((x - m) * kLog2eF);
+  }
+#pragma unroll
+  for (int o = LANES / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, LANES);
   const float L = m + logf(sum);
   float acc[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) acc[j] = 0.f;
   const TO *po = part_o + row * k * kHeadDim + lane * N;
-  // all slots of the row in flight at once (16 per batch)
+  // all slots of the row in flight at once (16 per batch); lane u of the
+  // group holds the weight of slot i0 + u, 0 for a slot past nsel or without
+  // a block (whose row is not loaded)
   for (int i0 = 0; i0 < nsel; i0 += 16) {
+    const float x = lane < 16 && i0 + lane < nsel ? pl[i0 + lane] : -INFINITY;
+    const float wl = x > -INFINITY ? __builtin_amdgcn_exp2f((x - L) * kLog2eF) : 0.f;
+    float wgt[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) wgt[u] = __shfl(wl, u, LANES);
     uint4 raw[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      raw[u] = i0 + u < nsel ? *(const uint4 *)(po + (int64_t)(i0 + u) * kHeadDim)
+      raw[u] = wgt[u] != 0.f ? *(const uint4 *)(po + (int64_t)(i0 + u) * kHeadDim)
                              : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      if (i0 + u >= nsel) break;
-      if (!(pl[i0 + u] > -INFINITY)) continue;
-      const float wgt = __builtin_amdgcn_exp2f((pl[i0 + u] - L) * kLog2eF);
       const TO *v = (const TO *)&raw[u];
 #pragma unroll
-      for (int j = 0; j < N; ++j) acc[j] += wgt * (float)v[j];
+      for (int j = 0; j < N; ++j) acc[j] += wgt[u] * (float)v[j];
     }
   }
   TO res[N];
