@@ -88,6 +88,7 @@ SMALL = [
     ([8197],                      32,  8, "bf16", 512,  3, 73),  # 8B head shape
     ([1500, 700],                  4,  4, "bf16", 256, 16, 74),  # topk covers all: dense
     ([3000, 1000, 5000],          16,  2, "bf16", 192,  5, 75),  # G = 8, block 3*64
+    ([40000, 17000],               4,  2, "bf16",  64,  6, 76),  # 624 and 265 earlier blocks
 ]
 
 
