@@ -202,6 +202,14 @@ def test_pass_size_and_determinism():
     torch.cuda.synchronize()
     for x in (b, c, e):
         assert torch.equal(a[0], x[0]) and torch.equal(a[1], x[1])
+    # a max_seqlen hint (it bounds the blocks per sequence, so the plan may
+    # take more kv heads per pass) changes no bit of the result
+    sh = moba.shape_of(d_all.q, d_all.kk, d_all.cu, max_seqlen=3000)
+    ws = torch.empty(moba.moba_fwd_workspace_size(sh, 256, 4, 0), dtype=torch.uint8,
+                     device="cuda")
+    f = moba.moba_fwd_ex(d_all.q, d_all.kk, d_all.v, d_all.cu, 256, 4, ws, max_seqlen=3000)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], f[0]) and torch.equal(a[1], f[1])
 
 
 @pytest.mark.parametrize("case", [
