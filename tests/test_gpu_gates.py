@@ -149,6 +149,7 @@ POOLED = [
     ([0, 700, 1500],     4,  2, "bf16",  64,  6, 2, 1, 62),   # vector gate (G = 2)
     ([1500, 513],        8,  8, "fp32", 128,  4, 1, 1, 63),   # fp32
     ([4096],            32,  8, "bf16", 256,  8, 2, 2, 64),   # 8B head shape
+    ([8192],             8,  2, "bf16",  64, 22, 2, 1, 65),   # mean ranking keeps 18 (list of 24)
 ]
 
 

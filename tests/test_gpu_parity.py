@@ -1,8 +1,10 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Small shapes are checked on every row; the full-size workloads on sampled rows
-(every block's first and last row, random rows, every row of short blocks),
-with the same launch configuration the benchmark times.
+Small shapes are checked on every row. The full-size workloads, in the launch
+configuration the benchmark times, have the selection of every (row, head)
+compared with the oracle's, the pooled keys of every block, and the outputs of
+sampled rows (8 per block at 1M tokens, 64 per block otherwise, each
+sequence's first and last row, 64 rows of every short block).
 """
 import sys
 
@@ -81,6 +83,16 @@ SMALL = [
     ([777, 1234],            2,  1, "fp32",  64,  6, 18),  # fp32, G = 2, many small blocks
     # 1500 sequences (the sequence-table scan carries past 1024 of them)
     (many_lengths(1500, 80, 71), 4, 2, "bf16",  64,  2, 19),
+    # top-k lists of every register size with real ranking (127 earlier
+    # blocks at the end): the matrix-core gate (bf16, G = 4) keeps 8, 12,
+    # 16, 24 or 32 entries, the vector gate (G = 2, or fp32) 8, 16 or 32
+    ([8192],                 8,  2, "bf16",  64,  7, 61),
+    ([8192],                 8,  2, "bf16",  64, 10, 62),
+    ([8192],                 4,  1, "bf16",  64, 17, 63),
+    ([8192],                 4,  1, "bf16",  64, 25, 64),
+    ([8192],                 4,  1, "bf16",  64, 33, 65),
+    ([8192],                 4,  2, "bf16",  64, 17, 66),
+    ([6000],                 2,  2, "fp32",  64, 33, 67),
 ]
 
 
@@ -319,9 +331,10 @@ def ramped_compare(go, gl, ref_out, ref_lse, inp, dtype, roundings):
 
 # --------------------------------------------------------------- full size
 
-def staged_run(d, rows, heads_cb=None):
+def staged_run(d):
     """The bench's launch sequence (moba_fwd_ex's stage order) through the
-    stage entry points, collecting the selection of `rows` after each gate."""
+    stage entry points, collecting the whole selection idx[T][Hq][k] after
+    each pass's gate."""
     import torch
     sh, lay, B, k = d.shape, d.lay, d.B, d.k
     T, Hq = d.q.shape[0], d.q.shape[1]
@@ -330,13 +343,12 @@ def staged_run(d, rows, heads_cb=None):
     moba.moba_seqtable(d.cu, sh, B, lay, d.ws)
     moba.moba_meanpool(d.kk, sh, B, lay, d.ws)
     Hp, P = lay.q_heads_per_pass, lay.kv_heads_per_pass
-    sel = np.zeros((len(rows), Hq, k), np.int32)
-    rows_t = torch.from_numpy(rows).cuda()
+    sel = np.empty((T, Hq, k), np.int32)
     for g0 in range(0, sh.num_kv_heads, P):
         moba.moba_gate(d.q, sh, B, k, lay, d.ws, g0)
         idx = d.view(lay.idx_offset, T * Hp * k, torch.int32).view(T, Hp, k)
         h0 = g0 * Hq // sh.num_kv_heads
-        sel[:, h0:h0 + Hp] = idx.index_select(0, rows_t).cpu().numpy()
+        sel[:, h0:h0 + Hp] = idx.cpu().numpy()
         moba.moba_dispatch(sh, B, k, lay, d.ws, g0)
         moba.moba_attn_fwd(d.q, d.kk, d.v, sh, B, k, lay, d.ws, g0)
         moba.moba_merge(sh, B, k, lay, d.ws, out, lse, g0)
@@ -347,8 +359,29 @@ def staged_run(d, rows, heads_cb=None):
 FULL = sorted(synth.WORKLOADS, key=lambda n: synth.WORKLOADS[n].total_tokens)
 
 
+def output_rows(w):
+    """Rows whose outputs are checked at full size: 8 per block at 1M tokens,
+    64 per block otherwise (first, last and random rows), each sequence's
+    first and last row, and 64 random rows of every short block."""
+    cu = w.cu_seqlens()
+    per_block = 8 if w.total_tokens >= (1 << 20) else 64
+    rows = [check.sample_rows(cu, w.block_size, per_block, w.seed,
+                              every_row_of_short_blocks=False),
+            cu[:-1], cu[1:] - 1]
+    rng = np.random.default_rng(w.seed + 3000)
+    for s in range(len(cu) - 1):
+        L = int(cu[s + 1] - cu[s])
+        if L % w.block_size:
+            r0 = int(cu[s]) + L // w.block_size * w.block_size
+            rows.append(rng.integers(r0, int(cu[s + 1]), 64))
+    rows = np.unique(np.concatenate([np.asarray(r, np.int64) for r in rows]))
+    return rows[rows < w.total_tokens]
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_full_workload_sampled_rows(name):
+def test_full_workload_every_selection(name):
+    """Selection of every (row, head) against the oracle; outputs on the
+    sampled rows; pooled keys of every block."""
     import torch
     w = synth.WORKLOADS[name]
     note("workload %s: generating inputs" % name)
@@ -361,20 +394,9 @@ def test_full_workload_sampled_rows(name):
             w.topk, P) > (48 << 30):
         P //= 2
     d = Dev(inp, w.block_size, w.topk, kv_heads_per_pass=P)
-    if T <= 4096:
-        rows = out_rows = np.arange(T)
-    else:
-        # selection on the first/last and 6 random rows of every block (all rows
-        # of short blocks); outputs on a random subset plus each sequence's
-        # first and last row
-        rows = check.sample_rows(w.cu_seqlens(), w.block_size, 8, w.seed)
-        rng = np.random.default_rng(w.seed + 2000)
-        n_out = 96 if T >= (1 << 20) else 160
-        ends = np.concatenate([w.cu_seqlens()[:-1], w.cu_seqlens()[1:] - 1])
-        out_rows = np.unique(np.concatenate([rng.choice(rows, n_out, replace=False), ends]))
-    note("workload %s: GPU run, pass of %d kv heads, %d/%d sampled rows" % (
-        name, P, len(rows), len(out_rows)))
-    out, lse, gsel = staged_run(d, rows)
+    out_rows = np.arange(T) if T <= 4096 else output_rows(w)
+    note("workload %s: GPU run, pass of %d kv heads" % (name, P))
+    out, lse, gsel = staged_run(d)
     # one-call path, same launch configuration: identical bits
     out2, lse2 = moba.moba_fwd_ex(d.q, d.kk, d.v, d.cu, w.block_size, w.topk, d.ws)
     torch.cuda.synchronize()
@@ -385,10 +407,24 @@ def test_full_workload_sampled_rows(name):
     kbar = d.view(d.lay.kbar_offset, nb * w.num_kv_heads * 128, torch.float32).view(
         nb, w.num_kv_heads, 128).cpu().numpy()
     assert np.all(np.abs(kbar - kbar_ref) <= 2.0 ** -23 * np.abs(kbar_ref) + 1e-12)
-    note("workload %s: oracle on sampled rows" % name)
-    sel, ref_out, ref_lse, info, oi = check.reference_for_rows(
-        inp.q, inp.k, inp.v, inp.cu_seqlens, kbar_ref, w.block_size, w.topk, rows,
-        gpu_sel_rows=gsel, out_rows=out_rows)
+    note("workload %s: selection of all %d rows x %d heads against the oracle" % (
+        name, T, w.num_q_heads))
+    info = check.check_selection_all(gsel, inp.q, kbar_ref, inp.cu_seqlens, w.block_size,
+                                     w.topk, progress=note)
+    note("workload %s: %s" % (name, info))
+    assert info["rows_checked"] == T
+    # outputs: the oracle's attention over the GPU's selection (equal to the
+    # oracle's own except inside near ties, where it was just validated)
+    note("workload %s: oracle outputs of %d rows" % (name, len(out_rows)))
     go, gl = gpu_rows(out, lse, out_rows)
+    ref_out = np.empty_like(go)
+    ref_lse = np.empty_like(gl)
+    for i0 in range(0, len(out_rows), 512):
+        r = out_rows[i0:i0 + 512]
+        ref_out[i0:i0 + len(r)], ref_lse[i0:i0 + len(r)] = oracle.attend(
+            inp.q, inp.k, inp.v, inp.cu_seqlens, w.block_size, w.topk,
+            np.ascontiguousarray(gsel[r]), rows=r)
+        if i0 + 512 < len(out_rows):
+            note("workload %s: oracle outputs %d/%d" % (name, i0 + len(r), len(out_rows)))
     stats = check.compare_outputs(go, gl, ref_out, ref_lse, w.dtype)
-    note("workload %s: %s %s" % (name, stats, info))
+    note("workload %s: outputs of %d rows %s" % (name, len(out_rows), stats))
