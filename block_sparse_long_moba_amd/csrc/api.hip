@@ -7,7 +7,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
-#include <string>
+#include <mutex>
 
 #include "bwd.h"
 #include "moba_internal.h"
@@ -16,16 +16,15 @@ using namespace moba;
 
 namespace {
 
-thread_local std::string g_last_error;
+// a fixed buffer per thread: reporting an error allocates nothing
+thread_local char g_last_error[512];
 
 moba_status_t fail(moba_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 moba_status_t fail(moba_status_t st, const char *fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return st;
 }
 
@@ -83,11 +82,50 @@ moba_status_t check_moba_args(const moba_shape_t *sh, int32_t B, int32_t k) {
   return MOBA_SUCCESS;
 }
 
-// Table region: blk_first[S+1], a copy of cu_seqlens[S+1], then (16-byte
-// aligned) blk_info[NBb].
+// Table region: blk_first[S+1], a copy of cu_seqlens[S+1], the status word,
+// then (16-byte aligned) blk_info[NBb].
 size_t cu_copy_offset(int S) { return sizeof(int32_t) * (S + 1); }
-size_t info_offset(int S) { return (2 * sizeof(int32_t) * (S + 1) + 15) / 16 * 16; }
+size_t status_offset(int S) { return 2 * sizeof(int32_t) * (S + 1); }
+size_t info_offset(int S) { return (status_offset(S) + sizeof(int32_t) + 15) / 16 * 16; }
 size_t table_bytes(int S, int64_t NBb) { return info_offset(S) + 16 * (size_t)NBb; }
+
+// Pointers of one table region.
+struct Table {
+  int32_t *first, *cu, *status;
+  int4 *info;
+};
+Table table_at(void *base, int S) {
+  char *b = (char *)base;
+  return Table{(int32_t *)b, (int32_t *)(b + cu_copy_offset(S)), (int32_t *)(b + status_offset(S)),
+               (int4 *)(b + info_offset(S))};
+}
+
+// The status word's meaning (see the kStatus* bits).
+moba_status_t status_error(int32_t st) {
+  if (st & kStatusBadSeqlens)
+    return fail(MOBA_ERROR_INVALID_VALUE,
+                "cu_seqlens is malformed: it must start at 0, never decrease and end at "
+                "total_tokens");
+  if (st & kStatusTooManyBlocks)
+    return fail(MOBA_ERROR_INVALID_VALUE,
+                "a sequence has more blocks than the plan allows: max_seqlen is understated");
+  return MOBA_SUCCESS;
+}
+
+// Synchronises the stream and reads a status word.
+moba_status_t read_status(const int32_t *status, hipStream_t s) {
+  int32_t h = 0;
+  MOBA_HIP(hipMemcpyAsync(&h, status, sizeof h, hipMemcpyDeviceToHost, s), "hipMemcpyAsync");
+  MOBA_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");
+  return status_error(h);
+}
+
+// MOBA_CHECK=1 (environment): whole-pass calls check the sequence table on
+// the host right after building it (one synchronisation) and return an error.
+bool check_enabled() {
+  const char *e = getenv("MOBA_CHECK");
+  return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
 
 // Bins region: count[nbins], offset[nbins+1], tile_offset[nbins+1],
 // cursor[nbins], work counters[kWorkCounters] (uint32), then (16-byte
@@ -195,9 +233,11 @@ Problem make_problem(const moba_shape_t *sh, int32_t B, int32_t k, float scale,
 Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   char *b = (char *)ws;
   Work w{};
-  w.blk_first = (int32_t *)(b + L->table_offset);
-  w.cu = (int32_t *)(b + L->table_offset + cu_copy_offset(pb.S));
-  w.blk_info = (int4 *)(b + L->table_offset + info_offset(pb.S));
+  const Table tb = table_at(b + L->table_offset, pb.S);
+  w.blk_first = tb.first;
+  w.cu = tb.cu;
+  w.status = tb.status;
+  w.blk_info = tb.info;
   w.kbar = (float *)(b + L->kbar_offset);
   const size_t nkb = (size_t)pb.NBb * pb.Hkv * kHeadDim;
   w.kbar_split = (__bf16 *)(w.kbar + nkb);
@@ -361,16 +401,24 @@ moba_status_t check_table_stage(const moba_shape_t *sh, int32_t B, const moba_la
   return MOBA_SUCCESS;
 }
 
+// Dense baseline workspace: the block table of 64-row key tiles (the
+// transposed values are laid out per such tile), the table of query tiles
+// (rows per attention workgroup), then the transposed values.
+int64_t dense_nb64(const moba_shape_t *sh) {
+  return ceil_div(sh->total_tokens, kKeyTile) + sh->num_seqs;
+}
+int64_t dense_nbq(const moba_shape_t *sh) {
+  return ceil_div(sh->total_tokens, attn_rows(sh->dtype == MOBA_DTYPE_BF16)) + sh->num_seqs;
+}
 size_t dense_table_bytes(const moba_shape_t *sh) {
-  const int64_t NB64 = ceil_div(sh->total_tokens, kKeyTile) + sh->num_seqs;
-  return align_up(table_bytes(sh->num_seqs, NB64));
+  return align_up(table_bytes(sh->num_seqs, dense_nb64(sh))) +
+         align_up(table_bytes(sh->num_seqs, dense_nbq(sh)));
 }
 
 size_t dense_ws_bytes(const moba_shape_t *sh) {
-  const int64_t NB64 = ceil_div(sh->total_tokens, kKeyTile) + sh->num_seqs;
   const size_t es = sh->dtype == MOBA_DTYPE_BF16 ? 2 : 4;
   return dense_table_bytes(sh) +
-         align_up(es * (size_t)sh->num_kv_heads * NB64 * kHeadDim * kKeyTile);
+         align_up(es * (size_t)sh->num_kv_heads * dense_nb64(sh) * kHeadDim * kKeyTile);
 }
 
 size_t workspace_limit_bytes() {
@@ -441,9 +489,11 @@ void decode_setup(const moba_shape_t *sh, int32_t B, int32_t k, float scale, con
   pb->rows = attn_rows(pb->bf16);
   char *b = (char *)ws;
   *w = Work{};
-  w->blk_first = (int32_t *)(b + D.table);
-  w->cu = (int32_t *)(b + D.table + cu_copy_offset(pb->S));
-  w->blk_info = (int4 *)(b + D.table + info_offset(pb->S));
+  const Table tb = table_at(b + D.table, pb->S);
+  w->blk_first = tb.first;
+  w->cu = tb.cu;
+  w->status = tb.status;
+  w->blk_info = tb.info;
   w->kbar = (float *)(b + D.kbar);
   w->kbar_split = (__bf16 *)(w->kbar + (size_t)D.NBb * pb->Hkv * kHeadDim);
   w->idx = (int32_t *)(b + D.idx);
@@ -466,7 +516,13 @@ const char *moba_status_string(moba_status_t s) {
   return "MOBA_ERROR_UNKNOWN";
 }
 
-const char *moba_last_error(void) { return g_last_error.c_str(); }
+const char *moba_last_error(void) { return g_last_error; }
+
+moba_status_t moba_workspace_status(int32_t num_seqs, const void *workspace, hipStream_t stream) {
+  if (num_seqs < 0) return fail(MOBA_ERROR_INVALID_VALUE, "num_seqs < 0");
+  if (!workspace) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
+  return read_status(table_at(const_cast<void *>(workspace), num_seqs).status, stream);
+}
 
 moba_status_t moba_plan(const moba_shape_t *shape, int32_t block_size, int32_t topk,
                         int32_t kv_heads_per_pass, moba_layout_t *layout) {
@@ -486,10 +542,9 @@ moba_status_t moba_seqtable(const int32_t *cu, const moba_shape_t *sh, int32_t B
   if (st != MOBA_SUCCESS) return st;
   if (sh->num_seqs > 0 && !cu) return fail(MOBA_ERROR_INVALID_VALUE, "cu_seqlens is NULL");
   if (sh->total_tokens == 0) return MOBA_SUCCESS;
-  char *b = (char *)ws + L->table_offset;
-  MOBA_HIP(launch_seqtable(cu, sh->num_seqs, B, L->num_blocks_bound, (int32_t *)b,
-                           (int32_t *)(b + cu_copy_offset(sh->num_seqs)),
-                           (int4 *)(b + info_offset(sh->num_seqs)), s),
+  const Table tb = table_at((char *)ws + L->table_offset, sh->num_seqs);
+  MOBA_HIP(launch_seqtable(cu, sh->num_seqs, B, sh->total_tokens, L->max_blocks_per_seq,
+                           L->num_blocks_bound, tb.first, tb.cu, tb.status, tb.info, s),
            "seqtable");
   return MOBA_SUCCESS;
 }
@@ -667,7 +722,10 @@ moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v, const 
   if (!ws) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
   Problem pb = make_problem(sh, B, topk, scale, &L);
   Work w = carve(pb, &L, ws);
-  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
+  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.T, pb.maxblk, pb.NBb, w.blk_first, w.cu, w.status,
+                           w.blk_info, s),
+           "seqtable");
+  if (check_enabled() && (st = read_status(w.status, s)) != MOBA_SUCCESS) return st;
   if (gate->kind != MOBA_GATE_WINDOW) MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
   if (gate->kind == MOBA_GATE_POOLED) MOBA_HIP(launch_minmaxpool(pb, w, k, s), "minmaxpool");
   for (int g0 = 0; g0 < pb.Hkv; g0 += pb.P)
@@ -725,7 +783,10 @@ moba_status_t moba_bwd(const void *q, const void *k, const void *v, const void *
   Work w = carve(pb, &L, ws);
   const BwdWork bw = carve_bwd(pb, &L, ws, &w);
   const BwdIo io{q, k, v, dout, lse, dq, dk, dv};
-  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
+  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.T, pb.maxblk, pb.NBb, w.blk_first, w.cu, w.status,
+                           w.blk_info, s),
+           "seqtable");
+  if (check_enabled() && (st = read_status(w.status, s)) != MOBA_SUCCESS) return st;
   if (gate->kind != MOBA_GATE_WINDOW) MOBA_HIP(launch_meanpool(pb, w, k, s), "meanpool");
   if (gate->kind == MOBA_GATE_POOLED) MOBA_HIP(launch_minmaxpool(pb, w, k, s), "minmaxpool");
   MOBA_HIP(launch_bwd_delta(pb, out, dout, bw.delta, s), "bwd_delta");
@@ -838,7 +899,10 @@ moba_status_t moba_decode_prepare(const void *k_cache, const int32_t *cu,
   Problem pb;
   Work w;
   decode_setup(sh, B, topk, 0.f, D, ws, &pb, &w);
-  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.NBb, w.blk_first, w.cu, w.blk_info, s), "seqtable");
+  MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.T, pb.maxblk, pb.NBb, w.blk_first, w.cu, w.status,
+                           w.blk_info, s),
+           "seqtable");
+  if (check_enabled() && (st = read_status(w.status, s)) != MOBA_SUCCESS) return st;
   if (sh->total_tokens > 0) MOBA_HIP(launch_meanpool(pb, w, k_cache, s), "meanpool");
   return MOBA_SUCCESS;
 }
@@ -909,20 +973,37 @@ moba_status_t moba_dense_causal_fwd(const void *q, const void *k, const void *v,
   }
   const int S = sh->num_seqs;
   const int64_t T = sh->total_tokens;
-  const int64_t NB64 = ceil_div(T, kKeyTile) + S;
+  const int64_t NB64 = dense_nb64(sh), NBq = dense_nbq(sh);
   const int bf16 = sh->dtype == MOBA_DTYPE_BF16;
-  const int maxlen = (int)(sh->max_seqlen > 0 ? std::min<int64_t>(sh->max_seqlen, T) : T);
-  char *b = (char *)ws;
-  int32_t *first = (int32_t *)b;
-  int4 *info = (int4 *)(b + info_offset(S));
-  void *vt = b + dense_table_bytes(sh);
-  hipError_t e = launch_seqtable(cu, S, kKeyTile, NB64, first, (int32_t *)(b + cu_copy_offset(S)),
-                                 info, s);
+  const int rows = attn_rows(bf16);
+  const Table t64 = table_at(ws, S);
+  const Table tq = table_at((char *)ws + align_up(table_bytes(S, NB64)), S);
+  void *vt = (char *)ws + dense_table_bytes(sh);
+  const int no_bound = 0x7fffffff;  // the grid covers every query tile: no length bound
+  hipError_t e = launch_seqtable(cu, S, kKeyTile, T, no_bound, NB64, t64.first, t64.cu, t64.status,
+                                 t64.info, s);
   if (e == hipSuccess)
-    e = launch_vtrans(v, bf16, T, sh->num_kv_heads, 0, sh->num_kv_heads, NB64, kKeyTile, info, vt, s);
+    e = launch_seqtable(cu, S, rows, T, no_bound, NBq, tq.first, tq.cu, tq.status, tq.info, s);
+  if (e == hipSuccess && check_enabled()) {
+    moba_status_t cst = read_status(t64.status, s);
+    if (cst != MOBA_SUCCESS) {
+      if (own) (void)hipFreeAsync(ws, s);
+      return cst;
+    }
+  }
   if (e == hipSuccess)
-    e = launch_dense(q, k, vt, cu, first, bf16, T, S, maxlen, sh->num_q_heads, sh->num_kv_heads,
-                     NB64, scale > 0.f ? scale : 1.0f / sqrtf((float)kHeadDim), out, lse, s);
+    e = launch_vtrans(v, bf16, T, sh->num_kv_heads, 0, sh->num_kv_heads, NB64, kKeyTile, t64.info,
+                      vt, s);
+  if (e == hipSuccess)
+    e = launch_dense(q, k, vt, t64.first, tq.info, bf16, T, NBq, sh->num_q_heads,
+                     sh->num_kv_heads, NB64, scale > 0.f ? scale : 1.0f / sqrtf((float)kHeadDim),
+                     out, lse, s);
+  // a failed table check leaves every tile out: out and lse become NaN
+  if (e == hipSuccess)
+    e = launch_poison(t64.status, out, T * sh->num_q_heads * kHeadDim / (bf16 ? 2 : 1),
+                      bf16 ? kNanBf16x2 : kNanF32, s);
+  if (e == hipSuccess && lse)
+    e = launch_poison(t64.status, lse, T * sh->num_q_heads, kNanF32, s);
   if (own) {
     hipError_t e2 = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = e2;

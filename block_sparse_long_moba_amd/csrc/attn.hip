@@ -194,9 +194,11 @@ struct AttnArgs {
   // partial outputs (MoBA) or final outputs (dense)
   void *part_o;
   float *part_lse;
-  const int32_t *cu, *blk_first64;
-  int S, nqt;
-  int64_t NBb64;
+  // dense: 64-row key tiles of each sequence (first tile index) and the
+  // query tiles {sequence, first row, rows, tile index in the sequence}
+  const int32_t *blk_first64;
+  const int4 *qtiles;
+  int64_t NBq, NBb64;
   void *out;
   float *lse;
 };
@@ -697,20 +699,18 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     vstep = kKeyTile;
     vstride = a.B;
   } else {  // MODE_DENSE
-    const int qt = a.nqt - 1 - (int)(blockIdx.x / a.S);
-    const int s = blockIdx.x % a.S;
-    const int L = a.cu[s + 1] - a.cu[s];
-    if (qt * ROWS >= L) return;
+    // query tiles from the last (most keys) to the first
+    const int4 bi = a.qtiles[a.NBq - 1 - (int64_t)blockIdx.x];
+    if (bi.x < 0) return;
     hq = blockIdx.y;
     g = hq / a.G;
-    nrows = min(ROWS, L - qt * ROWS);
-    qfirst = qt * ROWS;
+    nrows = bi.z;
+    qfirst = bi.w * ROWS;
     qpos = qfirst + r;
-    t = a.cu[s] + qfirst + (r < nrows ? r : 0);
-    const int kend = min(L, qfirst + ROWS);
-    nkt = (kend + kKeyTile - 1) / kKeyTile;
-    kbeg = a.cu[s];
-    vt0 = (const T *)a.vt + ((int64_t)g * a.NBb64 + a.blk_first64[s]) * kHeadDim * kKeyTile;
+    t = bi.y + (r < nrows ? r : 0);
+    nkt = (qfirst + nrows + kKeyTile - 1) / kKeyTile;  // keys up to the tile's last row
+    kbeg = bi.y - qfirst;                              // the sequence's first row
+    vt0 = (const T *)a.vt + ((int64_t)g * a.NBb64 + a.blk_first64[bi.x]) * kHeadDim * kKeyTile;
     vstep = (int64_t)kHeadDim * kKeyTile;
     vstride = kKeyTile;
   }
@@ -986,21 +986,18 @@ hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, con
   return launch_mode<MODE_HIST>(pb.bf16, dim3((unsigned)grid), a, s);
 }
 
-hipError_t launch_dense(const void *q, const void *k, const void *vt, const int32_t *cu,
-                        const int32_t *blk_first64, int bf16, int64_t T, int S, int maxlen, int Hq,
-                        int Hkv, int64_t NBb64, float scale, void *out, float *lse,
-                        hipStream_t s) {
+hipError_t launch_dense(const void *q, const void *k, const void *vt,
+                        const int32_t *blk_first64, const int4 *qtiles, int bf16, int64_t T,
+                        int64_t NBq, int Hq, int Hkv, int64_t NBb64, float scale, void *out,
+                        float *lse, hipStream_t s) {
   AttnArgs a{};
   a.q = q; a.k = k; a.vt = vt;
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.scale_log2 = scale * kLog2e;
-  a.cu = cu; a.blk_first64 = blk_first64; a.S = S;
-  const int rows = attn_rows(bf16);
-  a.nqt = (maxlen + rows - 1) / rows;
+  a.blk_first64 = blk_first64; a.qtiles = qtiles; a.NBq = NBq;
   a.NBb64 = NBb64;
   a.out = out; a.lse = lse;
-  return launch_mode<MODE_DENSE>(bf16 != 0, dim3((unsigned)((int64_t)S * a.nqt), (unsigned)Hq),
-                                 a, s);
+  return launch_mode<MODE_DENSE>(bf16 != 0, dim3((unsigned)NBq, (unsigned)Hq), a, s);
 }
 
 }  // namespace moba

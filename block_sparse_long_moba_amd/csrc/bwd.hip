@@ -392,12 +392,17 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const float *__restrict
                                                          const int32_t *__restrict__ idx,
                                                          const int32_t *__restrict__ cu, int S,
                                                          int64_t T, int Hq, int h0, int Hp, int B,
-                                                         int k, __bf16 *__restrict__ dq) {
+                                                         int k, const int32_t *__restrict__ status,
+                                                         __bf16 *__restrict__ dq) {
   const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   if (row >= T * Hp) return;
   const int lane = threadIdx.x & 31;
   const int64_t t = row / Hp;
   const int hl = (int)(row % Hp);
+  if (*status != 0) {  // the table check failed: no partial is valid
+    store_bf16x4(dq + (t * Hq + h0 + hl) * kHeadDim + lane * 4, NAN, NAN, NAN, NAN);
+    return;
+  }
   const int s = seq_of(cu, S, t);
   const int c = (int)((t - cu[s]) / B);
   const int nsel = min(k, c + 1);
@@ -964,7 +969,7 @@ hipError_t launch_bwd_dq_sum(const Problem &pb, const Work &w, const BwdWork &bw
   const int64_t rows = pb.T * pb.Hp;
   if (rows == 0) return hipSuccess;
   bwd_dq_sum_kernel<<<dim3((unsigned)((rows + 7) / 8)), 256, 0, s>>>(
-      bw.dq_part, w.idx, w.cu, pb.S, pb.T, pb.Hq, g0 * pb.G, pb.Hp, pb.B, pb.k,
+      bw.dq_part, w.idx, w.cu, pb.S, pb.T, pb.Hq, g0 * pb.G, pb.Hp, pb.B, pb.k, w.status,
       (__bf16 *)io.dq);
   return hipGetLastError();
 }
@@ -983,9 +988,12 @@ hipError_t launch_bwd_dkdv(const Problem &pb, const Work &w, const BwdWork &bw, 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.extra_wg > 0) {
     bwd_dkdv_sum_kernel<<<dim3((unsigned)(a.nbins * nch)), 256, 0, s>>>(a);
-    e = hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return e;
+  // a failed table check leaves every block out: dk and dv become NaN
+  const int64_t words = pb.T * pb.Hkv * kHeadDim / 2;
+  if ((e = launch_poison(w.status, io.dk, words, kNanBf16x2, s)) != hipSuccess) return e;
+  return launch_poison(w.status, io.dv, words, kNanBf16x2, s);
 }
 
 }  // namespace moba

@@ -76,7 +76,9 @@ __global__ __launch_bounds__(256) void decode_gate_kernel(const T *__restrict__ 
                                                           const int32_t *__restrict__ cu,
                                                           const int32_t *__restrict__ blk_first,
                                                           int Hq, int Hkv, int B, int k,
+                                                          const int32_t *__restrict__ status,
                                                           int32_t *__restrict__ idx) {
+  if (*status != 0) return;  // the table check failed: the merge writes NaN
   const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int L = cu[s + 1] - cu[s];
   int32_t *dst = idx + ((int64_t)s * Hq + h) * k;
@@ -172,7 +174,9 @@ template <typename T, int MH>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ idx, int Hq, int Hkv, int B,
-    int k, int ns, float scale_log2, float *__restrict__ part_o, float *__restrict__ part_lse) {
+    int k, int ns, float scale_log2, const int32_t *__restrict__ status,
+    float *__restrict__ part_o, float *__restrict__ part_lse) {
+  if (*status != 0) return;
   const int s = blockIdx.x, g = blockIdx.y, j = blockIdx.z / ns, sp = blockIdx.z % ns;
   const int tid = threadIdx.x;
   const int L = cu[s + 1] - cu[s];
@@ -323,12 +327,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float *__restri
                                                            const float *__restrict__ part_lse,
                                                            const int32_t *__restrict__ cu,
                                                            int S, int Hq, int B, int k, int ns,
+                                                           const int32_t *__restrict__ status,
                                                            T *__restrict__ out,
                                                            float *__restrict__ lse) {
   const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int L = cu[s + 1] - cu[s];
   T *dst = out + ((int64_t)s * Hq + h) * kHeadDim;
+  if (*status != 0) {  // bad cu_seqlens or an understated block bound
+    if (tid < kHeadDim) dst[tid] = (T)NAN;
+    if (tid == 0 && lse) lse[(int64_t)h * S + s] = NAN;
+    return;
+  }
+  const int L = cu[s + 1] - cu[s];
   if (L == 0) {
     if (tid < kHeadDim) dst[tid] = (T)0.f;
     if (tid == 0 && lse) lse[(int64_t)h * S + s] = -INFINITY;
@@ -408,30 +418,30 @@ hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const 
   const float sl2 = pb.scale * kLog2eDec;
   if (pb.bf16) {
     decode_gate_kernel<__bf16><<<gg, 256, 0, s>>>((const __bf16 *)q, w.kbar, w.cu, w.blk_first,
-                                                  pb.Hq, pb.Hkv, pb.B, pb.k, w.idx);
+                                                  pb.Hq, pb.Hkv, pb.B, pb.k, w.status, w.idx);
     if (pb.G <= 4)
       decode_attn_kernel<__bf16, 4><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
                                                        (const __bf16 *)vc, w.cu, w.idx, pb.Hq,
-                                                       pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
+                                                       pb.Hkv, pb.B, pb.k, ns, sl2, w.status, po, w.part_lse);
     else
       decode_attn_kernel<__bf16, 8><<<ga, 256, 0, s>>>((const __bf16 *)q, (const __bf16 *)kc,
                                                        (const __bf16 *)vc, w.cu, w.idx, pb.Hq,
-                                                       pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
+                                                       pb.Hkv, pb.B, pb.k, ns, sl2, w.status, po, w.part_lse);
     decode_merge_kernel<__bf16><<<gg, 256, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
-                                                   ns, (__bf16 *)out, lse);
+                                                   ns, w.status, (__bf16 *)out, lse);
   } else {
     decode_gate_kernel<float><<<gg, 256, 0, s>>>((const float *)q, w.kbar, w.cu, w.blk_first,
-                                                 pb.Hq, pb.Hkv, pb.B, pb.k, w.idx);
+                                                 pb.Hq, pb.Hkv, pb.B, pb.k, w.status, w.idx);
     if (pb.G <= 4)
       decode_attn_kernel<float, 4><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
                                                       (const float *)vc, w.cu, w.idx, pb.Hq,
-                                                      pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
+                                                      pb.Hkv, pb.B, pb.k, ns, sl2, w.status, po, w.part_lse);
     else
       decode_attn_kernel<float, 8><<<ga, 256, 0, s>>>((const float *)q, (const float *)kc,
                                                       (const float *)vc, w.cu, w.idx, pb.Hq,
-                                                      pb.Hkv, pb.B, pb.k, ns, sl2, po, w.part_lse);
+                                                      pb.Hkv, pb.B, pb.k, ns, sl2, w.status, po, w.part_lse);
     decode_merge_kernel<float><<<gg, 256, 0, s>>>(po, w.part_lse, w.cu, pb.S, pb.Hq, pb.B, pb.k,
-                                                  ns, (float *)out, lse);
+                                                  ns, w.status, (float *)out, lse);
   }
   return hipGetLastError();
 }

@@ -339,9 +339,11 @@ hipError_t launch_gate_t(const Problem &pb, const Work &w, const T *q, int g0, h
 // take all of them. Every head gets the same selection.
 __global__ __launch_bounds__(256) void gate_window_kernel(const int32_t *__restrict__ cu, int S,
                                                           int64_t T, int B, int Hp, int k,
-                                                          int n_sink, int32_t *__restrict__ idx) {
+                                                          int n_sink,
+                                                          const int32_t *__restrict__ status,
+                                                          int32_t *__restrict__ idx) {
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (t, hl)
-  if (row >= T * Hp) return;
+  if (row >= T * Hp || *status != 0) return;
   const int64_t t = row / Hp;
   int lo = 0, hi = S - 1;
   while (lo < hi) {
@@ -369,9 +371,10 @@ __global__ __launch_bounds__(256) void gate_window_kernel(const int32_t *__restr
 __global__ __launch_bounds__(256) void gate_union_kernel(
     const int32_t *__restrict__ lm, int km, const int32_t *__restrict__ lx, int kx,
     const int32_t *__restrict__ ln, int kn, const int32_t *__restrict__ cu, int S, int64_t T,
-    int B, int Hp, int k, int32_t *__restrict__ idx, float *__restrict__ part_lse) {
+    int B, int Hp, int k, const int32_t *__restrict__ status, int32_t *__restrict__ idx,
+    float *__restrict__ part_lse) {
   const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (row >= T * Hp) return;
+  if (row >= T * Hp || *status != 0) return;
   const int64_t t = row / Hp;
   int lo = 0, hi = S - 1;
   while (lo < hi) {
@@ -405,7 +408,7 @@ hipError_t launch_gate_window(const Problem &pb, const Work &w, int n_sink, hipS
   const int64_t rows = pb.T * pb.Hp;
   if (rows == 0) return hipSuccess;
   gate_window_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(
-      w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, n_sink, w.idx);
+      w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, n_sink, w.status, w.idx);
   return hipGetLastError();
 }
 
@@ -434,7 +437,7 @@ hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, i
     if (e != hipSuccess) return e;
   }
   gate_union_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(
-      lm, km, lx, kx, ln, kn, w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, w.idx, w.part_lse);
+      lm, km, lx, kx, ln, kn, w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, w.status, w.idx, w.part_lse);
   return hipGetLastError();
 }
 

@@ -20,6 +20,12 @@ constexpr int kMaxHistPick = 32;    // largest topk-1 kept in registers by the g
 constexpr int kWorkCounters = 8;    // one per XCD
 constexpr int kMaxExtraPick = 16;   // pooled gate: extra blocks per max / min ranking
 constexpr int kLdsBins = 16384;     // LDS histogram bins of the dispatch stage (64 KiB)
+// Bits of the status word the sequence-table scan writes (0: input accepted).
+constexpr int kStatusBadSeqlens = 1;     // cu_seqlens[0] != 0, a decrease, or cu_seqlens[S] != T
+constexpr int kStatusTooManyBlocks = 2;  // a sequence exceeds the plan's blocks per sequence
+// 32-bit fill patterns of NaN outputs
+constexpr uint32_t kNanF32 = 0x7fc00000u;
+constexpr uint32_t kNanBf16x2 = 0x7fc07fc0u;
 
 // Everything a launcher needs to know about one call.
 struct Problem {
@@ -40,6 +46,7 @@ struct Problem {
 struct Work {
   int32_t *blk_first;   // [S+1]
   int32_t *cu;          // [S+1] copy of cu_seqlens
+  int32_t *status;      // input check of the sequence table (kStatus* bits)
   int4 *blk_info;       // [NBb] {seq, first row, rows, local block}
   float *kbar;          // [NBb][Hkv][d]
   __bf16 *kbar_split;   // [NBb][Hkv][2][d]: bf16 hi and lo parts, kbar ~= hi + lo
@@ -61,8 +68,14 @@ struct Work {
 
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);
-hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t NBb, int32_t *blk_first,
-                           int32_t *cu_copy, int4 *blk_info, hipStream_t s);
+// Block table of cu_seqlens for block size B; max_blocks bounds the blocks of
+// any sequence (a larger count sets kStatusTooManyBlocks).
+hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t T, int max_blocks,
+                           int64_t NBb, int32_t *blk_first, int32_t *cu_copy, int32_t *status,
+                           int4 *blk_info, hipStream_t s);
+// Fills `words` 32-bit words at p with pattern if *status != 0.
+hipError_t launch_poison(const int32_t *status, void *p, int64_t words, uint32_t pattern,
+                         hipStream_t s);
 hipError_t launch_meanpool(const Problem &pb, const Work &w, const void *k, hipStream_t s);
 hipError_t launch_minmaxpool(const Problem &pb, const Work &w, const void *k, hipStream_t s);
 hipError_t launch_gate(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s);
@@ -81,9 +94,12 @@ hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, flo
 int decode_splits(int S, int Hq, int Hkv, int B, int k, int maxblk);
 hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const void *kc,
                          const void *vc, void *out, float *lse, hipStream_t s);
-hipError_t launch_dense(const void *q, const void *k, const void *vt, const int32_t *cu,
-                        const int32_t *blk_first64, int bf16, int64_t T, int S, int maxlen,
-                        int Hq, int Hkv, int64_t NBb64, float scale, void *out, float *lse,
-                        hipStream_t s);
+// Dense causal attention: one workgroup per (query tile, query head); qtiles is
+// the block table of the query tiles (attn_rows(bf16) rows), blk_first64 the
+// first 64-row key tile of each sequence in vt.
+hipError_t launch_dense(const void *q, const void *k, const void *vt,
+                        const int32_t *blk_first64, const int4 *qtiles, int bf16, int64_t T,
+                        int64_t NBq, int Hq, int Hkv, int64_t NBb64, float scale, void *out,
+                        float *lse, hipStream_t s);
 
 }  // namespace moba

@@ -2,6 +2,8 @@
 // the log-sum-exp merge of partial outputs.
 #include <math.h>
 
+#include <algorithm>
+
 #include "moba_internal.h"
 
 namespace moba {
@@ -42,18 +44,32 @@ __device__ int block_scan_incl_1024(int x, int *wsum) {
 // blk_first[s] = sum over earlier sequences of ceil(L/B) ("Context
 // Partitioning" of the MoBA summary page, section 3.4: blocks restart in every
 // sequence, the last one may be short). One workgroup of 1024 threads.
-// Also keeps a copy of cu_seqlens next to the table for later stages.
+// Also keeps a copy of cu_seqlens next to the table for later stages, and
+// checks what the host could not: cu_seqlens must start at 0, never decrease
+// and end at T, and no sequence may have more than max_blocks blocks (the
+// bound the workspace plan and the launch shapes were sized for). A failed
+// check sets the status word; the fill kernel then marks every block invalid,
+// so that no later kernel reads rows through the table.
 __global__ __launch_bounds__(1024) void seqtable_scan_kernel(const int32_t *cu, int S, int B,
+                                                             int64_t T, int max_blocks,
                                                              int32_t *blk_first,
-                                                             int32_t *cu_copy) {
+                                                             int32_t *cu_copy,
+                                                             int32_t *status) {
   __shared__ int wsum[16];
   __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
+  __shared__ int flags;
+  if (threadIdx.x == 0) { carry = 0; flags = 0; }
   __syncthreads();
+  int bad = 0;
   for (int base = 0; base < S; base += 1024) {
     int s = base + threadIdx.x;
     int v = 0;
-    if (s < S) v = (cu[s + 1] - cu[s] + B - 1) / B;
+    if (s < S) {
+      const int L = cu[s + 1] - cu[s];
+      if (L < 0) bad |= kStatusBadSeqlens;
+      v = L > 0 ? (L + B - 1) / B : 0;
+      if (v > max_blocks) bad |= kStatusTooManyBlocks;
+    }
     if (s <= S) cu_copy[s] = cu[s];
     int incl = block_scan_incl_1024(v, wsum) + carry;
     if (s < S) blk_first[s] = incl - v;
@@ -61,19 +77,26 @@ __global__ __launch_bounds__(1024) void seqtable_scan_kernel(const int32_t *cu, 
     if (threadIdx.x == 1023) carry = incl;
     __syncthreads();
   }
+  if (bad) atomicOr(&flags, bad);
+  __syncthreads();
   if (threadIdx.x == 0) {
     blk_first[S] = carry;
     cu_copy[S] = cu[S];
+    int f = flags;
+    if (cu[0] != 0 || (int64_t)cu[S] != T) f |= kStatusBadSeqlens;
+    *status = f;
   }
 }
 
-// blk_info[gb] = {sequence, first row, rows, local block index}; -1 past the end.
+// blk_info[gb] = {sequence, first row, rows, local block index}; -1 past the
+// end, and for every block when the status word reports bad input.
 __global__ __launch_bounds__(256) void seqtable_fill_kernel(const int32_t *cu,
                                                             const int32_t *blk_first, int S,
-                                                            int B, int64_t NBb, int4 *info) {
+                                                            int B, int64_t NBb,
+                                                            const int32_t *status, int4 *info) {
   int64_t gb = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gb >= NBb) return;
-  if (gb >= blk_first[S]) {
+  if (*status != 0 || gb >= blk_first[S]) {
     info[gb] = make_int4(-1, 0, 0, 0);
     return;
   }
@@ -86,6 +109,17 @@ __global__ __launch_bounds__(256) void seqtable_fill_kernel(const int32_t *cu,
   int len = cu[lo + 1] - cu[lo];
   int rows = min(B, len - j * B);
   info[gb] = make_int4(lo, cu[lo] + j * B, rows, j);
+}
+
+// Fills n 32-bit words with `pattern` when the status word reports bad input
+// (outputs of a call whose table check failed become NaN instead of stale
+// memory); otherwise every workgroup returns at once.
+__global__ __launch_bounds__(256) void poison_kernel(const int32_t *status, uint32_t *p, int64_t n,
+                                                     uint32_t pattern) {
+  if (*status == 0) return;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * 256)
+    p[i] = pattern;
 }
 
 template <typename T> struct Vec16;
@@ -279,7 +313,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
                                                     const float *__restrict__ part_lse,
                                                     const int32_t *__restrict__ cu, int S,
                                                     int64_t T_, int Hq, int h0, int Hp, int B,
-                                                    int k, TO *__restrict__ out,
+                                                    int k, const int32_t *__restrict__ status,
+                                                    TO *__restrict__ out,
                                                     float *__restrict__ lse_out) {
   constexpr int N = 16 / sizeof(TO);       // elements per thread
   constexpr int LANES = kHeadDim / N;      // threads per row: 16 (bf16) or 32 (fp32)
@@ -289,6 +324,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
   const int lane = threadIdx.x % LANES;
   const int64_t t = row / Hp;
   const int hl = (int)(row % Hp);
+  if (*status != 0) {  // bad cu_seqlens or block bound: no partial is valid
+    TO nan[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) nan[j] = (TO)NAN;
+    *(uint4 *)(out + (t * Hq + h0 + hl) * kHeadDim + lane * N) = *(const uint4 *)nan;
+    if (lane == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = NAN;
+    return;
+  }
   const int s = seq_of_row(cu, S, t);
   const int c = (int)((t - cu[s]) / B);
   const int nsel = min(k, c + 1);
@@ -350,13 +393,22 @@ hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t NBb, int32_t *blk_first,
-                           int32_t *cu_copy, int4 *blk_info, hipStream_t s) {
-  seqtable_scan_kernel<<<1, 1024, 0, s>>>(cu, S, B, blk_first, cu_copy);
+hipError_t launch_seqtable(const int32_t *cu, int S, int B, int64_t T, int max_blocks,
+                           int64_t NBb, int32_t *blk_first, int32_t *cu_copy, int32_t *status,
+                           int4 *blk_info, hipStream_t s) {
+  seqtable_scan_kernel<<<1, 1024, 0, s>>>(cu, S, B, T, max_blocks, blk_first, cu_copy, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  seqtable_fill_kernel<<<dim3((unsigned)((NBb + 255) / 256)), dim3(256), 0, s>>>(cu, blk_first, S,
-                                                                                 B, NBb, blk_info);
+  seqtable_fill_kernel<<<dim3((unsigned)((NBb + 255) / 256)), dim3(256), 0, s>>>(
+      cu, blk_first, S, B, NBb, status, blk_info);
+  return hipGetLastError();
+}
+
+hipError_t launch_poison(const int32_t *status, void *p, int64_t words, uint32_t pattern,
+                         hipStream_t s) {
+  if (words <= 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((words + 255) / 256, 1024);
+  poison_kernel<<<dim3((unsigned)grid), dim3(256), 0, s>>>(status, (uint32_t *)p, words, pattern);
   return hipGetLastError();
 }
 
@@ -404,10 +456,10 @@ hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, flo
   const int h0 = g0 * pb.G;
   if (pb.bf16)
     merge_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
-                                              pb.Hp, pb.B, pb.k, (__bf16 *)out, lse);
+                                              pb.Hp, pb.B, pb.k, w.status, (__bf16 *)out, lse);
   else
     merge_kernel<float><<<grid, 256, 0, s>>>((const float *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
-                                             pb.Hp, pb.B, pb.k, (float *)out, lse);
+                                             pb.Hp, pb.B, pb.k, w.status, (float *)out, lse);
   return hipGetLastError();
 }
 

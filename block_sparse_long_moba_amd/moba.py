@@ -18,7 +18,8 @@ STATUS = {0: "MOBA_SUCCESS", 1: "MOBA_ERROR_INVALID_VALUE", 2: "MOBA_ERROR_UNSUP
           3: "MOBA_ERROR_WORKSPACE_TOO_SMALL", 4: "MOBA_ERROR_HIP"}
 
 # Every entry point include/moba.h declares.
-EXPORTS = ["moba_status_string", "moba_last_error", "moba_plan", "moba_fwd_workspace_size",
+EXPORTS = ["moba_status_string", "moba_last_error", "moba_workspace_status", "moba_plan",
+           "moba_fwd_workspace_size",
            "moba_seqtable", "moba_meanpool", "moba_gate", "moba_minmaxpool", "moba_gate_window",
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
            "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
@@ -88,6 +89,7 @@ def lib():
         sig = {
             "moba_status_string": ([I32], ctypes.c_char_p),
             "moba_last_error": ([], ctypes.c_char_p),
+            "moba_workspace_status": ([I32, P, P], I32),
             "moba_plan": ([S, I32, I32, I32, LP], I32),
             "moba_fwd_workspace_size": ([S, I32, I32, I32], Z),
             "moba_seqtable": ([P, S, I32, LP, P, P], I32),
@@ -153,6 +155,12 @@ def shape_of(q, k, cu_seqlens, max_seqlen=0) -> Shape:
     T, Hq, d = q.shape
     dt = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}[q.dtype]
     return Shape(T, cu_seqlens.numel() - 1, int(max_seqlen), Hq, k.shape[1], d, dt)
+
+
+def moba_workspace_status(num_seqs, workspace, stream=None):
+    """Raises MobaError if the device-side input check of the last call that
+    built a block table in `workspace` failed (synchronises the stream)."""
+    _check(lib().moba_workspace_status(int(num_seqs), _ptr(workspace), _stream(stream)))
 
 
 def moba_plan(shape: Shape, block_size: int, topk: int, kv_heads_per_pass: int = 0) -> Layout:

@@ -48,6 +48,22 @@
  * describes the problem. A failed launch returns MOBA_ERROR_HIP. Faults inside
  * kernels surface at the caller's next synchronisation.
  *
+ * Device-side input check: what lives only in device memory is checked by the
+ * first kernel, which builds the block table: cu_seqlens must start at 0,
+ * never decrease and end at total_tokens, and no sequence may be longer than
+ * the shape's max_seqlen hint allows (the hint sizes the workspace plan, the
+ * gate's index width and the dispatch and decode launches; understating it is
+ * a contract violation). When the check fails, the table marks every block
+ * invalid, no kernel reads rows through it, and the outputs of the call (out
+ * and lse; dq, dk and dv; the decode outputs) are set to NaN, so a bad call
+ * never returns stale or partial numbers. Such a call still returns
+ * MOBA_SUCCESS, since nothing was synchronised; moba_workspace_status()
+ * reports the failure afterwards, and with the environment variable
+ * MOBA_CHECK=1 the whole-pass entry points (moba_fwd, moba_fwd_ex,
+ * moba_fwd_gated, moba_bwd, moba_decode_prepare, moba_dense_causal_fwd)
+ * synchronise the stream once right after the check and return
+ * MOBA_ERROR_INVALID_VALUE without launching anything further.
+ *
  * Limits of the GPU path: head_dim == 128; block_size a positive multiple of
  * 64; T < 2^31 and T*Hq*topk < 2^32; topk <= 33 unless topk is at least the
  * number of blocks of the longest sequence (then every earlier block is
@@ -83,7 +99,9 @@ typedef enum moba_dtype {
 typedef struct moba_shape {
   int64_t total_tokens;   /* T, rows of q/k/v/out */
   int32_t num_seqs;       /* S, cu_seqlens holds S+1 entries */
-  int32_t max_seqlen;     /* host-known upper bound on any sequence length, 0 = unknown (T) */
+  int32_t max_seqlen;     /* host-known upper bound on any sequence length, 0 = unknown (T);
+                           * a sequence longer than this bound allows (in blocks) fails the
+                           * device-side input check */
   int32_t num_q_heads;    /* Hq */
   int32_t num_kv_heads;   /* Hkv, divides Hq */
   int32_t head_dim;       /* d, 128 on the GPU path */
@@ -126,9 +144,13 @@ typedef struct moba_layout {
   int32_t max_blocks_per_seq; /* ceil(max_seqlen / block_size) */
   int32_t reserved;
   /* int32 blk_first[S+1] (first global block of each sequence), int32 copy
-   * of cu_seqlens[S+1], then (16-byte aligned) int32 blk_info[NBb][4] =
-   * {sequence, first row, rows, local block index} (sequence = -1 for
-   * indices past the last block). Written by moba_seqtable. */
+   * of cu_seqlens[S+1], int32 status (0, or the failed device-side input
+   * check: 1 = malformed cu_seqlens, 2 = a sequence with more than
+   * max_blocks_per_seq blocks), then (16-byte aligned) int32
+   * blk_info[NBb][4] = {sequence, first row, rows, local block index}
+   * (sequence = -1 for indices past the last block, and for every index
+   * when status != 0). Written by moba_seqtable. table_offset is 0 in every
+   * plan. */
   size_t table_offset;
   /* float32 kbar[NBb][Hkv][d]: mean-pooled keys of every block, followed by
    * bf16 kbar_split[NBb][Hkv][2][d]: hi = bf16(kbar), lo = bf16(kbar - hi);
@@ -168,6 +190,14 @@ const char *moba_status_string(moba_status_t status);
 /* Message describing the last non-success status returned on this thread. */
 const char *moba_last_error(void);
 
+/* Result of the device-side input check (see "Device-side input check"
+ * above) of the last call that built a block table in `workspace` (any
+ * forward, backward, decode or dense-baseline workspace: the table sits at
+ * its start); num_seqs is that call's S. Synchronises `stream`, then returns
+ * MOBA_SUCCESS, or MOBA_ERROR_INVALID_VALUE with moba_last_error() naming the
+ * failed check. */
+moba_status_t moba_workspace_status(int32_t num_seqs, const void *workspace, hipStream_t stream);
+
 /* Host only. Checks the shape and fills *layout for a pass size of
  * kv_heads_per_pass kv heads (0 = all of them, values are clamped to
  * [1, Hkv]; the pass may be lowered further to fit the dispatch stage's LDS
@@ -186,7 +216,8 @@ size_t moba_fwd_workspace_size(const moba_shape_t *shape, int32_t block_size, in
  * kv_head_begin selects the pass: kv heads [kv_head_begin, kv_head_begin+P)
  * (clipped to Hkv) and their query heads. */
 
-/* Block table from the device cu_seqlens ("Context Partitioning"). */
+/* Block table from the device cu_seqlens ("Context Partitioning"), with the
+ * device-side input check against the layout's max_blocks_per_seq. */
 moba_status_t moba_seqtable(const int32_t *cu_seqlens, const moba_shape_t *shape,
                             int32_t block_size, const moba_layout_t *layout, void *workspace,
                             hipStream_t stream);

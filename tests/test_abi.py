@@ -119,6 +119,15 @@ def test_empty_problem_is_a_no_op():
                                    None, 0, None) == 0
 
 
+def test_workspace_status_rejects_bad_arguments_without_a_device():
+    L = moba.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert L.moba_workspace_status(2, None, None) == 1
+    assert "workspace" in L.moba_last_error().decode()
+    assert L.moba_workspace_status(-1, fake, None) == 1
+    assert "num_seqs" in L.moba_last_error().decode()
+
+
 def test_status_strings():
     L = moba.lib()
     for code, name in moba.STATUS.items():
