@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoba.so")
 PROBE_LIB = os.path.join(HERE, "libmoba_probe.so")  # the benchmark's MFMA-rate probe
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "prep.hip", "gate.hip", "dispatch.hip", "attn.hip", "decode.hip", "bwd.hip"]
+SOURCES = ["api.hip", "prep.hip", "gate.hip", "dispatch.hip", "attn.hip", "decode.hip", "bwd.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

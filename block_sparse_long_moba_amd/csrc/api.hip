@@ -503,6 +503,10 @@ void decode_setup(const moba_shape_t *sh, int32_t B, int32_t k, float scale, con
 
 }  // namespace
 
+namespace moba {
+moba_status_t report_error(moba_status_t st, const char *msg) { return fail(st, "%s", msg); }
+}  // namespace moba
+
 extern "C" {
 
 const char *moba_status_string(moba_status_t s) {

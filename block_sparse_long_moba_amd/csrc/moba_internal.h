@@ -66,6 +66,9 @@ struct Work {
   int64_t max_tiles;
 };
 
+// Sets this thread's moba_last_error() message and returns st.
+moba_status_t report_error(moba_status_t st, const char *msg);
+
 // Launchers (enqueue only; return the launch status).
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s);
 // Block table of cu_seqlens for block size B; max_blocks bounds the blocks of

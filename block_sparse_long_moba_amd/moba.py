@@ -23,6 +23,7 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_workspace_status", "mo
            "moba_seqtable", "moba_meanpool", "moba_gate", "moba_minmaxpool", "moba_gate_window",
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
            "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
+           "moba_fwd_noalloc",
            "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
            "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd", "moba_bwd_delta",
            "moba_attn_bwd_dq", "moba_attn_bwd_dq_sum", "moba_attn_bwd_dkdv",
@@ -107,6 +108,7 @@ def lib():
             "moba_fwd_gated": ([P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, Z,
                                 P], I32),
             "moba_fwd": ([P, P, P, P, S, I32, I32, P, P, P], I32),
+            "moba_fwd_noalloc": ([P, P, P, P, S, I32, I32, F, P, P, P], I32),
             "moba_decode_workspace_size": ([S, I32, I32], Z),
             "moba_decode_prepare": ([P, P, S, I32, I32, P, Z, P], I32),
             "moba_decode": ([P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
@@ -258,6 +260,21 @@ def moba_fwd(q, k, v, cu_seqlens, block_size, topk, out=None, lse=None, max_seql
     sh = shape_of(q, k, cu_seqlens, max_seqlen)
     _check(lib().moba_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
                           block_size, topk, _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+NOALLOC_WORKSPACE_BYTES = 256 << 20  # MOBA_NOALLOC_WORKSPACE_BYTES of include/moba.h
+
+
+def moba_fwd_noalloc(q, k, v, cu_seqlens, block_size, topk, out=None, lse=None,
+                     softmax_scale=0.0, max_seqlen=0, stream=None):
+    """MoBA forward pass on the library's static workspace (no allocation in
+    the library; out and lse are allocated here only when not given)."""
+    out, lse = _outputs(q, out, lse)
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    _check(lib().moba_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
+                                  block_size, topk, softmax_scale, _ptr(out), _ptr(lse),
+                                  _stream(stream)))
     return out, lse
 
 

@@ -322,6 +322,25 @@ moba_status_t moba_fwd(const void *q, const void *k, const void *v, const int32_
                        const moba_shape_t *shape, int32_t block_size, int32_t topk, void *out,
                        float *lse, hipStream_t stream);
 
+/* ---- Forward pass without allocation, for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same as moba_fwd_ex, on a workspace the library owns: a static
+ * device array of MOBA_NOALLOC_WORKSPACE_BYTES that each GPU the library runs
+ * on holds until the process ends (its device address is looked up on the
+ * first call on each device). Calls no hipMalloc, hipFree or other
+ * allocating routine. Shapes whose workspace with one kv head per pass
+ * exceeds the array return MOBA_ERROR_UNSUPPORTED (moba_fwd_workspace_size
+ * with kv_heads_per_pass = 1 gives that size); otherwise the largest pass
+ * that fits is used. Every call on a GPU shares that GPU's array (the kernels
+ * clear what must start at zero), so calls that overlap on one GPU -- on
+ * different streams or from different threads -- race and must be ordered by
+ * the caller. */
+#define MOBA_NOALLOC_WORKSPACE_BYTES ((size_t)256 << 20)
+moba_status_t moba_fwd_noalloc(const void *q, const void *k, const void *v,
+                               const int32_t *cu_seqlens, const moba_shape_t *shape,
+                               int32_t block_size, int32_t topk, float softmax_scale, void *out,
+                               float *lse, hipStream_t stream);
+
 /* ---- Decode: one new query per sequence over its KV cache (section 3.4's
  * gate and block attention applied to a single query; the review page's
  * GSM-Infinite table reports MoBA used for both prefill and decode).

@@ -128,6 +128,13 @@ def test_workspace_status_rejects_bad_arguments_without_a_device():
     assert "num_seqs" in L.moba_last_error().decode()
 
 
+def test_noalloc_capacity_matches_the_header():
+    import re
+    hdr = open(os.path.join(ROOT, "include", "moba.h")).read()
+    m = re.search(r"#define MOBA_NOALLOC_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == moba.NOALLOC_WORKSPACE_BYTES
+
+
 def test_status_strings():
     L = moba.lib()
     for code, name in moba.STATUS.items():
