@@ -37,7 +37,7 @@ HEAD_DIM = 128
 # workload: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one counter
 # per pass, averaged over the launches of one step), each scaled by the factor
 # between the true bytes of a plain copy kernel and the same counter's reading
-# for it (block_sparse_long_moba_amd/hbm_copy.py). It describes the kernel
+# for it (bench_support/hbm_copy.py). It describes the kernel
 # sources whose SHA-256 is given; for any other sources traffic is reported as
 # null until it is measured again.
 MEASURED_TRAFFIC = {
@@ -626,7 +626,7 @@ def measured_ceilings(torch):
     gemm_ms = best_ms(lambda: torch.mm(a, b), 5)
     del a, b
     # pure MFMA loop (libmoba_probe.so): 8 waves per CU, 4 independent chains
-    probe = ctypes.CDLL(os.path.join(ROOT, "block_sparse_long_moba_amd", "libmoba_probe.so"))
+    probe = ctypes.CDLL(os.path.join(ROOT, "bench_support", "libmoba_probe.so"))
     probe.moba_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p]
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count

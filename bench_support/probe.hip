@@ -2,7 +2,8 @@
 // wave runs rounds of four independent v_mfma_f32_32x32x16_bf16 chains with
 // no memory traffic in the loop, so the rate it reaches is what the matrix
 // cores deliver at the clock they hold under sustained MFMA load. Built into
-// its own library (libmoba_probe.so); nothing on the MoBA path uses it.
+// its own library (bench_support/libmoba_probe.so); nothing on the MoBA path
+// uses it.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>

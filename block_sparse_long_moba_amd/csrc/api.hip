@@ -192,7 +192,7 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
 
 // Backward plan: the forward plan up to the items, then fp32 partial dq per
 // slot (in place of the partial outputs) and D per (head, row) (in place of
-// their lse). The vt region holds K^T.
+// their lse). The vt region is unused.
 moba_status_t bwd_plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_req,
                             moba_layout_t *L) {
   moba_status_t st = plan_impl(sh, B, k, P_req, L);

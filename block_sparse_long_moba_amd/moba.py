@@ -11,7 +11,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoba.so")
+# MOBA_LIBRARY names another build of the same library (e.g. the sanitizer build)
+LIB_PATH = os.environ.get("MOBA_LIBRARY") or os.path.join(HERE, "libmoba.so")
 
 DTYPE_FP32, DTYPE_BF16 = 0, 1
 STATUS = {0: "MOBA_SUCCESS", 1: "MOBA_ERROR_INVALID_VALUE", 2: "MOBA_ERROR_UNSUPPORTED",

@@ -105,7 +105,9 @@ typedef struct moba_shape {
   int32_t num_q_heads;    /* Hq */
   int32_t num_kv_heads;   /* Hkv, divides Hq */
   int32_t head_dim;       /* d, 128 on the GPU path */
-  moba_dtype_t dtype;     /* element type of q, k, v and out */
+  int32_t dtype;          /* element type of q, k, v and out: a moba_dtype_t value (an
+                           * integer field, so that any value a caller passes can be
+                           * checked) */
 } moba_shape_t;
 
 /* Workspace plan: byte offsets of every intermediate inside one workspace.
@@ -129,7 +131,8 @@ typedef enum {
 } moba_gate_kind_t;
 
 typedef struct moba_gate {
-  moba_gate_kind_t kind;
+  int32_t kind;       /* a moba_gate_kind_t value (an integer field, so that any value a
+                       * caller passes can be checked) */
   int32_t n_sink;     /* WINDOW: initial blocks always kept, 0 <= n_sink < topk */
   int32_t extra_max;  /* POOLED: extra blocks by max-pooled keys, 0..16 */
   int32_t extra_min;  /* POOLED: extra blocks by min-pooled keys, 0..16;

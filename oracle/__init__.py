@@ -20,12 +20,30 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moba_oracle.c")
-_LIB = os.path.join(_HERE, "libmoba_oracle.so")
+# MOBA_ORACLE_LIBRARY names a prebuilt copy (the sanitizer build); it is loaded as is
+_PREBUILT = os.environ.get("MOBA_ORACLE_LIBRARY")
+_LIB = _PREBUILT or os.path.join(_HERE, "libmoba_oracle.so")
 _lib = None
+
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    """The oracle with AddressSanitizer and UndefinedBehaviorSanitizer (clang,
+    the runtime the sanitized HIP library uses), into out_dir."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "libmoba_oracle.so")
+    subprocess.check_call(["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp",
+                           "-fPIC", "-shared", "-Wall", "-Wextra"] + SANITIZE_FLAGS +
+                          ["-o", lib, _SRC, "-lm"])
+    return lib
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if _PREBUILT:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",

@@ -163,7 +163,7 @@ void oracle_select(const void *q, int is_bf16, const double *kbar, int64_t T,
         for (int j = 0; j < max_blocks; ++j) dst[j] = NAN;
         for (int j = 0; j < c && j < max_blocks; ++j) dst[j] = cand[j].s;
       }
-      qsort(cand, (size_t)c, sizeof(cand_t), cand_cmp);
+      if (c > 0) qsort(cand, (size_t)c, sizeof(cand_t), cand_cmp);  /* no candidates: nothing to sort */
       int n_hist = topk - 1 < c ? topk - 1 : c;  /* the current block takes one of the k */
       uint8_t flag = 0;
       if (topk - 1 >= 1 && c > topk - 1) {
@@ -256,7 +256,7 @@ static int rank_blocks(const void *q, int is_bf16, const double *pool, int64_t t
     cand[j].s = acc;
     cand[j].j = j;
   }
-  qsort(cand, (size_t)c, sizeof(cand_t), cand_cmp);
+  if (c > 0) qsort(cand, (size_t)c, sizeof(cand_t), cand_cmp);
   if (pick < 1 || c <= pick) return 0;
   double a = cand[pick - 1].s, b = cand[pick].s;
   double m = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
