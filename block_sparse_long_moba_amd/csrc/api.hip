@@ -128,13 +128,19 @@ bool check_enabled() {
 }
 
 // Bins region: count[nbins], offset[nbins+1], tile_offset[nbins+1],
-// cursor[nbins], work counters[kWorkCounters] (uint32), then (16-byte
-// aligned) int4 tile records.
+// cursor[nbins], work counters[kWorkCounters], the counted flag (uint32),
+// then (16-byte aligned) int4 tile records.
 size_t tile_rec_offset(int64_t nbins) {
-  return (sizeof(uint32_t) * (size_t)(4 * nbins + 2 + kWorkCounters) + 15) / 16 * 16;
+  return (sizeof(uint32_t) * (size_t)(4 * nbins + 2 + kWorkCounters + 1) + 15) / 16 * 16;
 }
 size_t bins_bytes(int64_t nbins, int64_t max_tiles) {
   return tile_rec_offset(nbins) + 16 * (size_t)max_tiles;
+}
+
+// The vt region: transposed values, then (256-byte aligned) the largest key
+// norm of every block.
+size_t vt_bytes(size_t es, int P, int64_t NBb, int B) {
+  return align_up(es * (size_t)P * NBb * kHeadDim * B);
 }
 
 int largest_divisor_at_most(int n, int cap) {
@@ -180,7 +186,8 @@ moba_status_t plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_t P_
   size_t off = 0;
   L->table_offset = off;     off = align_up(off + table_bytes(S, NBb));
   L->kbar_offset = off;      off = align_up(off + 3 * (sizeof(float) + 4) * (size_t)NBb * Hkv * kHeadDim);
-  L->vt_offset = off;        off = align_up(off + es * (size_t)P * NBb * kHeadDim * B);
+  L->vt_offset = off;        off = align_up(off + vt_bytes(es, P, NBb, B) +
+                                            sizeof(float) * (size_t)P * NBb);
   L->idx_offset = off;       off = align_up(off + sizeof(int32_t) * (size_t)slots);
   L->bins_offset = off;      off = align_up(off + bins_bytes(nbins, max_tiles));
   L->items_offset = off;     off = align_up(off + sizeof(uint32_t) * (size_t)std::max<int64_t>(1, hist_items));
@@ -227,6 +234,11 @@ Problem make_problem(const moba_shape_t *sh, int32_t B, int32_t k, float scale,
   pb.Hp = L->q_heads_per_pass;
   pb.maxblk = L->max_blocks_per_seq;
   pb.rows = attn_rows(pb.bf16);
+  // contiguous [T][H][d] tensors
+  pb.qs = RowHead{(int64_t)pb.Hq * kHeadDim, kHeadDim};
+  pb.ks = RowHead{(int64_t)pb.Hkv * kHeadDim, kHeadDim};
+  pb.vs = pb.ks;
+  pb.os = pb.qs;
   return pb;
 }
 
@@ -246,6 +258,7 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.kmin = (float *)(w.kmax_split + 2 * nkb);
   w.kmin_split = (__bf16 *)(w.kmin + nkb);
   w.vt = b + L->vt_offset;
+  w.knorm = (float *)(b + L->vt_offset + vt_bytes(pb.bf16 ? 2 : 4, pb.P, pb.NBb, pb.B));
   w.idx = (int32_t *)(b + L->idx_offset);
   const int64_t nbins = (int64_t)pb.P * pb.NBb;
   uint32_t *bins = (uint32_t *)(b + L->bins_offset);
@@ -254,6 +267,7 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.tile_off = bins + 2 * nbins + 1;
   w.cursor = bins + 3 * nbins + 2;
   w.work = bins + 4 * nbins + 2;
+  w.counted = w.work + kWorkCounters;
   w.tile_rec = (int4 *)((char *)bins + tile_rec_offset(nbins));
   w.items = (uint32_t *)(b + L->items_offset);
   w.part_o = b + L->part_o_offset;
@@ -348,7 +362,8 @@ moba_status_t run_pass(const Problem &pb, const Work &w, const void *q, const vo
   else
     MOBA_HIP(launch_gate(pb, w, q, g0, s), "gate");
   MOBA_HIP(launch_dispatch(pb, w, s), "dispatch");
-  MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+  MOBA_HIP(launch_vtrans(v, pb.vs, k, pb.ks, pb.bf16, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt,
+                         w.knorm, s),
            "vtrans");
   MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
   MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
@@ -383,6 +398,40 @@ moba_status_t check_io(const void *q, const void *k, const void *v, const int32_
   if (sh->total_tokens > 0 && (!q || !k || !v || !out))
     return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v and out must be non-NULL");
   if (sh->num_seqs > 0 && !cu) return fail(MOBA_ERROR_INVALID_VALUE, "cu_seqlens is NULL");
+  // every head row is read and written in 16-byte vectors
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
+    return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v and out must be 16-byte aligned");
+  return MOBA_SUCCESS;
+}
+
+// Strides of the whole forward pass (elements): positive multiples of 16
+// bytes, so every head row stays 16-byte aligned; out's (row, head) vectors
+// must not overlap; one block of key rows must span less than 2 GiB, since
+// the attention kernels address a block's keys with 32-bit byte offsets.
+moba_status_t check_strides(const moba_shape_t *sh, int32_t B, const moba_strides_t *st) {
+  const int64_t es = sh->dtype == MOBA_DTYPE_BF16 ? 2 : 4, unit = 16 / es;
+  const struct { const char *name; int64_t t, h; } all[4] = {
+      {"q", st->q_token, st->q_head}, {"k", st->k_token, st->k_head},
+      {"v", st->v_token, st->v_head}, {"out", st->out_token, st->out_head}};
+  for (const auto &x : all) {
+    if (x.t <= 0 || x.h <= 0 || x.t % unit || x.h % unit)
+      return fail(MOBA_ERROR_INVALID_VALUE,
+                  "%s strides (%lld, %lld): must be positive multiples of %lld elements", x.name,
+                  (long long)x.t, (long long)x.h, (long long)unit);
+  }
+  if (st->k_token * es * B > INT32_MAX)
+    return fail(MOBA_ERROR_UNSUPPORTED, "k token stride %lld: a block of %d rows spans 2 GiB or more",
+                (long long)st->k_token, B);
+  // out: the smaller stride must step over a whole head row, the larger one
+  // over all vectors of the smaller
+  int64_t s1 = st->out_head, n1 = sh->num_q_heads, s2 = st->out_token, n2 = sh->total_tokens;
+  if (s1 > s2) {
+    std::swap(s1, s2);
+    std::swap(n1, n2);
+  }
+  if ((n1 > 1 && s1 < kHeadDim) || (n2 > 1 && s2 < (n1 - 1) * s1 + kHeadDim))
+    return fail(MOBA_ERROR_INVALID_VALUE, "out strides (%lld, %lld): rows overlap",
+                (long long)st->out_token, (long long)st->out_head);
   return MOBA_SUCCESS;
 }
 
@@ -417,8 +466,8 @@ size_t dense_table_bytes(const moba_shape_t *sh) {
 
 size_t dense_ws_bytes(const moba_shape_t *sh) {
   const size_t es = sh->dtype == MOBA_DTYPE_BF16 ? 2 : 4;
-  return dense_table_bytes(sh) +
-         align_up(es * (size_t)sh->num_kv_heads * dense_nb64(sh) * kHeadDim * kKeyTile);
+  return dense_table_bytes(sh) + vt_bytes(es, sh->num_kv_heads, dense_nb64(sh), kKeyTile) +
+         align_up(sizeof(float) * (size_t)sh->num_kv_heads * dense_nb64(sh));
 }
 
 size_t workspace_limit_bytes() {
@@ -649,7 +698,8 @@ moba_status_t moba_attn_fwd(const void *q, const void *k, const void *v, const m
   if (!q || !k || !v) return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v must be non-NULL");
   Problem pb = make_problem(sh, B, topk, scale, L);
   Work w = carve(pb, L, ws);
-  MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+  MOBA_HIP(launch_vtrans(v, pb.vs, k, pb.ks, pb.bf16, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt,
+                         w.knorm, s),
            "vtrans");
   MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
   MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
@@ -668,7 +718,8 @@ moba_status_t moba_attn_fwd_diag(const void *q, const void *k, const void *v,
   if (!q || !k || !v) return fail(MOBA_ERROR_INVALID_VALUE, "q, k, v must be non-NULL");
   Problem pb = make_problem(sh, B, topk, scale, L);
   Work w = carve(pb, L, ws);
-  MOBA_HIP(launch_vtrans(v, pb.bf16, pb.T, pb.Hkv, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt, s),
+  MOBA_HIP(launch_vtrans(v, pb.vs, k, pb.ks, pb.bf16, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt,
+                         w.knorm, s),
            "vtrans");
   MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
   return MOBA_SUCCESS;
@@ -704,14 +755,17 @@ moba_status_t moba_merge(const moba_shape_t *sh, int32_t B, int32_t k, const mob
   return MOBA_SUCCESS;
 }
 
-moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v, const int32_t *cu,
-                             const moba_shape_t *sh, int32_t B, int32_t topk,
-                             const moba_gate_t *gate, float scale, void *out, float *lse,
-                             void *ws, size_t ws_bytes, hipStream_t s) {
+moba_status_t moba_fwd_strided(const void *q, const void *k, const void *v, const int32_t *cu,
+                               const moba_shape_t *sh, const moba_strides_t *strides, int32_t B,
+                               int32_t topk, const moba_gate_t *gate_or_null, float scale,
+                               void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t s) {
+  const moba_gate_t mean{MOBA_GATE_MEAN, 0, 0, 0};
+  const moba_gate_t *gate = gate_or_null ? gate_or_null : &mean;
   moba_status_t st = check_moba_args(sh, B, topk);
   if (st != MOBA_SUCCESS) return st;
   if ((st = check_gate(gate, topk)) != MOBA_SUCCESS) return st;
   if ((st = check_io(q, k, v, cu, out, sh)) != MOBA_SUCCESS) return st;
+  if (strides && (st = check_strides(sh, B, strides)) != MOBA_SUCCESS) return st;
   if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
   moba_layout_t L;
   if ((st = plan_impl(sh, B, topk, sh->num_kv_heads, &L)) != MOBA_SUCCESS) return st;
@@ -725,6 +779,12 @@ moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v, const 
   if (sh->total_tokens == 0) return MOBA_SUCCESS;
   if (!ws) return fail(MOBA_ERROR_INVALID_VALUE, "workspace is NULL");
   Problem pb = make_problem(sh, B, topk, scale, &L);
+  if (strides) {
+    pb.qs = RowHead{strides->q_token, strides->q_head};
+    pb.ks = RowHead{strides->k_token, strides->k_head};
+    pb.vs = RowHead{strides->v_token, strides->v_head};
+    pb.os = RowHead{strides->out_token, strides->out_head};
+  }
   Work w = carve(pb, &L, ws);
   MOBA_HIP(launch_seqtable(cu, pb.S, B, pb.T, pb.maxblk, pb.NBb, w.blk_first, w.cu, w.status,
                            w.blk_info, s),
@@ -735,6 +795,15 @@ moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v, const 
   for (int g0 = 0; g0 < pb.Hkv; g0 += pb.P)
     if ((st = run_pass(pb, w, q, k, v, g0, out, lse, s, *gate)) != MOBA_SUCCESS) return st;
   return MOBA_SUCCESS;
+}
+
+moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v, const int32_t *cu,
+                             const moba_shape_t *sh, int32_t B, int32_t topk,
+                             const moba_gate_t *gate, float scale, void *out, float *lse,
+                             void *ws, size_t ws_bytes, hipStream_t s) {
+  if (!gate) return fail(MOBA_ERROR_INVALID_VALUE, "gate is NULL");
+  return moba_fwd_strided(q, k, v, cu, sh, nullptr, B, topk, gate, scale, out, lse, ws, ws_bytes,
+                          s);
 }
 
 moba_status_t moba_fwd_ex(const void *q, const void *k, const void *v, const int32_t *cu,
@@ -983,6 +1052,7 @@ moba_status_t moba_dense_causal_fwd(const void *q, const void *k, const void *v,
   const Table t64 = table_at(ws, S);
   const Table tq = table_at((char *)ws + align_up(table_bytes(S, NB64)), S);
   void *vt = (char *)ws + dense_table_bytes(sh);
+  float *knorm = (float *)((char *)vt + vt_bytes(bf16 ? 2 : 4, sh->num_kv_heads, NB64, kKeyTile));
   const int no_bound = 0x7fffffff;  // the grid covers every query tile: no length bound
   hipError_t e = launch_seqtable(cu, S, kKeyTile, T, no_bound, NB64, t64.first, t64.cu, t64.status,
                                  t64.info, s);
@@ -996,10 +1066,11 @@ moba_status_t moba_dense_causal_fwd(const void *q, const void *k, const void *v,
     }
   }
   if (e == hipSuccess)
-    e = launch_vtrans(v, bf16, T, sh->num_kv_heads, 0, sh->num_kv_heads, NB64, kKeyTile, t64.info,
-                      vt, s);
+    e = launch_vtrans(v, RowHead{(int64_t)sh->num_kv_heads * kHeadDim, kHeadDim}, k,
+                      RowHead{(int64_t)sh->num_kv_heads * kHeadDim, kHeadDim}, bf16, 0,
+                      sh->num_kv_heads, NB64, kKeyTile, t64.info, vt, knorm, s);
   if (e == hipSuccess)
-    e = launch_dense(q, k, vt, t64.first, tq.info, bf16, T, NBq, sh->num_q_heads,
+    e = launch_dense(q, k, vt, knorm, t64.first, tq.info, bf16, T, NBq, sh->num_q_heads,
                      sh->num_kv_heads, NB64, scale > 0.f ? scale : 1.0f / sqrtf((float)kHeadDim),
                      out, lse, s);
   // a failed table check leaves every tile out: out and lse become NaN

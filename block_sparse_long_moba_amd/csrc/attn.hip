@@ -175,11 +175,18 @@ template <class Pol, bool CHECK> struct Stage {
 // (log2 units), so probabilities stay <= 2^8 and the rescale of the output
 // accumulators is rare. The result is exact: l uses the same reference.
 constexpr float kRescaleSlack = 8.0f;
+// A run of tiles whose every score is within this distance (log2 units) of
+// the first tile's max goes without the other tiles' maxima: its
+// probabilities stay <= 2^64, far inside the fp32 and bf16 ranges, and the
+// result is the same (l uses the same reference).
+constexpr float kBoundSlack = 64.0f;
 
 enum { MODE_HIST = 0, MODE_DIAG = 1, MODE_DENSE = 2 };
 
 struct AttnArgs {
   const void *q, *k, *vt;
+  const float *knorm;  // largest key norm of every block, laid out like vt's blocks
+  RowHead qs, ks, os;  // strides of q, k and (dense) out
   int64_t T;
   int Hq, Hkv, G, B, topk;
   float scale_log2;
@@ -346,12 +353,26 @@ template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// c2 |q| for the query row a lane holds (each lane half holds half of it).
+__device__ __forceinline__ float q_bound(const PolBf16::Q &qr, float c2) {
+  float ss = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < kHeadDim / 16; ++kk)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf((float)qr.v[kk][j], (float)qr.v[kk][j], ss);
+  ss += __shfl_xor(ss, 32);
+  return c2 * sqrtf(ss);
+}
+
+// kn_run: the largest key norm over the run's tiles; qnc2 = c2 |q| of this
+// lane's query, so that qnc2 * kn_run bounds every scaled score of the run.
 template <int MODE, int NW, int NS, int A, int PRE, class Pre>
 __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, uint32_t kstride,
                                              int64_t rows_after, const __bf16 *vt0, int64_t vstep,
                                              uint32_t vstride, int nkt, const PolBf16::Q &qr,
-                                             int qfirst, int qpos, float c2, floatx16 (&o)[4],
-                                             float &m, float &l, Pre &&pre) {
+                                             int qfirst, int qpos, float c2, float kn_run,
+                                             float qnc2, floatx16 (&o)[4], float &m, float &l,
+                                             Pre &&pre) {
   constexpr bool CAUSAL = MODE != MODE_HIST;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -457,13 +478,19 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
       for (int i = 0; i < 16; ++i) sv[st][i] = sc[st][i];
     return tile_max(sv, c2);
   };
+  // set after the first tile: whether this lane's row needs every tile's max
+  // (row_max) and whether any row of the wave does (exact_max)
+  bool row_max = true, exact_max = true;
   static_assert((NS == 2 || NS == 4) && NS >= A + 1 && A >= 1, "pipeline shape");
   using D = Direct<NS>;
   // Loads issued by body j (j < 0: the prologue's share of the pipeline).
   auto loads_of = [&](int j) { return (j + A < nkt ? 1 : 0) + (j + A + 1 < nkt ? 1 : 0); };
-  // One tile: tile kt's masked raw scores are in cur and their scaled max in
-  // mt_cur. With HAS_NEXT the next tile's scores (masked) and max are
-  // produced in the same branch-free region as this tile's exp and P V.
+  // One tile: tile kt's masked raw scores are in cur; mt_cur is the first
+  // tile's scaled max for kt = 0 and -inf after it (a later tile's max is
+  // computed at the start of its body, in waves with a row that needs it,
+  // outside the scheduled region). With HAS_NEXT the next tile's scores
+  // (masked) are produced in the same branch-free region as this tile's exp
+  // and P V.
   // PH = kt % NS selects the buffers at compile time.
   // TAG: the body's index inside the unrolled prefetch section, or -1
   auto body = [&](auto has_next, auto phase, auto tag, int kt, floatx16 (&cur)[2],
@@ -473,12 +500,18 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
     if (kt + A < nkt) issue_v(kt + A, D::V((PH + A) % NS));
     if (kt + A + 1 < nkt) issue_k(kt + A + 1, D::K((PH + A + 1) % NS));
     if constexpr (decltype(tag)::value >= 0) pre(tag);
-    const float nm = move_max(mt_cur, m, l, o);
+    // this tile's max: the first tile's comes from the prologue; later ones
+    // are computed here only in waves with a row that needs them
+    float mt = mt_cur;
+    if (exact_max && kt > 0) {
+      const float x = smax(cur);
+      mt = row_max ? x : -INFINITY;
+    }
+    const float nm = move_max(mt, m, l, o);
     // ---- branch-free region
     if (HAS_NEXT) {
       qk(nxt, D::K((PH + 1) % NS));
       mask(nxt, kt + 1);
-      mt_nxt = smax(nxt);
     }
     exp_pv(cur, nm, D::V(PH));
     // schedule: LDS operand reads run 4 MFMAs ahead; the VALU work is spread
@@ -492,6 +525,7 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
       if (i + kAhead < nmfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, HAS_NEXT ? 4 : 6, 0);
     }
+    if (HAS_NEXT) mt_nxt = -INFINITY;
     // loads issued by bodies kt + 2 - A .. kt may stay in flight
     int later = 0;
 #pragma unroll
@@ -517,6 +551,14 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   qk(sa, D::K(0));
   mask(sa, 0);
   float ma = smax(sa), mb = 0.f;
+  // Every score of the row's run is at most qnc2 * kn_run; within
+  // kBoundSlack of the first tile's max the row keeps that max as its
+  // reference. Otherwise each tile's max moves the reference lazily. The
+  // choice depends on the row alone (both lanes of a row agree), so a row's
+  // result does not depend on the other rows of its wave; the wave computes
+  // tile maxima only when one of its rows needs them.
+  row_max = qnc2 * kn_run > ma + kBoundSlack;
+  exact_max = __builtin_amdgcn_ballot_w64(row_max) != 0;
   // body 0 refills K buffer 0 when A + 1 == NS: every wave must have read it
   if ((A + 1) % NS == 0) __syncthreads();
   // even bodies hold the current tile's scores in sa, odd ones in sb
@@ -641,6 +683,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   int64_t t, kbeg, slot = 0, vstep, vstride;
   int qpos = 0, qfirst = 0;     // causal modes: positions relative to kbeg
   const T *vt0;
+  float kn_run;                 // largest key norm over the keys of the run
 
   if (MODE == MODE_HIST) {
     // XCD-aware order: workgroup i runs on XCD i % 8; give every XCD a
@@ -663,6 +706,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     kbeg = rec.w;
     nkt = a.B / kKeyTile;
     vt0 = (const T *)a.vt + ((int64_t)p * a.NBb + gb) * kHeadDim * a.B;
+    kn_run = a.knorm[(int64_t)p * a.NBb + gb];
     vstep = kKeyTile;
     vstride = a.B;
   } else if (MODE == MODE_DIAG) {
@@ -696,6 +740,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     const int nsel = min(a.topk, bi.w + 1);  // own block is the last chosen slot
     slot = (t * a.Hp + hl) * a.topk + nsel - 1;
     vt0 = (const T *)a.vt + ((int64_t)(g - a.g0) * a.NBb + gb) * kHeadDim * a.B;
+    kn_run = a.knorm[(int64_t)(g - a.g0) * a.NBb + gb];  // the whole block: a valid bound
     vstep = kKeyTile;
     vstride = a.B;
   } else {  // MODE_DENSE
@@ -711,16 +756,22 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     nkt = (qfirst + nrows + kKeyTile - 1) / kKeyTile;  // keys up to the tile's last row
     kbeg = bi.y - qfirst;                              // the sequence's first row
     vt0 = (const T *)a.vt + ((int64_t)g * a.NBb64 + a.blk_first64[bi.x]) * kHeadDim * kKeyTile;
+    // blocks of 64 keys here: the largest norm over the run's
+    const float *kn = a.knorm + (int64_t)g * a.NBb64 + a.blk_first64[bi.x];
+    kn_run = 0.f;
+    for (int i = threadIdx.x & 63; i < nkt; i += 64) kn_run = fmaxf(kn_run, kn[i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kn_run = fmaxf(kn_run, __shfl_xor(kn_run, off));
     vstep = (int64_t)kHeadDim * kKeyTile;
     vstride = kKeyTile;
   }
   const bool valid = r < nrows;
 
   typename Pol::Q qr;
-  Pol::load_q(qr, q + (t * a.Hq + hq) * kHeadDim, hh);
+  Pol::load_q(qr, q + t * a.qs.t + hq * a.qs.h, hh);
 
-  const T *kbase = (const T *)a.k + (int64_t)g * kHeadDim;
-  const int64_t kstride = (int64_t)a.Hkv * kHeadDim;
+  const T *kbase = (const T *)a.k + g * a.ks.h;
+  const int64_t kstride = a.ks.t;
   floatx16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -733,7 +784,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   if constexpr (std::is_same<Pol, PolBf16>::value)
     tiles_direct<MODE, Pol::kThreads / 64, Pol::kStages, Pol::kLoadAhead, 0>(
         lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride, nkt, qr, qfirst,
-        qpos, a.scale_log2, o, m, l, [](int) {});
+        qpos, a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l, [](int) {});
   else
     tiles_staged<Pol, MODE>((T *)lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep,
                             (uint32_t)vstride, nkt, qr, qfirst, qpos, a.scale_log2, o, m, l);
@@ -752,7 +803,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
                   o[dt][4 * aa + 2] * inv, o[dt][4 * aa + 3] * inv);
     if (hh == 0) a.part_lse[slot] = lse;
   } else {
-    T *dst = (T *)a.out + (t * a.Hq + hq) * kHeadDim + 4 * hh;
+    T *dst = (T *)a.out + t * a.os.t + hq * a.os.h + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -784,8 +835,10 @@ struct HistLds {
   static constexpr int NW = PolBf16::kThreads / 64;
   static constexpr int QW = 32 * kHeadDim * 2;  // one wave's 32 query rows
   static constexpr int Q = KV;
-  static constexpr int META = Q + NW * QW;      // per wave: record (16 B), items (256 B)
-  static constexpr int MW = 512;
+  // per wave: the record (16 B, at 0), the items (256 B, at 256) and the
+  // block's key norm (4 B, at 512), each landing as 64 lane-consecutive dwords
+  static constexpr int META = Q + NW * QW;
+  static constexpr int MW = 768;
   static constexpr int NEXT = META + NW * MW;   // next tile index (shared)
   static constexpr int BYTES = NEXT + 16;
   static constexpr int PRE = 5;                 // bodies that prefetch
@@ -799,7 +852,7 @@ __device__ __forceinline__ void fetch_q_rows(const AttnArgs &a, uint32_t slot, i
   const uint32_t th = slot / (uint32_t)a.topk;
   const uint32_t t = th / (uint32_t)a.Hp;
   const int hq = a.h0 + (int)(th % (uint32_t)a.Hp);
-  const __bf16 *row = (const __bf16 *)a.q + ((int64_t)t * a.Hq + hq) * kHeadDim + 8 * hh;
+  const __bf16 *row = (const __bf16 *)a.q + t * a.qs.t + hq * a.qs.h + 8 * hh;
 #pragma unroll
   for (int j = 0; j < kHeadDim / 16; ++j)
     __builtin_amdgcn_global_load_lds((global_ptr_t)(row + 16 * j), (lds_ptr_t)(qst + 1024 * j),
@@ -841,8 +894,9 @@ __global__ __launch_bounds__(PolBf16::kThreads, 1) void attn_hist_loop_kernel(co
   int4 rec = a.tile_rec[base + first];
   uint32_t slot = a.items[(uint32_t)rec.x + min(r, rec.y - 1)];
   fetch_q_rows(a, slot, hh, qst);
+  float kn_run = a.knorm[rec.z];  // bins and norms share the index p * NBb + block
 
-  const int64_t kstride = (int64_t)a.Hkv * kHeadDim;
+  const int64_t kstride = a.ks.t;
   const int nkt = a.B / kKeyTile;
   // the tile loop runs the prefetch steps only if it has more key tiles
   // than its unrolled prefetch section
@@ -857,7 +911,7 @@ __global__ __launch_bounds__(PolBf16::kThreads, 1) void attn_hist_loop_kernel(co
     const int64_t gb = (uint32_t)rec.z % a.NBb;
     const int64_t kbeg = rec.w;
     const int nrows = rec.y;
-    const __bf16 *ktile = (const __bf16 *)a.k + (int64_t)(a.g0 + p) * kHeadDim + kbeg * kstride;
+    const __bf16 *ktile = (const __bf16 *)a.k + (a.g0 + p) * a.ks.h + kbeg * kstride;
     const __bf16 *vt0 = (const __bf16 *)a.vt + ((int64_t)p * a.NBb + gb) * kHeadDim * a.B;
     floatx16 o[4];
 #pragma unroll
@@ -881,6 +935,7 @@ __global__ __launch_bounds__(PolBf16::kThreads, 1) void attn_hist_loop_kernel(co
         } else if (st == 3) {
           const int4 rn = uniform_int4(*(const int4 *)meta);
           fetch_dwords(a.items + (uint32_t)rn.x, rn.y, (uint32_t)min(r, rn.y - 1), meta + 256);
+          fetch_dwords(a.knorm + (uint32_t)rn.z, 1, 0, meta + 512);
         } else if (st == 4) {
           fetch_q_rows(a, *(const uint32_t *)(meta + 256 + 4 * lane), hh, qst);
         }
@@ -888,7 +943,8 @@ __global__ __launch_bounds__(PolBf16::kThreads, 1) void attn_hist_loop_kernel(co
     };
     tiles_direct<MODE_HIST, HistLds::NW, NS, PolBf16::kLoadAhead, HistLds::PRE>(
         lds, ktile, (uint32_t)kstride, a.T - kbeg, vt0, kKeyTile, (uint32_t)a.B, nkt, qr, 0, 0,
-        a.scale_log2, o, m, l, [&](auto kt) { step(decltype(kt)::value); });
+        a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l,
+        [&](auto kt) { step(decltype(kt)::value); });
     if (!inloop) {  // short blocks: the prefetch steps one after another
 #pragma unroll
       for (int st = 0; st < HistLds::PRE; ++st) {
@@ -913,6 +969,7 @@ __global__ __launch_bounds__(PolBf16::kThreads, 1) void attn_hist_loop_kernel(co
     if (__builtin_amdgcn_readfirstlane(*next_idx) >= range) break;
     rec = uniform_int4(*(const int4 *)meta);
     slot = *(const uint32_t *)(meta + 256 + 4 * lane);
+    kn_run = *(const float *)(meta + 512);
   }
 }
 
@@ -935,7 +992,8 @@ hipError_t compute_units(int *out) {
 
 AttnArgs base_args(const Problem &pb, const Work &w, const void *q, const void *k, int g0) {
   AttnArgs a{};
-  a.q = q; a.k = k; a.vt = w.vt;
+  a.q = q; a.k = k; a.vt = w.vt; a.knorm = w.knorm;
+  a.qs = pb.qs; a.ks = pb.ks; a.os = pb.os;
   a.T = pb.T; a.Hq = pb.Hq; a.Hkv = pb.Hkv; a.G = pb.G; a.B = pb.B; a.topk = pb.k;
   a.scale_log2 = pb.scale * kLog2e;
   a.g0 = g0; a.h0 = g0 * pb.G; a.Hp = pb.Hp;
@@ -986,12 +1044,15 @@ hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, con
   return launch_mode<MODE_HIST>(pb.bf16, dim3((unsigned)grid), a, s);
 }
 
-hipError_t launch_dense(const void *q, const void *k, const void *vt,
+hipError_t launch_dense(const void *q, const void *k, const void *vt, const float *knorm,
                         const int32_t *blk_first64, const int4 *qtiles, int bf16, int64_t T,
                         int64_t NBq, int Hq, int Hkv, int64_t NBb64, float scale, void *out,
                         float *lse, hipStream_t s) {
   AttnArgs a{};
-  a.q = q; a.k = k; a.vt = vt;
+  a.q = q; a.k = k; a.vt = vt; a.knorm = knorm;
+  a.qs = RowHead{(int64_t)Hq * kHeadDim, kHeadDim};  // contiguous [T][H][d]
+  a.ks = RowHead{(int64_t)Hkv * kHeadDim, kHeadDim};
+  a.os = a.qs;
   a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv;
   a.scale_log2 = scale * kLog2e;
   a.blk_first64 = blk_first64; a.qtiles = qtiles; a.NBq = NBq;

@@ -6,48 +6,78 @@
 // handled separately (causal, contiguous) and is not dispatched.
 //
 // Bins are (kv head of the pass p, global block gb) -> p*NBb + gb. Three
-// passes: per-workgroup LDS histograms added into global counts, one
-// exclusive scan (items, and tiles of the attention kernel's query rows), and
-// a scatter that reserves a range per (workgroup, bin) and fills it from LDS
-// cursors; a record per tile follows the scan. Item order inside a bin is
-// unspecified; every consumer treats a bin's items independently.
+// passes: per-workgroup LDS histograms added into global counts (the mean
+// gate's matrix-core kernel already adds its own and marks them counted, and
+// then this pass returns at once), one exclusive scan (items, and tiles of
+// the attention kernel's query rows), and a scatter that reserves a range
+// per (workgroup, bin) and fills it from LDS cursors; a record per tile
+// follows the scan. Item order inside a bin is unspecified; every consumer
+// treats a bin's items independently.
 #include "moba_internal.h"
 
 namespace moba {
 namespace {
 
+// Division by a runtime divisor d >= 1 of numerators n < 2^31: with
+// m = floor((2^32 - 1) / d), umulhi(n, m) is floor(n / d) or one less
+// (its error is below n (1 + 1/d) / 2^32 < 1), and one correction step
+// makes it exact.
+struct Div {
+  uint32_t m, d;
+  __device__ uint32_t div(uint32_t n) const {
+    const uint32_t q = __umulhi(n, m);
+    return q + (n - q * d >= d ? 1u : 0u);
+  }
+};
+
+// One workgroup per (block, kDispRows rows): the idx entries of those rows
+// (all query heads of the pass) form one contiguous run, read in order, one
+// entry per lane. Entry f of the run is slot f % k of (row, head) f / k; its
+// bin is (kv head of the pass) * c + (chosen block) for earlier blocks
+// 0 <= block < c, and the item is the entry's index in idx.
+// COUNT: adds the LDS histogram to the global bin counts (skipped when the
+// gate counted already: *counted != 0). SCATTER: reserves a range per
+// (workgroup, bin) and writes the items into it.
+constexpr int kUnroll = 8;
+
 template <bool SCATTER>
 __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t *__restrict__ idx,
                                                        const int4 *__restrict__ info, int64_t NBb,
-                                                       int Hp, int G, int k,
+                                                       int Hp, int G, int k, Div by_kG, Div by_P,
+                                                       const uint32_t *__restrict__ counted,
                                                        uint32_t *__restrict__ bin_count,
                                                        const uint32_t *__restrict__ bin_off,
                                                        uint32_t *__restrict__ cursor,
                                                        uint32_t *__restrict__ items) {
+  if (!SCATTER && *counted) return;
   const int64_t gb = blockIdx.x;
   const int4 bi = info[gb];
-  if (bi.x < 0 || (int)blockIdx.y * kDispatchTokens >= bi.z) return;
+  if (bi.x < 0 || (int)blockIdx.y * kDispatchRows >= bi.z) return;
   const int c = bi.w;
   if (c == 0 || k == 1) return;  // no earlier blocks to dispatch
   const int P = Hp / G;
   const int nbins = P * c;       // local bin (p, j) -> p*c + j
-  if (nbins > kLdsBins) return;  // only if max_seqlen understated the longest sequence
-  __shared__ uint32_t hist[kLdsBins];
+  if (nbins > kLdsBins) return;  // never with a passed table check (the plan bounds P*c)
+  extern __shared__ uint32_t hist[];  // P * (largest block count) entries
   for (int i = threadIdx.x; i < nbins; i += 256) hist[i] = 0;
   __syncthreads();
-  const int nh = min(k, c + 1) - 1;  // earlier-block entries per (row, head)
-  const int rows = min(kDispatchTokens, bi.z - (int)blockIdx.y * kDispatchTokens);
-  const int64_t t0 = bi.y + (int64_t)blockIdx.y * kDispatchTokens;
-  const int n = rows * Hp;
-  for (int rr = threadIdx.x; rr < n; rr += 256) {
-    const int hl = rr % Hp;
-    const int64_t row = (t0 + rr / Hp) * Hp + hl;
-    const int32_t *sel = idx + row * k;
-    const int base = (hl / G) * c;
-    for (int s = 0; s < nh; ++s) {
-      const int j = sel[s];
-      if (j >= 0 && j < c) atomicAdd(&hist[base + j], 1u);
-    }
+  const int rows = min(kDispatchRows, bi.z - (int)blockIdx.y * kDispatchRows);
+  const int64_t f0 = (bi.y + (int64_t)blockIdx.y * kDispatchRows) * Hp * k;
+  const uint32_t nf = (uint32_t)(rows * Hp * k);
+  const int32_t *run = idx + f0;
+  // bin of entry f: kv head (f / (k G)) mod P of the pass, block j
+  auto bin_of = [&](uint32_t f, int j) {
+    const uint32_t rg = by_kG.div(f);
+    return (int)(rg - by_P.div(rg) * (uint32_t)P) * c + j;
+  };
+  // kUnroll entries per thread in flight at a time
+  for (uint32_t f0l = threadIdx.x; f0l < nf; f0l += 256 * kUnroll) {
+    int j[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) j[u] = f0l + 256 * u < nf ? run[f0l + 256 * u] : -1;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (j[u] >= 0 && j[u] < c) atomicAdd(&hist[bin_of(f0l + 256 * u, j[u])], 1u);
   }
   __syncthreads();
   const int64_t first = gb - c;  // global index of the sequence's block 0
@@ -66,19 +96,27 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const int32_t *__restrict
     }
   }
   __syncthreads();
-  for (int rr = threadIdx.x; rr < n; rr += 256) {
-    const int hl = rr % Hp;
-    const int64_t row = (t0 + rr / Hp) * Hp + hl;
-    const int32_t *sel = idx + row * k;
-    const int base = (hl / G) * c;
-    for (int s = 0; s < nh; ++s) {
-      const int j = sel[s];
-      if (j >= 0 && j < c) {
-        const uint32_t pos = atomicAdd(&hist[base + j], 1u);
-        items[pos] = (uint32_t)(row * k + s);
+  for (uint32_t f0l = threadIdx.x; f0l < nf; f0l += 256 * kUnroll) {
+    int j[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) j[u] = f0l + 256 * u < nf ? run[f0l + 256 * u] : -1;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (j[u] >= 0 && j[u] < c) {
+        const uint32_t f = f0l + 256 * u;
+        const uint32_t pos = atomicAdd(&hist[bin_of(f, j[u])], 1u);
+        items[pos] = (uint32_t)(f0 + f);
       }
-    }
   }
+}
+
+// Zeroes the bin counts unless the gate counted (*counted != 0).
+__global__ __launch_bounds__(256) void dispatch_clear_kernel(const uint32_t *__restrict__ counted,
+                                                             uint32_t *__restrict__ bin_count,
+                                                             int64_t nbins) {
+  if (*counted) return;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nbins) bin_count[i] = 0;
 }
 
 // Inclusive scan of one uint32 per thread over 1024 threads.
@@ -159,13 +197,20 @@ __global__ __launch_bounds__(256) void tile_rec_kernel(const uint32_t *__restric
 
 }  // namespace
 
+Div make_div(uint32_t d) { return Div{0xffffffffu / d, d}; }
+
 hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s) {
   const int64_t nbins = (int64_t)pb.P * pb.NBb;
-  hipError_t e = launch_fill_u32(w.bin_count, 0u, nbins, s);
+  dispatch_clear_kernel<<<dim3((unsigned)((nbins + 255) / 256)), 256, 0, s>>>(w.counted, w.bin_count,
+                                                                             nbins);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kDispatchTokens - 1) / kDispatchTokens));
-  dispatch_kernel<false><<<grid, 256, 0, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k,
-                                              w.bin_count, w.bin_off, w.cursor, w.items);
+  dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kDispatchRows - 1) / kDispatchRows));
+  const Div by_kG = make_div((uint32_t)(pb.k * pb.G)), by_P = make_div((uint32_t)pb.P);
+  const size_t lds = sizeof(uint32_t) * (size_t)pb.P * pb.maxblk;
+  dispatch_kernel<false><<<grid, 256, lds, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k, by_kG,
+                                              by_P, w.counted, w.bin_count, w.bin_off, w.cursor,
+                                              w.items);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dispatch_scan_kernel<<<1, 1024, 0, s>>>(w.bin_count, nbins, (uint32_t)pb.rows, w.bin_off,
                                           w.tile_off, w.cursor);
@@ -174,8 +219,9 @@ hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s) {
       w.tile_off, w.bin_off, w.blk_info, pb.NBb, nbins, w.max_tiles, (uint32_t)pb.rows,
       w.tile_rec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dispatch_kernel<true><<<grid, 256, 0, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k,
-                                             w.bin_count, w.bin_off, w.cursor, w.items);
+  dispatch_kernel<true><<<grid, 256, lds, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k, by_kG,
+                                             by_P, w.counted, w.bin_count, w.bin_off, w.cursor,
+                                             w.items);
   return hipGetLastError();
 }
 

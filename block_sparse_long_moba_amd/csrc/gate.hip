@@ -65,7 +65,7 @@ __device__ __forceinline__ void topk_insert(float (&ts)[KMAX], int (&ti)[KMAX], 
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ q,
                                                    const float *__restrict__ kbar,
-                                                   const int4 *__restrict__ info, int Hq,
+                                                   const int4 *__restrict__ info, RowHead qs,
                                                    int Hkv, int G, int h0, int Hp, int k,
                                                    int32_t *__restrict__ idx) {
   const int64_t gb = blockIdx.x;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ q,
   }
 
   float qf[kHeadDim];
-  load_row_f32<T>(q + (t * Hq + h) * kHeadDim, qf);
+  load_row_f32<T>(q + t * qs.t + h * qs.h, qf);
   float ts[KMAX];
   int ti[KMAX];
 #pragma unroll
@@ -181,7 +181,7 @@ __device__ __forceinline__ uint32_t score_key(float s, uint32_t keep, uint32_t l
 template <int KMAX>
 __global__ __launch_bounds__(512) void gate_mfma_kernel(const __bf16 *__restrict__ q,
                                                         const __bf16 *__restrict__ kbar_split,
-                                                        const int4 *__restrict__ info, int Hq,
+                                                        const int4 *__restrict__ info, RowHead qs,
                                                         int Hkv, int G, int h0, int Hp, int k,
                                                         int idx_bits, int32_t *__restrict__ idx) {
   const int64_t gb = blockIdx.x;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(512) void gate_mfma_kernel(const __bf16 *__restrict
   }
 
   bf16x8 qv[kHeadDim / 16];
-  const __bf16 *qrow = q + (t * Hq + h) * kHeadDim + 8 * hh;
+  const __bf16 *qrow = q + t * qs.t + h * qs.h + 8 * hh;
 #pragma unroll
   for (int kk = 0; kk < kHeadDim / 16; ++kk) qv[kk] = *(const bf16x8 *)(qrow + 16 * kk);
 
@@ -286,13 +286,228 @@ int index_bits(int maxblk) {
   return b;
 }
 
+// ---- Matrix-core gate with the pooled keys resident in LDS.
+//
+// Same scores, keys and tie rule as gate_mfma_kernel; the workgroup (16 waves)
+// covers up to kResRows rows of one block for 4 query heads of one kv head and
+// first stages the hi / lo pooled keys of all c earlier blocks into LDS once
+// (one 528-byte row per block: hi, lo and 16 bytes of padding, so the 16 rows
+// a half-wave reads at one column fall in 16 different bank groups and every
+// operand offset is a constant). Each wave then takes (32-row group, head) tasks in turn and
+// scores all c candidates of a task with no barrier. The top-k list of each
+// lane holds exactly KMAX = k - 1 keys when KMAX is an instantiated size
+// (EXACT): the two half-lists of a row (lanes n and n + 32) are then merged
+// by one max per slot against the reversed other list, which leaves the KMAX
+// largest keys of their union (in bitonic order; only the set matters). The
+// own block's padding in the last 32-block chunk is masked only there.
+// With bin_count non-NULL the workgroup also counts its choices per block in
+// LDS and adds them to the dispatch stage's bin counts (bin p * NBb + global
+// block, p the kv head of the pass), so that stage need not read idx twice.
+constexpr int kResRows = 512;        // rows per workgroup
+constexpr int kResWaves = 16;
+constexpr int kResMaxBlocks = 288;   // earlier blocks held in LDS (148.5 KiB)
+
+template <int KMAX, bool EXACT>
+__global__ __launch_bounds__(1024, 1) void gate_resident_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kbar_split,
+    const int4 *__restrict__ info, int64_t NBb, RowHead qs, int Hkv, int G, int h0, int Hp, int k,
+    int idx_bits, int32_t *__restrict__ idx, uint32_t *__restrict__ bin_count) {
+  // blocks with the most earlier blocks first
+  const int64_t gb = NBb - 1 - (int64_t)blockIdx.x;
+  const int4 bi = info[gb];
+  const int row0 = (int)blockIdx.y * kResRows;
+  if (bi.x < 0 || row0 >= bi.z) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n = lane & 31, hh = lane >> 5;
+  const int c = bi.w;
+  const int64_t first = gb - c;
+  const int hl0 = (int)blockIdx.z * 4;
+  const int g = (h0 + hl0) / G;  // the 4 heads share one kv head
+  const int pick = k - 1;
+  const int rows = min(kResRows, bi.z - row0);
+  const int ntasks = ((rows + 31) >> 5) * 4;
+  uint32_t *const bins = bin_count ? bin_count + (int64_t)(hl0 / G) * NBb + first : nullptr;
+
+  if (pick >= c) {  // every earlier block fits: nothing to rank
+    if (bins)  // every (row, head) chose every earlier block
+      for (int j = threadIdx.x; j < c; j += kResWaves * 64) atomicAdd(&bins[j], 4u * rows);
+    for (int task = wave; task < ntasks; task += kResWaves) {
+      const int r = row0 + (task >> 2) * 32 + n;
+      if (hh || r >= bi.z) continue;
+      int32_t *dst = idx + ((int64_t)(bi.y + r) * Hp + hl0 + (task & 3)) * k;
+      for (int j = 0; j < c; ++j) dst[j] = j;
+      dst[c] = c;
+      for (int j = c + 1; j < k; ++j) dst[j] = -1;
+    }
+    return;
+  }
+
+  __shared__ __attribute__((aligned(16))) __bf16 kl[kResMaxBlocks * kGatePitch];
+  __shared__ uint32_t hist[kResMaxBlocks];
+  for (int j = threadIdx.x; j < c; j += kResWaves * 64) hist[j] = 0;
+  {
+    const __bf16 *ksrc = kbar_split + (first * Hkv + g) * 2 * kHeadDim;
+    const int64_t krow = (int64_t)Hkv * 2 * kHeadDim;
+    const int cpad = (c + 31) & ~31;
+    for (int x = threadIdx.x; x < cpad * 32; x += kResWaves * 64) {
+      const int row = x >> 5, piece = x & 31;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < c) v = *(const uint4 *)(ksrc + row * krow + piece * 8);
+      *(uint4 *)(kl + row * kGatePitch + piece * 8) = v;
+    }
+  }
+  __syncthreads();
+
+  // A key's low bits hold maxi - j' with j' = j - 4 hh, which is the same
+  // for both lane halves of a chunk position (so it is formed by the scalar
+  // unit) and orders each half-list's blocks like j; before the two
+  // half-lists meet, the upper half subtracts 4 from its real keys.
+  const uint32_t maxi = (1u << idx_bits) - 1u, keep = ~maxi;
+  // the query row of a task (this lane's half of it); the next task's row is
+  // fetched while the current one is scored
+  auto qrow_of = [&](int task) {
+    const int r = min(row0 + (task >> 2) * 32 + n, bi.z - 1);
+    return q + (bi.y + r) * qs.t + (h0 + hl0 + (task & 3)) * qs.h + 8 * hh;
+  };
+  bf16x8 qn[kHeadDim / 16];
+  {
+    const __bf16 *qrow = qrow_of(wave);
+#pragma unroll
+    for (int kk = 0; kk < kHeadDim / 16; ++kk) qn[kk] = *(const bf16x8 *)(qrow + 16 * kk);
+  }
+  for (int task = wave; task < ntasks; task += kResWaves) {
+    const int hl = hl0 + (task & 3);
+    const int r = row0 + (task >> 2) * 32 + n;
+    const bool active = r < bi.z;
+    const int64_t t = bi.y + (active ? r : 0);
+    bf16x8 qv[kHeadDim / 16];
+#pragma unroll
+    for (int kk = 0; kk < kHeadDim / 16; ++kk) qv[kk] = qn[kk];
+    if (task + kResWaves < ntasks) {
+      const __bf16 *qrow = qrow_of(task + kResWaves);
+#pragma unroll
+      for (int kk = 0; kk < kHeadDim / 16; ++kk) qn[kk] = *(const bf16x8 *)(qrow + 16 * kk);
+    }
+    uint32_t ts[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) ts[i] = 0u;
+    for (int j0 = 0; j0 < c; j0 += 32) {
+      floatx16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      const __bf16 *ar = kl + (j0 + n) * kGatePitch + 8 * hh;  // this lane's block row
+#pragma unroll
+      for (int kk = 0; kk < kHeadDim / 16; ++kk) {
+        const bf16x8 ahi = *(const bf16x8 *)(ar + 16 * kk);
+        const bf16x8 alo = *(const bf16x8 *)(ar + kHeadDim + 16 * kk);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qv[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qv[kk], acc, 0, 0, 0);
+      }
+      const uint32_t lb = maxi - (uint32_t)j0;
+      if (j0 + 32 <= c) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)  // accumulator i holds block j0 + 8(i/4) + 4hh + i%4
+          key_insert<KMAX>(ts, score_key(acc[i], keep, lb - (uint32_t)(8 * (i >> 2) + (i & 3))));
+      } else {
+        const int jb = j0 + 4 * hh;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = jb + 8 * (i >> 2) + (i & 3);
+          key_insert<KMAX>(ts, j < c ? score_key(acc[i], keep,
+                                                 lb - (uint32_t)(8 * (i >> 2) + (i & 3)))
+                                     : 0u);
+        }
+      }
+    }
+    // the row's two half-lists (lanes n and n + 32); empty entries stay 0
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (hh) ts[i] = ts[i] ? ts[i] - 4u : 0u;
+    uint32_t other[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) other[i] = __shfl_xor(ts[i], 32);
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) ts[i] = max(ts[i], other[KMAX - 1 - i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) key_insert<KMAX>(ts, other[i]);
+    }
+    // chosen indices in ascending order (entries past `pick` become sentinels;
+    // with EXACT every entry is chosen)
+    int sel[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) sel[i] = i < pick ? (int)(maxi - (ts[i] & maxi)) : INT_MAX;
+#pragma unroll
+    for (int pass = 0; pass < KMAX; ++pass)
+#pragma unroll
+      for (int i = pass & 1; i + 1 < KMAX; i += 2) {
+        const int a = sel[i], b = sel[i + 1];
+        sel[i] = min(a, b);
+        sel[i + 1] = max(a, b);
+      }
+    if (active && hh == 0) {
+      int32_t *dst = idx + (t * Hp + hl) * k;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i < pick) {
+          dst[i] = sel[i];
+          if (bins) atomicAdd(&hist[sel[i]], 1u);
+        }
+      dst[pick] = c;
+    }
+  }
+  if (bins) {
+    __syncthreads();
+    for (int j = threadIdx.x; j < c; j += kResWaves * 64)
+      if (hist[j]) atomicAdd(&bins[j], hist[j]);
+  }
+}
+
+
+// Whether the matrix-core gate keeps every earlier block in LDS (then it also
+// counts the dispatch bins).
+bool gate_resident(const Problem &pb) {
+  // every earlier block fits in LDS, and lists of up to 16 keys fit the
+  // registers of 16 waves
+  return pb.bf16 && pb.G % 4 == 0 && index_bits(pb.maxblk) <= 12 &&
+         pb.maxblk - 1 <= kResMaxBlocks && pb.k - 1 <= 16;
+}
+
 hipError_t launch_gate_mfma(const Problem &pb, const Work &w, const __bf16 *q, int g0,
-                            hipStream_t s, int bits) {
-  dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kGateRows - 1) / kGateRows), (unsigned)(pb.Hp / 4));
+                            hipStream_t s, int bits, uint32_t *bin_count) {
   const int h0 = g0 * pb.G;
   const int pick = pb.k - 1;
+  if (gate_resident(pb)) {
+    dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kResRows - 1) / kResRows), (unsigned)(pb.Hp / 4));
+#define MOBA_GATE_RES(KM, EX)                                                                   \
+  gate_resident_kernel<KM, EX><<<grid, kResWaves * 64, 0, s>>>(                                \
+      q, w.kbar_split, w.blk_info, pb.NBb, pb.qs, pb.Hkv, pb.G, h0, pb.Hp, pb.k, bits, w.idx,   \
+      bin_count)
+    switch (pick) {
+      case 1: MOBA_GATE_RES(1, true); break;
+      case 2: MOBA_GATE_RES(2, true); break;
+      case 3: MOBA_GATE_RES(3, true); break;
+      case 4: MOBA_GATE_RES(4, true); break;
+      case 5: MOBA_GATE_RES(5, true); break;
+      case 6: MOBA_GATE_RES(6, true); break;
+      case 7: MOBA_GATE_RES(7, true); break;
+      case 8: MOBA_GATE_RES(8, true); break;
+      case 11: MOBA_GATE_RES(11, true); break;
+      case 12: MOBA_GATE_RES(12, true); break;
+      case 15: MOBA_GATE_RES(15, true); break;
+      case 16: MOBA_GATE_RES(16, true); break;
+      default:
+        if (pick <= 0) MOBA_GATE_RES(1, true);  // topk 1: select-all path only
+        else if (pick <= 12) MOBA_GATE_RES(12, false);
+        else MOBA_GATE_RES(16, false);
+    }
+#undef MOBA_GATE_RES
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)pb.NBb, (unsigned)((pb.B + kGateRows - 1) / kGateRows), (unsigned)(pb.Hp / 4));
 #define MOBA_GATE_MFMA(KM)                                                                       \
-  gate_mfma_kernel<KM><<<grid, 512, 0, s>>>(q, w.kbar_split, w.blk_info, pb.Hq, pb.Hkv, pb.G, h0, \
+  gate_mfma_kernel<KM><<<grid, 512, 0, s>>>(q, w.kbar_split, w.blk_info, pb.qs, pb.Hkv, pb.G, h0, \
                                             pb.Hp, pb.k, bits, w.idx)
   if (pick <= 4) MOBA_GATE_MFMA(4);
   else if (pick <= 8) MOBA_GATE_MFMA(8);
@@ -312,19 +527,19 @@ hipError_t launch_gate_t(const Problem &pb, const Work &w, const T *q, int g0, h
   const int h0 = g0 * pb.G;
   const int pick = pb.k - 1;
   if (pick <= 4)
-    gate_kernel<T, 4><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.Hq, pb.Hkv, pb.G, h0, pb.Hp,
+    gate_kernel<T, 4><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.qs, pb.Hkv, pb.G, h0, pb.Hp,
                                            pb.k, w.idx);
   else if (pick <= 8)
-    gate_kernel<T, 8><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.Hq, pb.Hkv, pb.G, h0, pb.Hp,
+    gate_kernel<T, 8><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.qs, pb.Hkv, pb.G, h0, pb.Hp,
                                            pb.k, w.idx);
   else if (pick <= 16)
-    gate_kernel<T, 16><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.Hq, pb.Hkv, pb.G, h0, pb.Hp,
+    gate_kernel<T, 16><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.qs, pb.Hkv, pb.G, h0, pb.Hp,
                                             pb.k, w.idx);
   else if (pick <= kMaxHistPick)
-    gate_kernel<T, kMaxHistPick><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.Hq, pb.Hkv, pb.G,
+    gate_kernel<T, kMaxHistPick><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.qs, pb.Hkv, pb.G,
                                                       h0, pb.Hp, pb.k, w.idx);
   else  // only reached when every sequence has at most topk blocks (select-all path)
-    gate_kernel<T, 4><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.Hq, pb.Hkv, pb.G, h0, pb.Hp,
+    gate_kernel<T, 4><<<grid, 256, 0, s>>>(q, w.kbar, w.blk_info, pb.qs, pb.Hkv, pb.G, h0, pb.Hp,
                                            pb.k, w.idx);
   return hipGetLastError();
 }
@@ -407,15 +622,22 @@ __global__ __launch_bounds__(256) void gate_union_kernel(
 hipError_t launch_gate_window(const Problem &pb, const Work &w, int n_sink, hipStream_t s) {
   const int64_t rows = pb.T * pb.Hp;
   if (rows == 0) return hipSuccess;
+  hipError_t e = launch_fill_u32(w.counted, 0u, 1, s);  // the dispatch counts
+  if (e != hipSuccess) return e;
   gate_window_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(
       w.cu, pb.S, pb.T, pb.B, pb.Hp, pb.k, n_sink, w.status, w.idx);
   return hipGetLastError();
 }
 
+hipError_t launch_gate_impl(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s,
+                            bool count);
+
 hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, int g0,
                               int extra_max, int extra_min, hipStream_t s) {
   const int64_t rows = pb.T * pb.Hp;
   if (rows == 0) return hipSuccess;
+  hipError_t e0 = launch_fill_u32(w.counted, 0u, 1, s);  // the dispatch counts the union
+  if (e0 != hipSuccess) return e0;
   // scratch lists in the partial-output region (unused until the attention);
   // a ranking with nothing to pick gets no list (length 0)
   const int pm = pb.k - extra_max - extra_min - 1;
@@ -433,7 +655,7 @@ hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, i
     w2.kbar = r.f;
     w2.kbar_split = r.split;
     w2.idx = r.list;
-    hipError_t e = launch_gate(p2, w2, q, g0, s);
+    hipError_t e = launch_gate_impl(p2, w2, q, g0, s, false);
     if (e != hipSuccess) return e;
   }
   gate_union_kernel<<<dim3((unsigned)((rows + 255) / 256)), 256, 0, s>>>(
@@ -441,14 +663,27 @@ hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, i
   return hipGetLastError();
 }
 
-hipError_t launch_gate(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s) {
+// Mean gate; with `count` the matrix-core kernel that keeps the pooled keys
+// resident also fills the dispatch bin counts and marks them counted.
+hipError_t launch_gate_impl(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s,
+                            bool count) {
   // matrix-core gate: bf16, groups of a multiple of 4 heads, at most 4096
   // blocks per sequence (12 index bits keep 20 score bits in the keys)
   const int bits = index_bits(pb.maxblk);
+  const bool counts = count && gate_resident(pb);
+  hipError_t e = launch_fill_u32(w.counted, counts ? 1u : 0u, 1, s);
+  if (e != hipSuccess) return e;
+  if (counts && (e = launch_fill_u32(w.bin_count, 0u, (int64_t)pb.P * pb.NBb, s)) != hipSuccess)
+    return e;
   if (pb.bf16 && pb.G % 4 == 0 && bits <= 12)
-    return launch_gate_mfma(pb, w, (const __bf16 *)q, g0, s, bits);
+    return launch_gate_mfma(pb, w, (const __bf16 *)q, g0, s, bits,
+                            counts ? w.bin_count : nullptr);
   return pb.bf16 ? launch_gate_t<__bf16>(pb, w, (const __bf16 *)q, g0, s)
                  : launch_gate_t<float>(pb, w, (const float *)q, g0, s);
+}
+
+hipError_t launch_gate(const Problem &pb, const Work &w, const void *q, int g0, hipStream_t s) {
+  return launch_gate_impl(pb, w, q, g0, s, true);
 }
 
 }  // namespace moba

@@ -15,7 +15,7 @@ constexpr int kRowsBf16 = 256;      // bf16 attention workgroup: 8 waves x 32 ro
 constexpr int kRowsF32 = 128;       // fp32 attention workgroup: 4 waves x 32 rows
 inline int attn_rows(int bf16) { return bf16 ? kRowsBf16 : kRowsF32; }
 constexpr int kGateTokens = 64;     // tokens per gate workgroup (one wave per query head)
-constexpr int kDispatchTokens = 64; // tokens per dispatch workgroup
+constexpr int kDispatchRows = 256;  // rows per dispatch workgroup
 constexpr int kMaxHistPick = 32;    // largest topk-1 kept in registers by the gate
 constexpr int kWorkCounters = 8;    // one per XCD
 constexpr int kMaxExtraPick = 16;   // pooled gate: extra blocks per max / min ranking
@@ -26,6 +26,12 @@ constexpr int kStatusTooManyBlocks = 2;  // a sequence exceeds the plan's blocks
 // 32-bit fill patterns of NaN outputs
 constexpr uint32_t kNanF32 = 0x7fc00000u;
 constexpr uint32_t kNanBf16x2 = 0x7fc07fc0u;
+
+// Element strides of a [T][H][d] tensor: between rows t and t + 1 and between
+// heads h and h + 1 of a row; the d elements of one head are contiguous.
+struct RowHead {
+  int64_t t, h;
+};
 
 // Everything a launcher needs to know about one call.
 struct Problem {
@@ -40,6 +46,7 @@ struct Problem {
   int P, Hp;        // kv heads and query heads per pass
   int maxblk;       // ceil(maxlen / B)
   int rows;         // query rows per attention workgroup (and per dispatch tile)
+  RowHead qs, ks, vs, os;  // strides of q, k, v and out
 };
 
 // Device buffers carved out of a workspace (see moba_layout_t).
@@ -53,12 +60,14 @@ struct Work {
   float *kmax, *kmin;   // [NBb][Hkv][d] max- and min-pooled keys
   __bf16 *kmax_split, *kmin_split;  // [NBb][Hkv][2][d] their bf16 hi and lo parts
   void *vt;             // [P][NBb][d][B]
+  float *knorm;         // [P][NBb] largest key norm of each block
   int32_t *idx;         // [T][Hp][k]
   uint32_t *bin_count;  // [P*NBb]
   uint32_t *bin_off;    // [P*NBb + 1]
   uint32_t *tile_off;   // [P*NBb + 1]
   uint32_t *cursor;     // [P*NBb]
   uint32_t *work;       // [kWorkCounters] tile counters of the persistent attention (per XCD)
+  uint32_t *counted;    // 1: bin_count already holds the gate's counts for the dispatch
   int4 *tile_rec;       // [max tiles] {first item, rows, bin, first token of the block}
   uint32_t *items;      // [T*Hp*(k-1)]
   void *part_o;         // [T*Hp*k][d], element type of the inputs
@@ -86,8 +95,11 @@ hipError_t launch_gate_window(const Problem &pb, const Work &w, int n_sink, hipS
 hipError_t launch_gate_pooled(const Problem &pb, const Work &w, const void *q, int g0,
                               int extra_max, int extra_min, hipStream_t s);
 hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s);
-hipError_t launch_vtrans(const void *v, int bf16, int64_t T, int Hkv, int g0, int P,
-                         int64_t NBb, int B, const int4 *blk_info, void *vt, hipStream_t s);
+// Values transposed per block (vt[P][NBb][d][B]) and the largest key norm of
+// every block (knorm[P][NBb]).
+hipError_t launch_vtrans(const void *v, RowHead vs, const void *k, RowHead ks, int bf16, int g0,
+                         int P, int64_t NBb, int B, const int4 *blk_info, void *vt, float *knorm,
+                         hipStream_t s);
 hipError_t launch_attn_diag(const Problem &pb, const Work &w, const void *q, const void *k,
                             int g0, hipStream_t s);
 hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, const void *k,
@@ -100,7 +112,7 @@ hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const 
 // Dense causal attention: one workgroup per (query tile, query head); qtiles is
 // the block table of the query tiles (attn_rows(bf16) rows), blk_first64 the
 // first 64-row key tile of each sequence in vt.
-hipError_t launch_dense(const void *q, const void *k, const void *vt,
+hipError_t launch_dense(const void *q, const void *k, const void *vt, const float *knorm,
                         const int32_t *blk_first64, const int4 *qtiles, int bf16, int64_t T,
                         int64_t NBq, int Hq, int Hkv, int64_t NBb64, float scale, void *out,
                         float *lse, hipStream_t s);

@@ -150,7 +150,7 @@ template <> struct Vec16<float> {
 // Also writes the bf16 split hi = bf16(mean), lo = bf16(mean - hi) that the
 // gate's matrix-core scores use (two bf16 products recover ~16 mantissa bits).
 template <typename T>
-__global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
+__global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k, RowHead ks,
                                                        const int4 *__restrict__ info, int Hkv,
                                                        float *__restrict__ kbar,
                                                        __bf16 *__restrict__ kbar_split) {
@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
   double acc[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) acc[i] = 0.0;
-  const int64_t stride = (int64_t)Hkv * kHeadDim;
-  const T *base = k + ((int64_t)bi.y * Hkv + g) * kHeadDim + col * N;
+  const int64_t stride = ks.t;
+  const T *base = k + bi.y * ks.t + g * ks.h + col * N;
   int r = rg;
   for (; r + 3 * RG < bi.z; r += 4 * RG) {
     float f[4][N];
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void meanpool_kernel(const T *__restrict__ k,
 // workgroup shape as the mean; max and min are exact, and the bf16 hi / lo
 // splits serve the matrix-core gate as for the mean.
 template <typename T>
-__global__ __launch_bounds__(256) void minmaxpool_kernel(const T *__restrict__ k,
+__global__ __launch_bounds__(256) void minmaxpool_kernel(const T *__restrict__ k, RowHead ks,
                                                          const int4 *__restrict__ info, int Hkv,
                                                          float *__restrict__ kmax,
                                                          float *__restrict__ kmin,
@@ -222,8 +222,8 @@ __global__ __launch_bounds__(256) void minmaxpool_kernel(const T *__restrict__ k
   float mx[N], mn[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) { mx[i] = -INFINITY; mn[i] = INFINITY; }
-  const int64_t stride = (int64_t)Hkv * kHeadDim;
-  const T *base = k + ((int64_t)bi.y * Hkv + g) * kHeadDim + col * N;
+  const int64_t stride = ks.t;
+  const T *base = k + bi.y * ks.t + g * ks.h + col * N;
   for (int r = rg; r < bi.z; r += RG) {
     float f[N];
     Vec16<T>::load(base + (int64_t)r * stride, f);
@@ -252,12 +252,20 @@ __global__ __launch_bounds__(256) void minmaxpool_kernel(const T *__restrict__ k
 // vt[p][gb][e][j] = v[first row of gb + j][g0 + p][e], zero past the block's
 // rows: each block's values transposed so the attention kernels can feed them
 // to the matrix cores with keys along the contraction. One 64-key tile per
-// workgroup, transposed through LDS.
+// workgroup, transposed through LDS. The same workgroup also raises
+// knorm[p][gb] to the largest Euclidean norm of its key rows, so that knorm
+// ends as the largest key norm of the block (zeroed before the launch; norms
+// are non-negative, so their bit patterns order like the values). It bounds
+// every score of the block for a given query (|<q, k>| <= |q| |k|) and lets
+// the attention kernels skip the exact tile maxima where the bound is small
+// enough.
 template <typename T>
-__global__ __launch_bounds__(256) void vtrans_kernel(const T *__restrict__ v, int64_t T_, int Hkv,
+__global__ __launch_bounds__(256) void vtrans_kernel(const T *__restrict__ v, RowHead vs,
+                                                     const T *__restrict__ k, RowHead ks,
                                                      int g0, int64_t NBb, int B,
                                                      const int4 *__restrict__ info,
-                                                     T *__restrict__ vt) {
+                                                     T *__restrict__ vt,
+                                                     float *__restrict__ knorm) {
   constexpr int N = 16 / sizeof(T);
   constexpr int VPR = kHeadDim / N;   // 16-byte vectors per source row
   constexpr int PITCH = kHeadDim + 2; // LDS row pitch in elements
@@ -268,20 +276,38 @@ __global__ __launch_bounds__(256) void vtrans_kernel(const T *__restrict__ v, in
   const int4 bi = info[gb];
   if (bi.x < 0) return;
   __shared__ T tile[kKeyTile * PITCH];
+  __shared__ float wmax[4];
+  float nmax = 0.f;  // largest squared key norm among this thread's rows
   for (int c = threadIdx.x; c < kKeyTile * VPR; c += 256) {
     int r = c / VPR, col = c % VPR;
     int j = jt * kKeyTile + r;
     T tmp[N];
+    float ss = 0.f;
     if (j < bi.z) {
-      *(uint4 *)tmp = *(const uint4 *)(v + ((int64_t)(bi.y + j) * Hkv + g0 + p) * kHeadDim + col * N);
+      const int64_t row = bi.y + j;
+      *(uint4 *)tmp = *(const uint4 *)(v + row * vs.t + (g0 + p) * vs.h + col * N);
+      T kv[N];
+      *(uint4 *)kv = *(const uint4 *)(k + row * ks.t + (g0 + p) * ks.h + col * N);
+#pragma unroll
+      for (int i = 0; i < N; ++i) ss = fmaf((float)kv[i], (float)kv[i], ss);
     } else {
 #pragma unroll
       for (int i = 0; i < N; ++i) tmp[i] = (T)0.0f;
     }
+    // a row's VPR vectors are consecutive threads of one wave
+#pragma unroll
+    for (int o = 1; o < VPR; o <<= 1) ss += __shfl_xor(ss, o);
+    nmax = fmaxf(nmax, ss);
 #pragma unroll
     for (int i = 0; i < N; ++i) tile[r * PITCH + col * N + i] = tmp[i];
   }
+#pragma unroll
+  for (int o = 32; o >= VPR; o >>= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = nmax;
   __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax((unsigned *)&knorm[(int64_t)p * NBb + gb],
+              __float_as_uint(sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])))));
   constexpr int OVPR = kKeyTile / N;  // 16-byte vectors per output row
   T *dst = vt + (((int64_t)p * NBb + gb) * kHeadDim) * B + jt * kKeyTile;
   for (int c = threadIdx.x; c < kHeadDim * OVPR; c += 256) {
@@ -314,7 +340,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
                                                     const int32_t *__restrict__ cu, int S,
                                                     int64_t T_, int Hq, int h0, int Hp, int B,
                                                     int k, const int32_t *__restrict__ status,
-                                                    TO *__restrict__ out,
+                                                    TO *__restrict__ out, RowHead os,
                                                     float *__restrict__ lse_out) {
   constexpr int N = 16 / sizeof(TO);       // elements per thread
   constexpr int LANES = kHeadDim / N;      // threads per row: 16 (bf16) or 32 (fp32)
@@ -328,7 +354,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
     TO nan[N];
 #pragma unroll
     for (int j = 0; j < N; ++j) nan[j] = (TO)NAN;
-    *(uint4 *)(out + (t * Hq + h0 + hl) * kHeadDim + lane * N) = *(const uint4 *)nan;
+    *(uint4 *)(out + t * os.t + (h0 + hl) * os.h + lane * N) = *(const uint4 *)nan;
     if (lane == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = NAN;
     return;
   }
@@ -381,7 +407,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
   TO res[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) res[j] = (TO)acc[j];
-  *(uint4 *)(out + (t * Hq + h0 + hl) * kHeadDim + lane * N) = *(const uint4 *)res;
+  *(uint4 *)(out + t * os.t + (h0 + hl) * os.h + lane * N) = *(const uint4 *)res;
   if (lane == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = L;
 }
 
@@ -415,34 +441,37 @@ hipError_t launch_poison(const int32_t *status, void *p, int64_t words, uint32_t
 hipError_t launch_meanpool(const Problem &pb, const Work &w, const void *k, hipStream_t s) {
   dim3 grid((unsigned)pb.NBb, (unsigned)pb.Hkv);
   if (pb.bf16)
-    meanpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, w.blk_info, pb.Hkv, w.kbar,
-                                                  w.kbar_split);
+    meanpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, pb.ks, w.blk_info, pb.Hkv,
+                                                  w.kbar, w.kbar_split);
   else
-    meanpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kbar,
-                                                 w.kbar_split);
+    meanpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, pb.ks, w.blk_info, pb.Hkv,
+                                                 w.kbar, w.kbar_split);
   return hipGetLastError();
 }
 
 hipError_t launch_minmaxpool(const Problem &pb, const Work &w, const void *k, hipStream_t s) {
   dim3 grid((unsigned)pb.NBb, (unsigned)pb.Hkv);
   if (pb.bf16)
-    minmaxpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, w.blk_info, pb.Hkv, w.kmax,
-                                                    w.kmin, w.kmax_split, w.kmin_split);
+    minmaxpool_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)k, pb.ks, w.blk_info, pb.Hkv,
+                                                    w.kmax, w.kmin, w.kmax_split, w.kmin_split);
   else
-    minmaxpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, w.blk_info, pb.Hkv, w.kmax,
-                                                   w.kmin, w.kmax_split, w.kmin_split);
+    minmaxpool_kernel<float><<<grid, 256, 0, s>>>((const float *)k, pb.ks, w.blk_info, pb.Hkv,
+                                                   w.kmax, w.kmin, w.kmax_split, w.kmin_split);
   return hipGetLastError();
 }
 
-hipError_t launch_vtrans(const void *v, int bf16, int64_t T, int Hkv, int g0, int P, int64_t NBb,
-                         int B, const int4 *blk_info, void *vt, hipStream_t s) {
+hipError_t launch_vtrans(const void *v, RowHead vs, const void *k, RowHead ks, int bf16, int g0,
+                         int P, int64_t NBb, int B, const int4 *blk_info, void *vt, float *knorm,
+                         hipStream_t s) {
   dim3 grid((unsigned)(NBb * (B / kKeyTile)), (unsigned)P);
+  const hipError_t e = launch_fill_u32((uint32_t *)knorm, 0u, (int64_t)P * NBb, s);
+  if (e != hipSuccess) return e;
   if (bf16)
-    vtrans_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)v, T, Hkv, g0, NBb, B, blk_info,
-                                               (__bf16 *)vt);
+    vtrans_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)v, vs, (const __bf16 *)k, ks, g0,
+                                               NBb, B, blk_info, (__bf16 *)vt, knorm);
   else
-    vtrans_kernel<float><<<grid, 256, 0, s>>>((const float *)v, T, Hkv, g0, NBb, B, blk_info,
-                                              (float *)vt);
+    vtrans_kernel<float><<<grid, 256, 0, s>>>((const float *)v, vs, (const float *)k, ks, g0,
+                                              NBb, B, blk_info, (float *)vt, knorm);
   return hipGetLastError();
 }
 
@@ -455,11 +484,13 @@ hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, flo
   dim3 grid((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
   const int h0 = g0 * pb.G;
   if (pb.bf16)
-    merge_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
-                                              pb.Hp, pb.B, pb.k, w.status, (__bf16 *)out, lse);
+    merge_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)w.part_o, w.part_lse, cu, pb.S,
+                                              pb.T, pb.Hq, h0, pb.Hp, pb.B, pb.k, w.status,
+                                              (__bf16 *)out, pb.os, lse);
   else
-    merge_kernel<float><<<grid, 256, 0, s>>>((const float *)w.part_o, w.part_lse, cu, pb.S, pb.T, pb.Hq, h0,
-                                             pb.Hp, pb.B, pb.k, w.status, (float *)out, lse);
+    merge_kernel<float><<<grid, 256, 0, s>>>((const float *)w.part_o, w.part_lse, cu, pb.S, pb.T,
+                                             pb.Hq, h0, pb.Hp, pb.B, pb.k, w.status, (float *)out,
+                                             pb.os, lse);
   return hipGetLastError();
 }
 

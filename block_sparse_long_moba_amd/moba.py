@@ -23,8 +23,8 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_workspace_status", "mo
            "moba_fwd_workspace_size",
            "moba_seqtable", "moba_meanpool", "moba_gate", "moba_minmaxpool", "moba_gate_window",
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
-           "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated", "moba_fwd",
-           "moba_fwd_noalloc",
+           "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated",
+           "moba_fwd_strided", "moba_fwd", "moba_fwd_noalloc",
            "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
            "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd", "moba_bwd_delta",
            "moba_attn_bwd_dq", "moba_attn_bwd_dq_sum", "moba_attn_bwd_dkdv",
@@ -61,6 +61,12 @@ def gate_window(n_sink=0) -> Gate:
 
 def gate_pooled(extra_max=1, extra_min=1) -> Gate:
     return Gate(GATE_POOLED, 0, int(extra_max), int(extra_min))
+
+
+class Strides(ctypes.Structure):
+    """Element strides (row, head) of q, k, v and out (moba_strides_t)."""
+    _fields_ = [(n, ctypes.c_int64) for n in ("q_token", "q_head", "k_token", "k_head",
+                                               "v_token", "v_head", "out_token", "out_head")]
 
 
 class Layout(ctypes.Structure):
@@ -108,6 +114,8 @@ def lib():
             "moba_fwd_ex": ([P, P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
             "moba_fwd_gated": ([P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, Z,
                                 P], I32),
+            "moba_fwd_strided": ([P, P, P, P, S, ctypes.POINTER(Strides), I32, I32,
+                                  ctypes.POINTER(Gate), F, P, P, P, Z, P], I32),
             "moba_fwd": ([P, P, P, P, S, I32, I32, P, P, P], I32),
             "moba_fwd_noalloc": ([P, P, P, P, S, I32, I32, F, P, P, P], I32),
             "moba_decode_workspace_size": ([S, I32, I32], Z),
@@ -245,10 +253,27 @@ def moba_merge(shape, block_size, topk, layout, workspace, out, lse=None, kv_hea
                             _stream(stream)))
 
 
+def _contiguous(**tensors):
+    """The entry points without strides read [T][H][d] tensors packed row by row."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous (moba_fwd_strided takes strided tensors)"
+                             % name)
+
+
+def strides_of(q, k, v, out) -> Strides:
+    """Strides of [T][H][d] tensors whose last dimension is contiguous."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("%s: a [T][H][d] tensor with contiguous d is required" % name)
+    return Strides(q.stride(0), q.stride(1), k.stride(0), k.stride(1), v.stride(0), v.stride(1),
+                   out.stride(0), out.stride(1))
+
+
 def _outputs(q, out, lse, want_lse=True):
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     return out, lse
@@ -257,6 +282,7 @@ def _outputs(q, out, lse, want_lse=True):
 def moba_fwd(q, k, v, cu_seqlens, block_size, topk, out=None, lse=None, max_seqlen=0,
              stream=None):
     """MoBA forward pass; returns (out [T][Hq][d], lse [Hq][T])."""
+    _contiguous(q=q, k=k, v=v, out=out)
     out, lse = _outputs(q, out, lse)
     sh = shape_of(q, k, cu_seqlens, max_seqlen)
     _check(lib().moba_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
@@ -271,6 +297,7 @@ def moba_fwd_noalloc(q, k, v, cu_seqlens, block_size, topk, out=None, lse=None,
                      softmax_scale=0.0, max_seqlen=0, stream=None):
     """MoBA forward pass on the library's static workspace (no allocation in
     the library; out and lse are allocated here only when not given)."""
+    _contiguous(q=q, k=k, v=v, out=out)
     out, lse = _outputs(q, out, lse)
     sh = shape_of(q, k, cu_seqlens, max_seqlen)
     _check(lib().moba_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
@@ -282,6 +309,7 @@ def moba_fwd_noalloc(q, k, v, cu_seqlens, block_size, topk, out=None, lse=None,
 def moba_fwd_ex(q, k, v, cu_seqlens, block_size, topk, workspace, out=None, lse=None,
                 softmax_scale=0.0, max_seqlen=0, stream=None):
     """MoBA forward pass with a caller-provided workspace (uint8 device tensor)."""
+    _contiguous(q=q, k=k, v=v, out=out)
     out, lse = _outputs(q, out, lse)
     sh = shape_of(q, k, cu_seqlens, max_seqlen)
     _check(lib().moba_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
@@ -294,12 +322,29 @@ def moba_fwd_ex(q, k, v, cu_seqlens, block_size, topk, workspace, out=None, lse=
 def moba_fwd_gated(q, k, v, cu_seqlens, block_size, topk, gate, workspace, out=None, lse=None,
                    softmax_scale=0.0, max_seqlen=0, stream=None):
     """Forward pass with a gate variant (Gate) and a caller-provided workspace."""
+    _contiguous(q=q, k=k, v=v, out=out)
     out, lse = _outputs(q, out, lse)
     sh = shape_of(q, k, cu_seqlens, max_seqlen)
     _check(lib().moba_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
                                 block_size, topk, ctypes.byref(gate), softmax_scale, _ptr(out),
                                 _ptr(lse), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
+
+
+def moba_fwd_strided(q, k, v, cu_seqlens, block_size, topk, workspace, gate=None, out=None,
+                     lse=None, softmax_scale=0.0, max_seqlen=0, stream=None):
+    """Forward pass over [T][H][d] tensors with any row and head strides (the
+    last dimension contiguous), e.g. views of one fused qkv tensor; gate None
+    is the mean gate. Returns (out, lse); a given out keeps its strides."""
+    out, lse = _outputs(q, out, lse)
+    sh = shape_of(q, k, cu_seqlens, max_seqlen)
+    st = strides_of(q, k, v, out)
+    _check(lib().moba_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), ctypes.byref(sh),
+                                  ctypes.byref(st), block_size, topk,
+                                  None if gate is None else ctypes.byref(gate), softmax_scale,
+                                  _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

@@ -25,7 +25,8 @@
  *
  * Tensor layout ("THD", packed variable-length batch, all device memory):
  *   q   [T][Hq][d], k and v [T][Hkv][d], out [T][Hq][d], rows contiguous, no
- *       padding; element type given by moba_dtype_t;
+ *       padding (moba_fwd_strided also takes other row and head strides);
+ *       element type given by moba_dtype_t; every tensor 16-byte aligned;
  *   lse [Hq][T] float32, natural-log log-sum-exp of the scaled logits;
  *   cu_seqlens [S+1] int32 on the device: cu[0] = 0, non-decreasing,
  *       cu[S] = T; sequence s owns rows [cu[s], cu[s+1]); empty sequences are
@@ -60,7 +61,7 @@
  * MOBA_SUCCESS, since nothing was synchronised; moba_workspace_status()
  * reports the failure afterwards, and with the environment variable
  * MOBA_CHECK=1 the whole-pass entry points (moba_fwd, moba_fwd_ex,
- * moba_fwd_gated, moba_bwd, moba_decode_prepare, moba_dense_causal_fwd)
+ * moba_fwd_gated, moba_fwd_strided, moba_bwd, moba_decode_prepare, moba_dense_causal_fwd)
  * synchronise the stream once right after the check and return
  * MOBA_ERROR_INVALID_VALUE without launching anything further.
  *
@@ -161,7 +162,9 @@ typedef struct moba_layout {
    * min-pooled keys (kmin, kmin_split). */
   size_t kbar_offset;
   /* element type, vt[P][NBb][d][block_size]: for each kv head of the pass
-   * and each block, the block's value rows transposed (zero past its rows). */
+   * and each block, the block's value rows transposed (zero past its rows);
+   * then (256-byte aligned) float32 knorm[P][NBb]: the largest Euclidean norm
+   * of the key rows of each block. */
   size_t vt_offset;
   /* int32 idx[T][Hp][topk]: chosen local block ids of the pass's query heads,
    * ascending, unused entries -1; the query's own block c is always at
@@ -171,7 +174,9 @@ typedef struct moba_layout {
   /* dispatch tables over bins b = p*NBb + global_block (p < P), uint32:
    * count[P*NBb], offset[P*NBb+1], tile_offset[P*NBb+1] (tiles of the
    * attention kernel's query rows: 256 for bf16, 128 for float32),
-   * cursor[P*NBb], 8 tile counters of the earlier-block attention; then,
+   * cursor[P*NBb], 8 tile counters of the earlier-block attention, a flag
+   * (1: the gate already filled count, so moba_dispatch does not recount);
+   * then,
    * 16-byte aligned, int32x4 tile records
    * [max_tiles] = {first item, rows, bin, first token of the bin's block},
    * where max_tiles = ceil(T*Hp*(topk-1)/128) + P*NBb bounds the tile count. */
@@ -265,7 +270,11 @@ moba_status_t moba_gate_pooled(const void *q, const moba_shape_t *shape, int32_t
 
 /* Regroup queries by chosen block (step 2): histogram, prefix sum and scatter
  * of the earlier-block entries of idx into the bins and items regions. The
- * query's own block is not dispatched (the diagonal attention covers it). */
+ * query's own block is not dispatched (the diagonal attention covers it).
+ * moba_gate may already have filled the histogram (for bf16 with groups of a
+ * multiple of 4 query heads, top-k <= 17 and at most 289 blocks per
+ * sequence); every gate stage records in the bins region whether it did, so
+ * moba_dispatch must follow a gate stage on the same workspace and pass. */
 moba_status_t moba_dispatch(const moba_shape_t *shape, int32_t block_size, int32_t topk,
                             const moba_layout_t *layout, void *workspace, int32_t kv_head_begin,
                             hipStream_t stream);
@@ -318,6 +327,34 @@ moba_status_t moba_fwd_gated(const void *q, const void *k, const void *v,
                              int32_t block_size, int32_t topk, const moba_gate_t *gate,
                              float softmax_scale, void *out, float *lse, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* Strided q, k, v and out for the whole forward pass: element strides of a
+ * [T][H][d] tensor between rows t and t + 1 (token) and between heads h and
+ * h + 1 of one row (head); the d elements of one head stay contiguous. The
+ * contiguous layout is token = H * d, head = d; q, k and v taken as views of
+ * one fused projection output, or a head-major [H][T][d] tensor (token = d,
+ * head = T * d), need no copy. Every stride must be a positive multiple of 16
+ * bytes (8 bf16 or 4 float32 elements) and every pointer 16-byte aligned; out's
+ * (row, head) vectors must not overlap; block_size rows of k must span less
+ * than 2 GiB (k_token * element size * block_size < 2^31). Violations return
+ * MOBA_ERROR_INVALID_VALUE (MOBA_ERROR_UNSUPPORTED for the 2 GiB bound)
+ * before any work is queued. The stage entry points take contiguous tensors. */
+typedef struct moba_strides {
+  int64_t q_token, q_head;
+  int64_t k_token, k_head;
+  int64_t v_token, v_head;
+  int64_t out_token, out_head;
+} moba_strides_t;
+
+/* moba_fwd_gated over strided tensors: strides NULL means contiguous, gate
+ * NULL means MOBA_GATE_MEAN. Results equal moba_fwd_gated's on the same
+ * values bit for bit (the layout changes only where rows are read and
+ * written). The workspace and lse are as for moba_fwd_ex. */
+moba_status_t moba_fwd_strided(const void *q, const void *k, const void *v,
+                               const int32_t *cu_seqlens, const moba_shape_t *shape,
+                               const moba_strides_t *strides, int32_t block_size, int32_t topk,
+                               const moba_gate_t *gate, float softmax_scale, void *out, float *lse,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Same as moba_fwd_ex with softmax_scale = 1/sqrt(d) and stream-ordered scratch of at most
  * MOBA_WORKSPACE_LIMIT_GIB GiB (environment, default 48) per call. */

@@ -230,3 +230,41 @@ def test_bwd_plan_and_validation():
     assert L.moba_bwd(null, null, null, null, null, null, null, ctypes.byref(empty), 4096, 12,
                       null, 0.0, null, null, null, null,
                       moba.moba_bwd_workspace_size(empty, 4096, 12, 0), null) == 0
+
+
+def test_strided_forward_validation_without_a_device():
+    L = moba.lib()
+    sh = shape()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+    def call(st, q=fake, out=fake, sh=sh):
+        return L.moba_fwd_strided(q, fake, fake, fake, ctypes.byref(sh),
+                                  None if st is None else ctypes.byref(st), 4096, 12, None, 0.0,
+                                  out, None, fake, 16, None)
+
+    d = 128
+    contiguous = moba.Strides(32 * d, d, 8 * d, d, 8 * d, d, 32 * d, d)
+    # valid strides reach the workspace check (status 3), invalid ones stop before it
+    assert call(None) == 3
+    assert call(contiguous) == 3
+    fused = moba.Strides(48 * d, d, 48 * d, d, 48 * d, d, 32 * d, d)  # views of one qkv tensor
+    assert call(fused) == 3
+    head_major_out = moba.Strides(32 * d, d, 8 * d, d, 8 * d, d, d, 4096 * d)
+    assert call(head_major_out) == 3
+    for bad in (moba.Strides(32 * d, 4, 8 * d, d, 8 * d, d, 32 * d, d),    # 8 bytes
+                moba.Strides(-32 * d, d, 8 * d, d, 8 * d, d, 32 * d, d),   # negative
+                moba.Strides(32 * d, d, 8 * d, 0, 8 * d, d, 32 * d, d),    # zero
+                moba.Strides(32 * d, d, 8 * d, d, 8 * d, d, 32 * d, 64),   # heads overlap
+                moba.Strides(32 * d, d, 8 * d, d, 8 * d, d, 31 * d, d)):   # rows overlap
+        assert call(bad) == 1, (bad.q_token, bad.q_head, bad.out_token, bad.out_head)
+        assert b"stride" in L.moba_last_error()
+    # a block of key rows spanning 2 GiB
+    huge = moba.Strides(32 * d, d, 1 << 18, d, 8 * d, d, 32 * d, d)
+    assert call(huge) == 2
+    # fp32 rows are 16-byte aligned at multiples of 4 elements
+    sh32 = shape(dtype="fp32")
+    assert call(moba.Strides(36 * d + 4, d + 4, 8 * d, d, 8 * d, d, 32 * d, d), sh=sh32) == 3
+    assert call(moba.Strides(36 * d + 2, d, 8 * d, d, 8 * d, d, 32 * d, d), sh=sh32) == 1
+    # every pointer 16-byte aligned, with or without strides
+    assert call(None, q=ctypes.c_void_p(0x1008)) == 1
+    assert b"aligned" in L.moba_last_error()
