@@ -102,12 +102,24 @@ class Timer:
         return {n: (sum(a.elapsed_time(b) for a, b in v), len(v)) for n, v in self.pairs.items()}
 
 
+# Further workloads timed after the headline one, each reported under
+# "workloads" with its own roofline and CPU baseline: the metric is quoted at
+# 128K and 1M tokens; the 32K layer and the packed batch are the other
+# single-GPU shapes of the same head layout.
+ALSO_WORKLOADS = ["gqa32x8_t128k_b4096_k12_bf16", "gqa32x8_t32k_b512_k3_bf16",
+                  "gqa32x8_varlen4_t256k_b4096_k12_bf16"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default="auto",
+                    help="comma-separated further workloads reported under \"workloads\" "
+                    "(auto: %s after the default workload, none otherwise; none: skip)"
+                    % ",".join(ALSO_WORKLOADS))
     ap.add_argument("--no-dense", action="store_true", help="skip the dense causal baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gate", choices=["mean", "window", "pooled"], default="mean",
@@ -123,7 +135,8 @@ def main():
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (dq, dk, dv; with --gate) instead of the forward")
     ap.add_argument("--cpu-rows", type=int, default=0,
-                    help="rows the CPU oracle times (0 = sized for about 15 s)")
+                    help="rows the CPU oracle times (0 = sized for about 15 s; 5 s for the "
+                    "further workloads)")
     ap.add_argument("--flush", choices=["auto", "on", "off"], default="auto",
                     help="write a 512 MiB buffer between timed forward steps, outside the "
                     "steps' events, so that no step finds its inputs in L2 / MALL (auto: on "
@@ -144,11 +157,49 @@ def main():
         bwd_bench(args)
         return
 
+    if args.also == "auto":
+        also = ALSO_WORKLOADS if args.workload == DEFAULT_WORKLOAD and args.gate == "mean" else []
+    elif args.also in ("", "none"):
+        also = []
+    else:
+        also = [x for x in args.also.split(",") if x]
+    from block_sparse_long_moba_amd import synth
+    for name in [args.workload] + also:
+        if name not in synth.WORKLOADS:
+            print("unknown workload %s (known: %s)" % (name, ", ".join(synth.WORKLOADS)),
+                  file=sys.stderr)
+            sys.exit(2)
+
+    head = forward_bench(args, args.workload, headline=True)
+    res = {
+        "metric": "MoBA fwd ms + effective TFLOP/s at 128K/1M tokens (8B heads), % MFMA peak",
+        "value": head["value"], "unit": "TFLOP/s (effective)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"], "data": "synthetic (seeded N(0,1) q/k/v, per-block key offsets)",
+        "config": head["config"],
+    }
+    res.update({k: v for k, v in head.items() if k not in ("value", "ms", "dtype", "config")})
+    if also:
+        res["workloads"] = {}
+        for name in also:
+            r = forward_bench(args, name, headline=False)
+            res["workloads"][name] = {
+                "value": r["value"], "unit": "TFLOP/s (effective)", "ms_per_step": r["ms"],
+                "dtype": r["dtype"], "config": r["config"],
+                "attention_mfma_frac": r["attention_mfma_frac"], "stage_ms": r["stage_ms"],
+                "hbm": r["hbm"], "roofline": r["roofline"], "cpu_baseline": r["cpu_baseline"]}
+    print(json.dumps(res), flush=True)
+
+
+def forward_bench(args, name, headline):
+    """Times the forward pass on workload `name`; with headline, also the
+    dense causal baseline and the measured ceilings (unless switched off)."""
     import torch
     from block_sparse_long_moba_amd import moba, synth
     from block_sparse_long_moba_amd.tensors import to_device, workspace_view
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[name]
     B, k, Hq, Hkv = w.block_size, w.topk, w.num_q_heads, w.num_kv_heads
     if args.gate == "pooled":
         k += args.extra_max + args.extra_min  # slots: the mean gate's k plus the extra picks
@@ -195,17 +246,19 @@ def main():
             tm.run("attn_hist", lambda: moba.moba_attn_fwd_hist(q, kk, shape, B, k, lay, ws, g0))
             tm.run("merge", lambda: moba.moba_merge(shape, B, k, lay, ws, out, lse, g0))
 
-    # earlier-block rows dispatched per pass (for the dominant kernel's flops)
+    # earlier-block rows dispatched per pass (for the dominant kernel's flops),
+    # and whether the gate counted them (then the dispatch reads idx once)
     nbins = lay.kv_heads_per_pass * lay.num_blocks_bound
-    hist_rows = []
+    hist_rows, gate_counted = [], []
     moba.moba_seqtable(cu, shape, B, lay, ws)
     pools()
     for g0 in passes:
         gate(g0)
         moba.moba_dispatch(shape, B, k, lay, ws, g0)
         torch.cuda.synchronize()
-        off = workspace_view(ws, lay.bins_offset + 4 * nbins, nbins + 1, torch.int32)
-        hist_rows.append(int(off[-1].item()) & 0xFFFFFFFF)
+        words = workspace_view(ws, lay.bins_offset, 4 * nbins + 2 + 8 + 1, torch.int32)
+        hist_rows.append(int(words[2 * nbins].item()) & 0xFFFFFFFF)  # offset[nbins]
+        gate_counted.append(int(words[4 * nbins + 2 + 8].item()) != 0)
 
     log("warmup %d step(s)" % args.warmup)
     for _ in range(args.warmup):
@@ -264,24 +317,26 @@ def main():
     else:
         mp_bytes = T * Hkv * HEAD_DIM * es + nb * Hkv * HEAD_DIM * 4
         gate_bytes = T * Hq * HEAD_DIM * es + T * Hq * k * 4
-    # dispatch: idx read by the count and the scatter pass, items written
+    # dispatch: idx read by the scatter pass (and by the count pass unless the
+    # gate counted), items written
     n_hist = sum(hist_rows)
-    disp_bytes = 2 * T * Hq * k * 4 + n_hist * 4
+    idx_reads = sum(1 if c else 2 for c in gate_counted) / len(passes)
+    disp_bytes = int(idx_reads * T * Hq * k * 4) + n_hist * 4
     # merge: every valid slot's partial (row and lse) read, out and lse written
     merge_bytes = (n_hist + T * Hq) * (HEAD_DIM * es + 4) + T * Hq * (HEAD_DIM * es + 4)
     hbm = {}
-    for name, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes), ("dispatch", disp_bytes),
-                         ("merge", merge_bytes)):
-        sm = stages[name][0]
+    for sname, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes), ("dispatch", disp_bytes),
+                          ("merge", merge_bytes)):
+        sm = stages[sname][0]
         if nbytes == 0 or sm <= 0:
             continue
-        hbm[name] = {"ms": round(sm, 4), "GB/s": round(nbytes / (sm * 1e-3) / 1e9, 1),
-                     "frac": round(nbytes / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        hbm[sname] = {"ms": round(sm, 4), "GB/s": round(nbytes / (sm * 1e-3) / 1e9, 1),
+                      "frac": round(nbytes / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     attn_ms = stages["attn_diag"][0] + stages["attn_hist"][0]
     attn_eff = eff / (attn_ms * 1e-3) / 1e12
 
     dense = None
-    if not args.no_dense:
+    if headline and not args.no_dense:
         log("dense causal baseline")
         dws = torch.empty(moba.moba_dense_causal_workspace_size(shape), dtype=torch.uint8,
                           device="cuda")
@@ -305,7 +360,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, w, args.cpu_rows, args.gate, k, args.n_sink, args.extra_max,
-                           args.extra_min)
+                           args.extra_min, seconds=15 if headline else 5)
         # the whole pass on the CPU, extrapolated from the sample by effective FLOP
         cpu["extrapolated_full_pass_s"] = round(eff / (cpu["value"] * 1e12), 1)
 
@@ -315,7 +370,8 @@ def main():
                   "ms_at_hbm_peak": round(io_bytes / (PEAK_HBM_GBS * 1e9) * 1e3, 3)}
 
     ceilings = None
-    if not args.no_ceilings:
+    if headline and not args.no_ceilings:
+        del ws, out, lse, q, kk, v
         ceilings = measured_ceilings(torch)
         ceilings["attn_hist_frac_of_gemm"] = round(achieved / ceilings["bf16_gemm_TFLOP/s"], 4)
         ceilings["attn_hist_frac_of_mfma_loop"] = round(
@@ -323,20 +379,16 @@ def main():
         ceilings["hbm_stages_frac_of_copy"] = {
             n: round(x["GB/s"] / ceilings["hbm_copy_GB/s"], 4) for n, x in hbm.items()}
 
-    res = {
-        "metric": "MoBA fwd ms + effective TFLOP/s at 128K/1M tokens (8B heads), % MFMA peak",
-        "value": round(value, 3), "unit": "TFLOP/s (effective)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic (seeded N(0,1) q/k/v, per-block key offsets)",
-        "config": {"workload": w.name, "seq_lens": list(w.lengths), "total_tokens": T,
-                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": HEAD_DIM, "block_size": B,
-                   "topk": k, "kv_heads_per_pass": lay.kv_heads_per_pass,
-                   "gate": {"mean": {"kind": "mean"},
-                            "window": {"kind": "window", "n_sink": args.n_sink},
-                            "pooled": {"kind": "pooled", "extra_max": args.extra_max,
-                                       "extra_min": args.extra_min}}[args.gate],
-                   "parallelism": "single GPU"},
+    config = {"workload": w.name, "seq_lens": list(w.lengths), "total_tokens": T,
+              "q_heads": Hq, "kv_heads": Hkv, "head_dim": HEAD_DIM, "block_size": B,
+              "topk": k, "kv_heads_per_pass": lay.kv_heads_per_pass,
+              "gate": {"mean": {"kind": "mean"},
+                       "window": {"kind": "window", "n_sink": args.n_sink},
+                       "pooled": {"kind": "pooled", "extra_max": args.extra_max,
+                                  "extra_min": args.extra_min}}[args.gate],
+              "parallelism": "single GPU"}
+    return {
+        "value": round(value, 3), "ms": round(ms, 3), "dtype": w.dtype, "config": config,
         "effective_flop": eff,
         "attention_effective_TFLOPs": round(attn_eff, 2),
         "attention_mfma_frac": round(attn_eff / peak, 4),
@@ -348,7 +400,6 @@ def main():
         "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res), flush=True)
 
 
 def bwd_bench(args):
@@ -648,19 +699,21 @@ def measured_ceilings(torch):
                    "(libmoba_probe.so)"}
 
 
-def cpu_baseline(inp, w, n_rows, gate="mean", k=None, n_sink=1, extra_max=1, extra_min=1):
+def cpu_baseline(inp, w, n_rows, gate="mean", k=None, n_sink=1, extra_max=1, extra_min=1,
+                 seconds=15):
     """The fp64 oracle on a bounded sample of the same workload: the block
     representations the gate needs (pooled keys of every block), then the
-    gate's selection and the attention for n sampled rows (all heads)."""
+    gate's selection and the attention for n sampled rows (all heads); with
+    n_rows = 0 the sample is sized for about `seconds` of attention work."""
     import oracle
     B, Hq = w.block_size, w.num_q_heads
     k = w.topk if k is None else k
     rng = np.random.default_rng(w.seed + 77)
     T = w.total_tokens
     if n_rows <= 0:
-        # about 15 s of attention work at ~1.5 GFLOP/s per thread (fp64, plain loops)
+        # about `seconds` of attention work at ~1.5 GFLOP/s per thread (fp64, plain loops)
         per_row = 4.0 * HEAD_DIM * Hq * (k * B)
-        n_rows = int(max(8, min(T, 15 * 1.5e9 * _threads() / per_row)))
+        n_rows = int(max(8, min(T, seconds * 1.5e9 * _threads() / per_row)))
     rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False)).astype(np.int64)
     log("cpu baseline: oracle on %d sampled rows (%s gate)" % (len(rows), gate))
     t0 = time.time()

@@ -23,3 +23,10 @@ def test_help_lists_the_modes():
     assert p.returncode == 0
     for opt in ("--bwd", "--decode", "--gate", "--no-cpu-baseline"):
         assert opt in p.stdout
+
+
+def test_unknown_workloads_are_refused_before_any_gpu_work():
+    for args in (("--workload", "nope"), ("--also", "gqa32x8_t128k_b4096_k12_bf16,nope")):
+        p = run(*args)
+        assert p.returncode == 2
+        assert "unknown workload nope" in p.stderr
