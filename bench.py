@@ -44,8 +44,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "4efdd82a6acf564a74f649058ada19e27b66fa5b18ad2e6f98bcbc6346ad872f",
-    "fetch_kib": 20448034.6, "write_kib": 25360275.6,
+    "sha256": "cac5e7f93bd13300f27ad8f9e7e35b018db757109548322d8f8d2cfded0d7429",
+    "fetch_kib": 23133954.2, "write_kib": 25392328.0,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 
