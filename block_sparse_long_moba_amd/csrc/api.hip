@@ -216,6 +216,14 @@ moba_status_t bwd_plan_impl(const moba_shape_t *sh, int32_t B, int32_t k, int32_
   return MOBA_SUCCESS;
 }
 
+// Strides of contiguous [T][H][d] q, k, v and out.
+void set_contiguous(Problem *pb) {
+  pb->qs = RowHead{(int64_t)pb->Hq * kHeadDim, kHeadDim};
+  pb->ks = RowHead{(int64_t)pb->Hkv * kHeadDim, kHeadDim};
+  pb->vs = pb->ks;
+  pb->os = pb->qs;
+}
+
 Problem make_problem(const moba_shape_t *sh, int32_t B, int32_t k, float scale,
                      const moba_layout_t *L) {
   Problem pb{};
@@ -234,11 +242,7 @@ Problem make_problem(const moba_shape_t *sh, int32_t B, int32_t k, float scale,
   pb.Hp = L->q_heads_per_pass;
   pb.maxblk = L->max_blocks_per_seq;
   pb.rows = attn_rows(pb.bf16);
-  // contiguous [T][H][d] tensors
-  pb.qs = RowHead{(int64_t)pb.Hq * kHeadDim, kHeadDim};
-  pb.ks = RowHead{(int64_t)pb.Hkv * kHeadDim, kHeadDim};
-  pb.vs = pb.ks;
-  pb.os = pb.qs;
+  set_contiguous(&pb);
   return pb;
 }
 
@@ -536,6 +540,7 @@ void decode_setup(const moba_shape_t *sh, int32_t B, int32_t k, float scale, con
   pb->Hp = pb->Hq;
   pb->maxblk = D.maxblk;
   pb->rows = attn_rows(pb->bf16);
+  set_contiguous(pb);  // the cache is a contiguous [T][Hkv][d] tensor
   char *b = (char *)ws;
   *w = Work{};
   const Table tb = table_at(b + D.table, pb->S);
