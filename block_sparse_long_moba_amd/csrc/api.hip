@@ -423,7 +423,7 @@ moba_status_t check_strides(const moba_shape_t *sh, int32_t B, const moba_stride
                   "%s strides (%lld, %lld): must be positive multiples of %lld elements", x.name,
                   (long long)x.t, (long long)x.h, (long long)unit);
   }
-  if (st->k_token * es * B > INT32_MAX)
+  if (st->k_token > INT32_MAX / (es * B))  // k_token * es * B would reach 2^31
     return fail(MOBA_ERROR_UNSUPPORTED, "k token stride %lld: a block of %d rows spans 2 GiB or more",
                 (long long)st->k_token, B);
   // out: the smaller stride must step over a whole head row, the larger one

@@ -261,6 +261,7 @@ def test_strided_forward_validation_without_a_device():
     # a block of key rows spanning 2 GiB
     huge = moba.Strides(32 * d, d, 1 << 18, d, 8 * d, d, 32 * d, d)
     assert call(huge) == 2
+    assert call(moba.Strides(32 * d, d, 1 << 60, d, 8 * d, d, 32 * d, d)) == 2  # no overflow
     # fp32 rows are 16-byte aligned at multiples of 4 elements
     sh32 = shape(dtype="fp32")
     assert call(moba.Strides(36 * d + 4, d + 4, 8 * d, d, 8 * d, d, 32 * d, d), sh=sh32) == 3
