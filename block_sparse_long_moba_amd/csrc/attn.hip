@@ -485,12 +485,12 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   using D = Direct<NS>;
   // Loads issued by body j (j < 0: the prologue's share of the pipeline).
   auto loads_of = [&](int j) { return (j + A < nkt ? 1 : 0) + (j + A + 1 < nkt ? 1 : 0); };
-  // One tile: tile kt's masked raw scores are in cur; mt_cur is the first
-  // tile's scaled max for kt = 0 and -inf after it (a later tile's max is
-  // computed at the start of its body, in waves with a row that needs it,
-  // outside the scheduled region). With HAS_NEXT the next tile's scores
-  // (masked) are produced in the same branch-free region as this tile's exp
-  // and P V.
+  // One tile: tile kt's raw scores are in cur (masked already for kt = 0);
+  // mt_cur is the first tile's scaled max for kt = 0 and -inf after it. A
+  // later tile's causal mask and, in waves with a row that needs it, its max
+  // are applied at the start of its body, outside the scheduled region. With
+  // HAS_NEXT the next tile's scores are produced in the same branch-free
+  // region as this tile's exp and P V.
   // PH = kt % NS selects the buffers at compile time.
   // TAG: the body's index inside the unrolled prefetch section, or -1
   auto body = [&](auto has_next, auto phase, auto tag, int kt, floatx16 (&cur)[2],
@@ -500,6 +500,10 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
     if (kt + A < nkt) issue_v(kt + A, D::V((PH + A) % NS));
     if (kt + A + 1 < nkt) issue_k(kt + A + 1, D::K((PH + A + 1) % NS));
     if constexpr (decltype(tag)::value >= 0) pre(tag);
+    // the causal mask of a later tile, here rather than in the region: its
+    // branch (taken only on the tiles that cross the diagonal) would split
+    // the region and undo the interleave of the other tiles
+    if (kt > 0) mask(cur, kt);
     // this tile's max: the first tile's comes from the prologue; later ones
     // are computed here only in waves with a row that needs them
     float mt = mt_cur;
@@ -509,10 +513,7 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
     }
     const float nm = move_max(mt, m, l, o);
     // ---- branch-free region
-    if (HAS_NEXT) {
-      qk(nxt, D::K((PH + 1) % NS));
-      mask(nxt, kt + 1);
-    }
+    if (HAS_NEXT) qk(nxt, D::K((PH + 1) % NS));
     exp_pv(cur, nm, D::V(PH));
     // schedule: LDS operand reads run 4 MFMAs ahead; the VALU work is spread
     // evenly between all MFMAs of the region
