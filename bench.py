@@ -44,8 +44,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "cac5e7f93bd13300f27ad8f9e7e35b018db757109548322d8f8d2cfded0d7429",
-    "fetch_kib": 23133954.2, "write_kib": 25392328.0,
+    "sha256": "a5c3538bb6dfada8dbdbc7904bfeb99638fff0462b4d7aae117249fbed9a65d7",
+    "fetch_kib": 23132351.4, "write_kib": 25393743.5,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 
