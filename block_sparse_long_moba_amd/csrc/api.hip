@@ -128,10 +128,10 @@ bool check_enabled() {
 }
 
 // Bins region: count[nbins], offset[nbins+1], tile_offset[nbins+1],
-// cursor[nbins], work counters[kWorkCounters], the counted flag (uint32),
-// then (16-byte aligned) int4 tile records.
+// cursor[nbins], the counted flag (uint32), then (16-byte aligned) int4 tile
+// records.
 size_t tile_rec_offset(int64_t nbins) {
-  return (sizeof(uint32_t) * (size_t)(4 * nbins + 2 + kWorkCounters + 1) + 15) / 16 * 16;
+  return (sizeof(uint32_t) * (size_t)(4 * nbins + 2 + 1) + 15) / 16 * 16;
 }
 size_t bins_bytes(int64_t nbins, int64_t max_tiles) {
   return tile_rec_offset(nbins) + 16 * (size_t)max_tiles;
@@ -270,8 +270,7 @@ Work carve(const Problem &pb, const moba_layout_t *L, void *ws) {
   w.bin_off = bins + nbins;
   w.tile_off = bins + 2 * nbins + 1;
   w.cursor = bins + 3 * nbins + 2;
-  w.work = bins + 4 * nbins + 2;
-  w.counted = w.work + kWorkCounters;
+  w.counted = bins + 4 * nbins + 2;
   w.tile_rec = (int4 *)((char *)bins + tile_rec_offset(nbins));
   w.items = (uint32_t *)(b + L->items_offset);
   w.part_o = b + L->part_o_offset;

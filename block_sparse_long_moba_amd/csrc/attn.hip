@@ -196,7 +196,6 @@ struct AttnArgs {
   // historical blocks
   const uint32_t *tile_off, *bin_off, *items;
   const int4 *tile_rec;
-  uint32_t *work;  // per-XCD tile counters (zero at launch)
   int64_t nbins;
   // partial outputs (MoBA) or final outputs (dense)
   void *part_o;
@@ -338,20 +337,7 @@ template <int PER, int MAXC> __device__ __forceinline__ void wait_vm_groups(int 
 // its end each wave waits for its loads that the next body reads (V^T tile
 // kt + 1, K tile kt + 2), then the workgroup synchronises. A buffer is
 // refilled only after the barrier that ends the last body reading it, which
-// needs NS >= A + 1. With PRE > 0 and more than pre_bodies(PRE, NS) key
-// tiles, the first pre_bodies(PRE, NS) bodies are unrolled and body kt calls
-// pre(integral_constant<int, kt>) right after its loads are issued (the
-// persistent kernel prefetches the next tile's inputs there); the main loop
-// and the last bodies never call it.
-constexpr int pre_bodies(int pre, int ns) { return (pre + ns - 1) / ns * ns; }
-
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F> __device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
+// needs NS >= A + 1.
 
 // c2 |q| for the query row a lane holds (each lane half holds half of it).
 __device__ __forceinline__ float q_bound(const PolBf16::Q &qr, float c2) {
@@ -366,13 +352,12 @@ __device__ __forceinline__ float q_bound(const PolBf16::Q &qr, float c2) {
 
 // kn_run: the largest key norm over the run's tiles; qnc2 = c2 |q| of this
 // lane's query, so that qnc2 * kn_run bounds every scaled score of the run.
-template <int MODE, int NW, int NS, int A, int PRE, class Pre>
+template <int MODE, int NW, int NS, int A>
 __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, uint32_t kstride,
                                              int64_t rows_after, const __bf16 *vt0, int64_t vstep,
                                              uint32_t vstride, int nkt, const PolBf16::Q &qr,
                                              int qfirst, int qpos, float c2, float kn_run,
-                                             float qnc2, floatx16 (&o)[4], float &m, float &l,
-                                             Pre &&pre) {
+                                             float qnc2, floatx16 (&o)[4], float &m, float &l) {
   constexpr bool CAUSAL = MODE != MODE_HIST;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -492,14 +477,12 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   // HAS_NEXT the next tile's scores are produced in the same branch-free
   // region as this tile's exp and P V.
   // PH = kt % NS selects the buffers at compile time.
-  // TAG: the body's index inside the unrolled prefetch section, or -1
-  auto body = [&](auto has_next, auto phase, auto tag, int kt, floatx16 (&cur)[2],
+  auto body = [&](auto has_next, auto phase, int kt, floatx16 (&cur)[2],
                   floatx16 (&nxt)[2], float mt_cur, float &mt_nxt) {
     constexpr bool HAS_NEXT = decltype(has_next)::value;
     constexpr int PH = decltype(phase)::value;
     if (kt + A < nkt) issue_v(kt + A, D::V((PH + A) % NS));
     if (kt + A + 1 < nkt) issue_k(kt + A + 1, D::K((PH + A + 1) % NS));
-    if constexpr (decltype(tag)::value >= 0) pre(tag);
     // the causal mask of a later tile, here rather than in the region: its
     // branch (taken only on the tiles that cross the diagonal) would split
     // the region and undo the interleave of the other tiles
@@ -563,58 +546,47 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   // body 0 refills K buffer 0 when A + 1 == NS: every wave must have read it
   if ((A + 1) % NS == 0) __syncthreads();
   // even bodies hold the current tile's scores in sa, odd ones in sb
-  auto run = [&](auto has_next, auto phase, auto tag, int kt) {
+  auto run = [&](auto has_next, auto phase, int kt) {
     constexpr int PH = decltype(phase)::value;
-    if constexpr (PH % 2 == 0) body(has_next, phase, tag, kt, sa, sb, ma, mb);
-    else body(has_next, phase, tag, kt, sb, sa, mb, ma);
+    if constexpr (PH % 2 == 0) body(has_next, phase, kt, sa, sb, ma, mb);
+    else body(has_next, phase, kt, sb, sa, mb, ma);
   };
   using P0 = integral_constant<int, 0>;
   using P1 = integral_constant<int, 1>;
   using P2 = integral_constant<int, 2>;
   using P3 = integral_constant<int, 3>;
-  using NoTag = integral_constant<int, -1>;
   auto full = [&](int kt) {
-    run(T_{}, P0{}, NoTag{}, kt);
-    run(T_{}, P1{}, NoTag{}, kt + 1);
+    run(T_{}, P0{}, kt);
+    run(T_{}, P1{}, kt + 1);
     if constexpr (NS > 2) {
-      run(T_{}, P2{}, NoTag{}, kt + 2);
-      run(T_{}, P3{}, NoTag{}, kt + 3);
+      run(T_{}, P2{}, kt + 2);
+      run(T_{}, P3{}, kt + 3);
     }
   };
   int kt = 0;
-  if constexpr (PRE > 0) {
-    constexpr int NPRE = pre_bodies(PRE, NS);
-    if (nkt > NPRE) {
-      static_for<NPRE>([&](auto i) {
-        constexpr int I = decltype(i)::value;
-        run(T_{}, integral_constant<int, I % NS>{}, i, I);
-      });
-      kt = NPRE;
-    }
-  }
   for (; kt + NS < nkt; kt += NS) full(kt);
   // 1 .. NS tiles left, kt % NS == 0
   const int left = nkt - kt;
   if constexpr (NS > 2) {
     if (left == 4) {
-      run(T_{}, P0{}, NoTag{}, kt);
-      run(T_{}, P1{}, NoTag{}, kt + 1);
-      run(T_{}, P2{}, NoTag{}, kt + 2);
-      run(F_{}, P3{}, NoTag{}, kt + 3);
+      run(T_{}, P0{}, kt);
+      run(T_{}, P1{}, kt + 1);
+      run(T_{}, P2{}, kt + 2);
+      run(F_{}, P3{}, kt + 3);
       return;
     }
     if (left == 3) {
-      run(T_{}, P0{}, NoTag{}, kt);
-      run(T_{}, P1{}, NoTag{}, kt + 1);
-      run(F_{}, P2{}, NoTag{}, kt + 2);
+      run(T_{}, P0{}, kt);
+      run(T_{}, P1{}, kt + 1);
+      run(F_{}, P2{}, kt + 2);
       return;
     }
   }
   if (left == 2) {
-    run(T_{}, P0{}, NoTag{}, kt);
-    run(F_{}, P1{}, NoTag{}, kt + 1);
+    run(T_{}, P0{}, kt);
+    run(F_{}, P1{}, kt + 1);
   } else {
-    run(F_{}, P0{}, NoTag{}, kt);
+    run(F_{}, P0{}, kt);
   }
 }
 
@@ -783,9 +755,9 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   const T *ktile = kbase + kbeg * kstride;
   const int64_t rows_after = a.T - kbeg;  // K rows from kbeg to the end of the tensor
   if constexpr (std::is_same<Pol, PolBf16>::value)
-    tiles_direct<MODE, Pol::kThreads / 64, Pol::kStages, Pol::kLoadAhead, 0>(
+    tiles_direct<MODE, Pol::kThreads / 64, Pol::kStages, Pol::kLoadAhead>(
         lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride, nkt, qr, qfirst,
-        qpos, a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l, [](int) {});
+        qpos, a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l);
   else
     tiles_staged<Pol, MODE>((T *)lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep,
                             (uint32_t)vstride, nkt, qr, qfirst, qpos, a.scale_log2, o, m, l);
@@ -815,182 +787,6 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   }
 }
 
-// ---- persistent earlier-block attention (bf16). One workgroup per CU takes
-// the tiles of its XCD's range in order from that XCD's counter, so the
-// tiles running on one XCD at any time are neighbours (mostly of one bin,
-// whose keys and values then stay in the XCD's L2), and a slow CU simply
-// takes fewer tiles. While a tile runs, its first bodies fetch what the next
-// tile needs, through LDS so that nothing of it occupies registers in the
-// main loop:
-//   body 0: wave 0 takes the next tile index from the counter;
-//   body 1: it publishes the index in LDS (the body's barrier orders it);
-//   body 2: every wave fetches the tile record into its own LDS area;
-//   body 3: every lane fetches the item of its query row;
-//   body 4: every lane fetches its query row.
-// A step's loads have landed at the end of its body (each body ends by
-// waiting for this wave's loads). Piece j of lane l of the query area is
-// chunk 2j + hh of the lane's own row, at 1024 j + 16 l: the MFMA B-operand
-// layout, so the read-back needs no exchange between lanes.
-struct HistLds {
-  static constexpr int KV = Direct<PolBf16::kStages>::BYTES;
-  static constexpr int NW = PolBf16::kThreads / 64;
-  static constexpr int QW = 32 * kHeadDim * 2;  // one wave's 32 query rows
-  static constexpr int Q = KV;
-  // per wave: the record (16 B, at 0), the items (256 B, at 256) and the
-  // block's key norm (4 B, at 512), each landing as 64 lane-consecutive dwords
-  static constexpr int META = Q + NW * QW;
-  static constexpr int MW = 768;
-  static constexpr int NEXT = META + NW * MW;   // next tile index (shared)
-  static constexpr int BYTES = NEXT + 16;
-  static constexpr int PRE = 5;                 // bodies that prefetch
-};
-
-typedef __attribute__((address_space(1))) const void *global_ptr_t;
-
-// Gather this lane's query row (slot -> token, head) into the wave's area
-// (64-bit per-lane addresses: the rows may lie anywhere in a large tensor).
-__device__ __forceinline__ void fetch_q_rows(const AttnArgs &a, uint32_t slot, int hh, char *qst) {
-  const uint32_t th = slot / (uint32_t)a.topk;
-  const uint32_t t = th / (uint32_t)a.Hp;
-  const int hq = a.h0 + (int)(th % (uint32_t)a.Hp);
-  const __bf16 *row = (const __bf16 *)a.q + t * a.qs.t + hq * a.qs.h + 8 * hh;
-#pragma unroll
-  for (int j = 0; j < kHeadDim / 16; ++j)
-    __builtin_amdgcn_global_load_lds((global_ptr_t)(row + 16 * j), (lds_ptr_t)(qst + 1024 * j),
-                                     16, 0, 0);
-}
-
-// dword i of the n dwords at p (wave-uniform p and n), lane l's at lds + 4 l
-__device__ __forceinline__ void fetch_dwords(const void *p, int n, uint32_t i, char *lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(uniform_rsrc(p, 4 * (int64_t)n), (lds_ptr_t)lds, 4,
-                                           4u * i, 0, 0, 0);
-}
-
-__device__ __forceinline__ int4 uniform_int4(int4 v) {
-  return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
-                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
-}
-
-__global__ __launch_bounds__(PolBf16::kThreads, 1) void attn_hist_loop_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[HistLds::BYTES];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hh = lane >> 5;
-  const int r = wave * 32 + (lane & 31);  // this lane's query row inside the tile
-  char *const qst = lds + HistLds::Q + wave * HistLds::QW;
-  char *const meta = lds + HistLds::META + wave * HistLds::MW;
-  uint32_t *const next_idx = (uint32_t *)(lds + HistLds::NEXT);
-
-  const uint32_t ntiles = a.tile_off[a.nbins];
-  const uint32_t per = (ntiles + 7) >> 3;
-  const uint32_t xcd = blockIdx.x & 7;
-  const uint32_t base = xcd * per;
-  const uint32_t range = base < ntiles ? min(per, ntiles - base) : 0u;
-  uint32_t *const ctr = a.work + xcd;
-
-  if (threadIdx.x == 0) *next_idx = atomicAdd(ctr, 1u);
-  __syncthreads();
-  const uint32_t first = __builtin_amdgcn_readfirstlane(*next_idx);
-  if (first >= range) return;
-  int4 rec = a.tile_rec[base + first];
-  uint32_t slot = a.items[(uint32_t)rec.x + min(r, rec.y - 1)];
-  fetch_q_rows(a, slot, hh, qst);
-  float kn_run = a.knorm[rec.z];  // bins and norms share the index p * NBb + block
-
-  const int64_t kstride = a.ks.t;
-  const int nkt = a.B / kKeyTile;
-  // the tile loop runs the prefetch steps only if it has more key tiles
-  // than its unrolled prefetch section
-  constexpr int NS = PolBf16::kStages;
-  const bool inloop = nkt > pre_bodies(HistLds::PRE, NS);
-  for (;;) {
-    wait_vm<0>();  // this wave's query rows are in LDS
-    PolBf16::Q qr;
-#pragma unroll
-    for (int j = 0; j < kHeadDim / 16; ++j) qr.v[j] = *(const bf16x8 *)(qst + 1024 * j + 16 * lane);
-    const int p = (int)((uint32_t)rec.z / a.NBb);
-    const int64_t gb = (uint32_t)rec.z % a.NBb;
-    const int64_t kbeg = rec.w;
-    const int nrows = rec.y;
-    const __bf16 *ktile = (const __bf16 *)a.k + (a.g0 + p) * a.ks.h + kbeg * kstride;
-    const __bf16 *vt0 = (const __bf16 *)a.vt + ((int64_t)p * a.NBb + gb) * kHeadDim * a.B;
-    floatx16 o[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    float m = -INFINITY, l = 0.f;
-
-    uint32_t taken = 0;  // counter value (thread 0 only)
-    auto step = [&](int st) {
-      if (st == 0) {
-        if (threadIdx.x == 0) taken = atomicAdd(ctr, 1u);
-      } else if (st == 1) {
-        if (threadIdx.x == 0) *next_idx = taken;
-      } else {
-        const uint32_t nx = __builtin_amdgcn_readfirstlane(*next_idx);
-        if (nx >= range) return;
-        if (st == 2) {
-          // lanes 0..3 fetch the record's fields; lane l's dword lands at meta + 4 l
-          fetch_dwords(a.tile_rec + base + nx, 4, lane & 3, meta);
-        } else if (st == 3) {
-          const int4 rn = uniform_int4(*(const int4 *)meta);
-          fetch_dwords(a.items + (uint32_t)rn.x, rn.y, (uint32_t)min(r, rn.y - 1), meta + 256);
-          fetch_dwords(a.knorm + (uint32_t)rn.z, 1, 0, meta + 512);
-        } else if (st == 4) {
-          fetch_q_rows(a, *(const uint32_t *)(meta + 256 + 4 * lane), hh, qst);
-        }
-      }
-    };
-    tiles_direct<MODE_HIST, HistLds::NW, NS, PolBf16::kLoadAhead, HistLds::PRE>(
-        lds, ktile, (uint32_t)kstride, a.T - kbeg, vt0, kKeyTile, (uint32_t)a.B, nkt, qr, 0, 0,
-        a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l,
-        [&](auto kt) { step(decltype(kt)::value); });
-    if (!inloop) {  // short blocks: the prefetch steps one after another
-#pragma unroll
-      for (int st = 0; st < HistLds::PRE; ++st) {
-        step(st);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-      }
-    }
-
-    const float lt = l + __shfl_xor(l, 32);
-    const float inv = 1.f / lt;
-    if (r < nrows) {
-      __bf16 *dst = (__bf16 *)a.part_o + (int64_t)slot * kHeadDim + 4 * hh;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int aa = 0; aa < 4; ++aa)
-          store4<__bf16>(dst + 32 * dt + 8 * aa, o[dt][4 * aa] * inv, o[dt][4 * aa + 1] * inv,
-                         o[dt][4 * aa + 2] * inv, o[dt][4 * aa + 3] * inv);
-      if (hh == 0) a.part_lse[slot] = (m + __log2f(lt)) * kLn2;
-    }
-    if (__builtin_amdgcn_readfirstlane(*next_idx) >= range) break;
-    rec = uniform_int4(*(const int4 *)meta);
-    slot = *(const uint32_t *)(meta + 256 + 4 * lane);
-    kn_run = *(const float *)(meta + 512);
-  }
-}
-
-// Compute units of the current device (cached per device).
-hipError_t compute_units(int *out) {
-  static int cached[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    cached[dev] = n;
-  }
-  *out = cached[dev];
-  return hipSuccess;
-}
-
 AttnArgs base_args(const Problem &pb, const Work &w, const void *q, const void *k, int g0) {
   AttnArgs a{};
   a.q = q; a.k = k; a.vt = w.vt; a.knorm = w.knorm;
@@ -1000,7 +796,6 @@ AttnArgs base_args(const Problem &pb, const Work &w, const void *q, const void *
   a.g0 = g0; a.h0 = g0 * pb.G; a.Hp = pb.Hp;
   a.NBb = pb.NBb; a.info = w.blk_info;
   a.tile_off = w.tile_off; a.tile_rec = w.tile_rec; a.bin_off = w.bin_off; a.items = w.items;
-  a.work = w.work;
   a.nbins = (int64_t)pb.P * pb.NBb;
   a.part_o = w.part_o; a.part_lse = w.part_lse;
   return a;
@@ -1030,17 +825,6 @@ hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, con
                             hipStream_t s) {
   if (pb.k <= 1) return hipSuccess;
   const AttnArgs a = base_args(pb, w, q, k, g0);
-  if (pb.bf16) {
-    // one workgroup per CU (a multiple of the 8 XCDs), never more than tiles
-    int cus = 0;
-    hipError_t e = compute_units(&cus);
-    if (e != hipSuccess) return e;
-    const int64_t grid = std::min<int64_t>(std::max(8, cus / 8 * 8), (w.max_tiles + 7) / 8 * 8);
-    e = launch_fill_u32(w.work, 0u, kWorkCounters, s);
-    if (e != hipSuccess) return e;
-    attn_hist_loop_kernel<<<dim3((unsigned)grid), PolBf16::kThreads, 0, s>>>(a);
-    return hipGetLastError();
-  }
   const int64_t grid = (w.max_tiles + 7) / 8 * 8;
   return launch_mode<MODE_HIST>(pb.bf16, dim3((unsigned)grid), a, s);
 }

@@ -17,7 +17,6 @@ inline int attn_rows(int bf16) { return bf16 ? kRowsBf16 : kRowsF32; }
 constexpr int kGateTokens = 64;     // tokens per gate workgroup (one wave per query head)
 constexpr int kDispatchRows = 256;  // rows per dispatch workgroup
 constexpr int kMaxHistPick = 32;    // largest topk-1 kept in registers by the gate
-constexpr int kWorkCounters = 8;    // one per XCD
 constexpr int kMaxExtraPick = 16;   // pooled gate: extra blocks per max / min ranking
 constexpr int kLdsBins = 16384;     // LDS histogram bins of the dispatch stage (64 KiB)
 // Bits of the status word the sequence-table scan writes (0: input accepted).
@@ -66,7 +65,6 @@ struct Work {
   uint32_t *bin_off;    // [P*NBb + 1]
   uint32_t *tile_off;   // [P*NBb + 1]
   uint32_t *cursor;     // [P*NBb]
-  uint32_t *work;       // [kWorkCounters] tile counters of the persistent attention (per XCD)
   uint32_t *counted;    // 1: bin_count already holds the gate's counts for the dispatch
   int4 *tile_rec;       // [max tiles] {first item, rows, bin, first token of the block}
   uint32_t *items;      // [T*Hp*(k-1)]

@@ -174,12 +174,11 @@ typedef struct moba_layout {
   /* dispatch tables over bins b = p*NBb + global_block (p < P), uint32:
    * count[P*NBb], offset[P*NBb+1], tile_offset[P*NBb+1] (tiles of the
    * attention kernel's query rows: 256 for bf16, 128 for float32),
-   * cursor[P*NBb], 8 tile counters of the earlier-block attention, a flag
-   * (1: the gate already filled count, so moba_dispatch does not recount);
-   * then,
-   * 16-byte aligned, int32x4 tile records
+   * cursor[P*NBb], a flag (1: the gate already filled count, so
+   * moba_dispatch does not recount); then, 16-byte aligned, int32x4 tile records
    * [max_tiles] = {first item, rows, bin, first token of the bin's block},
-   * where max_tiles = ceil(T*Hp*(topk-1)/128) + P*NBb bounds the tile count. */
+   * where max_tiles = ceil(T*Hp*(topk-1)/R) + P*NBb, with R the query rows
+   * of a tile above, bounds the tile count. */
   size_t bins_offset;
   /* uint32 items[T*Hp*(topk-1)]: per bin, the slots (t*Hp + hl)*topk + s that
    * chose the bin's block as an earlier block (order inside a bin unspecified). */
