@@ -44,8 +44,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "72d38011e2f174fda2748ae3a39ebf74106135bafb514aab9f4f0c05cf0f7562",
-    "fetch_kib": 20738297.7, "write_kib": 25350048.9,
+    "sha256": "16a3d792e0590bbe4a70f10d3b40eb9f70ef91a72627172e2ee8d711db39b945",
+    "fetch_kib": 20524519.6, "write_kib": 25349784.7,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 

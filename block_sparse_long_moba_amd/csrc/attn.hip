@@ -85,6 +85,17 @@ struct PolBf16 {
   }
 };
 
+// Own-block attention, bf16: half the rows per workgroup and two workgroups
+// per CU. The own block's runs are short (1 to B/64 key tiles, the first
+// ones among them), so the first loads of a run (query rows, first key and
+// value tiles) are a large share of its time; the other workgroup on the CU
+// computes meanwhile.
+struct PolBf16Own : PolBf16 {
+  static constexpr int kRows = kRowTile;
+  static constexpr int kThreads = 2 * kRows;
+  static constexpr int kOcc = 2;
+};
+
 // fp32 inputs: v_mfma_f32_32x32x2f32 (lane l holds A[l%32][l/32], B[l/32][l%32]).
 struct PolF32 {
   using T = float;
@@ -641,6 +652,9 @@ template <class Pol> struct LdsBytes {
   static constexpr int value = 2 * (kKeyTile * Pol::KP + kHeadDim * Pol::VP) * (int)sizeof(typename Pol::T);
 };
 template <> struct LdsBytes<PolBf16> { static constexpr int value = Direct<PolBf16::kStages>::BYTES; };
+template <> struct LdsBytes<PolBf16Own> {
+  static constexpr int value = Direct<PolBf16Own::kStages>::BYTES;
+};
 
 template <class Pol, int MODE>
 __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const AttnArgs a) {
@@ -754,7 +768,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
 
   const T *ktile = kbase + kbeg * kstride;
   const int64_t rows_after = a.T - kbeg;  // K rows from kbeg to the end of the tensor
-  if constexpr (std::is_same<Pol, PolBf16>::value)
+  if constexpr (std::is_same<T, __bf16>::value)
     tiles_direct<MODE, Pol::kThreads / 64, Pol::kStages, Pol::kLoadAhead>(
         lds, ktile, (uint32_t)kstride, rows_after, vt0, vstep, (uint32_t)vstride, nkt, qr, qfirst,
         qpos, a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l);
@@ -816,9 +830,15 @@ hipError_t launch_mode(bool bf16, dim3 grid, const AttnArgs &a, hipStream_t s) {
 hipError_t launch_attn_diag(const Problem &pb, const Work &w, const void *q, const void *k, int g0,
                             hipStream_t s) {
   const AttnArgs a = base_args(pb, w, q, k, g0);
-  const int64_t nq = (pb.B + pb.rows - 1) / pb.rows;
+  const int rows = pb.bf16 ? PolBf16Own::kRows : PolF32::kRows;
+  const int64_t nq = (pb.B + rows - 1) / rows;
   const int64_t grid = (pb.Hp * pb.NBb * nq + 7) / 8 * 8;
-  return launch_mode<MODE_DIAG>(pb.bf16, dim3((unsigned)grid), a, s);
+  if (grid == 0) return hipSuccess;
+  if (pb.bf16)
+    attn_kernel<PolBf16Own, MODE_DIAG><<<dim3((unsigned)grid), PolBf16Own::kThreads, 0, s>>>(a);
+  else
+    attn_kernel<PolF32, MODE_DIAG><<<dim3((unsigned)grid), PolF32::kThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, const void *k, int g0,
