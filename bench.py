@@ -44,8 +44,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "16a3d792e0590bbe4a70f10d3b40eb9f70ef91a72627172e2ee8d711db39b945",
-    "fetch_kib": 20524519.6, "write_kib": 25349784.7,
+    "sha256": "eb4a426cee6eecb874f39d456c0845415c8612aff9314202e15bc3200a9f5704",
+    "fetch_kib": 20846990.8, "write_kib": 25350336.9,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 
@@ -242,9 +242,18 @@ def forward_bench(args, name, headline):
         for g0 in passes:
             tm.run("gate", lambda: gate(g0))
             tm.run("dispatch", lambda: moba.moba_dispatch(shape, B, k, lay, ws, g0))
-            tm.run("attn_diag", lambda: moba.moba_attn_fwd_diag(q, kk, v, shape, B, k, lay, ws, g0))
-            tm.run("attn_hist", lambda: moba.moba_attn_fwd_hist(q, kk, shape, B, k, lay, ws, g0))
-            tm.run("merge", lambda: moba.moba_merge(shape, B, k, lay, ws, out, lse, g0))
+            if w.dtype == "bf16":  # as moba_fwd runs it: the own block merged last
+                tm.run("attn_prep", lambda: moba.moba_attn_prep(kk, v, shape, B, k, lay, ws, g0))
+                tm.run("attn_hist", lambda: moba.moba_attn_fwd_hist(q, kk, shape, B, k, lay, ws,
+                                                                     g0))
+                tm.run("attn_own_merge", lambda: moba.moba_attn_fwd_own_merge(
+                    q, kk, shape, B, k, lay, ws, out, lse, g0))
+            else:
+                tm.run("attn_diag", lambda: moba.moba_attn_fwd_diag(q, kk, v, shape, B, k, lay,
+                                                                     ws, g0))
+                tm.run("attn_hist", lambda: moba.moba_attn_fwd_hist(q, kk, shape, B, k, lay, ws,
+                                                                     g0))
+                tm.run("merge", lambda: moba.moba_merge(shape, B, k, lay, ws, out, lse, g0))
 
     # earlier-block rows dispatched per pass (for the dominant kernel's flops),
     # and whether the gate counted them (then the dispatch reads idx once)
@@ -322,17 +331,23 @@ def forward_bench(args, name, headline):
     n_hist = sum(hist_rows)
     idx_reads = sum(1 if c else 2 for c in gate_counted) / len(passes)
     disp_bytes = int(idx_reads * T * Hq * k * 4) + n_hist * 4
-    # merge: every valid slot's partial (row and lse) read, out and lse written
+    # merge (float32): every valid slot's partial (row and lse) read, out and
+    # lse written
     merge_bytes = (n_hist + T * Hq) * (HEAD_DIM * es + 4) + T * Hq * (HEAD_DIM * es + 4)
+    # value transpose (bf16 stage of its own): values and keys read, vt written
+    prep_bytes = 3 * T * Hkv * HEAD_DIM * es
     hbm = {}
     for sname, nbytes in (("meanpool", mp_bytes), ("gate", gate_bytes), ("dispatch", disp_bytes),
-                          ("merge", merge_bytes)):
-        sm = stages[sname][0]
+                          ("attn_prep", prep_bytes), ("merge", merge_bytes)):
+        sm = stages[sname][0] if sname in stages else 0.0
         if nbytes == 0 or sm <= 0:
             continue
         hbm[sname] = {"ms": round(sm, 4), "GB/s": round(nbytes / (sm * 1e-3) / 1e9, 1),
                       "frac": round(nbytes / (sm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    attn_ms = stages["attn_diag"][0] + stages["attn_hist"][0]
+    # attention: own and earlier blocks (bf16: with the merge, done by the
+    # own-block kernel; float32: with the value transpose)
+    attn_ms = sum(st[0] for name, st in stages.items()
+                  if name.startswith("attn_") and name != "attn_prep")
     attn_eff = eff / (attn_ms * 1e-3) / 1e12
 
     dense = None

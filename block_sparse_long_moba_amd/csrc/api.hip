@@ -368,6 +368,12 @@ moba_status_t run_pass(const Problem &pb, const Work &w, const void *q, const vo
   MOBA_HIP(launch_vtrans(v, pb.vs, k, pb.ks, pb.bf16, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt,
                          w.knorm, s),
            "vtrans");
+  if (pb.bf16) {  // earlier blocks first, then the own block merged with them
+    MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
+    MOBA_HIP(launch_attn_own_merge(pb, w, q, k, g0, out, lse, s), "attn_own_merge");
+    MOBA_HIP(launch_nan_rows(pb, w, g0, out, lse, s), "nan_rows");
+    return MOBA_SUCCESS;
+  }
   MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
   MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
   MOBA_HIP(launch_merge(pb, w, g0, out, lse, s), "merge");
@@ -742,6 +748,47 @@ moba_status_t moba_attn_fwd_hist(const void *q, const void *k, const moba_shape_
   Problem pb = make_problem(sh, B, topk, scale, L);
   Work w = carve(pb, L, ws);
   MOBA_HIP(launch_attn_hist(pb, w, q, k, g0, s), "attn_hist");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_prep(const void *k, const void *v, const moba_shape_t *sh, int32_t B,
+                             int32_t topk, const moba_layout_t *L, void *ws, int32_t g0,
+                             hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!k || !v) return fail(MOBA_ERROR_INVALID_VALUE, "k and v must be non-NULL");
+  Problem pb = make_problem(sh, B, topk, 0.f, L);
+  Work w = carve(pb, L, ws);
+  MOBA_HIP(launch_vtrans(v, pb.vs, k, pb.ks, pb.bf16, g0, pb.P, pb.NBb, pb.B, w.blk_info, w.vt,
+                         w.knorm, s),
+           "vtrans");
+  return MOBA_SUCCESS;
+}
+
+moba_status_t moba_attn_fwd_own_merge(const void *q, const void *k, const moba_shape_t *sh,
+                                      int32_t B, int32_t topk, float scale,
+                                      const moba_layout_t *L, void *ws, int32_t g0, void *out,
+                                      float *lse, hipStream_t s) {
+  moba_layout_t f;
+  moba_status_t st = check_stage(sh, B, topk, L, ws, &f);
+  if (st != MOBA_SUCCESS) return st;
+  if (!(scale >= 0.f) || isinf(scale)) return fail(MOBA_ERROR_INVALID_VALUE, "bad softmax_scale");
+  if (sh->total_tokens == 0) return MOBA_SUCCESS;
+  if ((st = check_pass(sh, L, g0)) != MOBA_SUCCESS) return st;
+  if (!q || !k) return fail(MOBA_ERROR_INVALID_VALUE, "q and k must be non-NULL");
+  if (!out) return fail(MOBA_ERROR_INVALID_VALUE, "out is NULL");
+  Problem pb = make_problem(sh, B, topk, scale, L);
+  Work w = carve(pb, L, ws);
+  if (pb.bf16) {
+    MOBA_HIP(launch_attn_own_merge(pb, w, q, k, g0, out, lse, s), "attn_own_merge");
+    MOBA_HIP(launch_nan_rows(pb, w, g0, out, lse, s), "nan_rows");
+  } else {
+    MOBA_HIP(launch_attn_diag(pb, w, q, k, g0, s), "attn_diag");
+    MOBA_HIP(launch_merge(pb, w, g0, out, lse, s), "merge");
+  }
   return MOBA_SUCCESS;
 }
 

@@ -192,7 +192,9 @@ constexpr float kRescaleSlack = 8.0f;
 // result is the same (l uses the same reference).
 constexpr float kBoundSlack = 64.0f;
 
-enum { MODE_HIST = 0, MODE_DIAG = 1, MODE_DENSE = 2 };
+// MODE_OWN_MERGE: the own block, merged with the earlier blocks' partial
+// results into the final output (bf16).
+enum { MODE_HIST = 0, MODE_DIAG = 1, MODE_DENSE = 2, MODE_OWN_MERGE = 3 };
 
 struct AttnArgs {
   const void *q, *k, *vt;
@@ -208,7 +210,7 @@ struct AttnArgs {
   const uint32_t *tile_off, *bin_off, *items;
   const int4 *tile_rec;
   int64_t nbins;
-  // partial outputs (MoBA) or final outputs (dense)
+  // partial outputs (MoBA) or final outputs (dense, own block merged)
   void *part_o;
   float *part_lse;
   // dense: 64-row key tiles of each sequence (first tile index) and the
@@ -648,6 +650,144 @@ __device__ __forceinline__ void tiles_staged(typename Pol::T *lds, const typenam
   }
 }
 
+// The own block's results of a workgroup's rows, merged with the rows'
+// earlier-block partial results (part_o / part_lse, written by the
+// earlier-block attention of this pass) into out and lse, with the
+// arithmetic of merge_kernel in the same order: the maximum lse,
+// exp(lse - max) summed per slot group s % 16 and the 16 group sums pairwise
+// (i, i + 8), (i, i + 4), (i, i + 2), (i, i + 1), then the weighted parts
+// added in ascending slot order with the own block's last. The own block's
+// part enters rounded to bf16, as it would be read back from part_o, so the
+// result has the bits of the own-block kernel followed by merge_kernel.
+// Called by every lane after the tile loop's last barrier (LDS is free).
+// Phase A: each lane of row n (two per row, in the MFMA layout: lane half hh
+// holds the 4-column chunks 4 hh + 8 j) computes the row's weights and puts
+// them, the row's lse and its rounded own part in the wave's LDS area.
+// Phase B: 16 lanes per row, lane j holding columns 8 j .. 8 j + 7 of rows
+// g, g + 4, ..., g + 28 (g = lane / 16), read the partial rows 16 bytes per
+// lane, as merge_kernel does, and write out.
+struct MergeLds {
+  static constexpr int OWN = 0;        // 32 rows x 256 B: the own part, bf16
+  static constexpr int W = 8192;       // 32 rows x 16 weights of the first 16 slots
+  static constexpr int L = W + 2048;   // 32 rows: the merged lse
+  static constexpr int WO = L + 128;   // 32 rows: the own part's weight
+  static constexpr int WAVE = 16384;   // bytes per wave
+};
+__device__ __forceinline__ void merge_own(const AttnArgs &a, char *lds, const floatx16 (&o)[4],
+                                          float inv, float lse_own, int64_t t0, int wave_row0,
+                                          int nrows, int hq, int hl, int nsel) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  constexpr int kBatch = 2;  // slots in flight per lane (8 rows each)
+  const int lane = threadIdx.x & 63;
+  const int nh = nsel - 1;   // earlier-block slots
+  char *const base = lds + (threadIdx.x >> 6) * MergeLds::WAVE;
+  auto slot0_of = [&](int row) { return ((t0 + row) * a.Hp + hl) * (int64_t)a.topk; };
+  {  // phase A
+    const int n = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][4 * aa + e] * inv);
+        *(bf16x4 *)(base + MergeLds::OWN + n * 256 + (32 * dt + 8 * aa + 4 * hh) * 2) = v;
+      }
+    if (wave_row0 + n < nrows) {
+      const float *pl = a.part_lse + slot0_of(wave_row0 + n);
+      float x16[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) x16[u] = u < nh ? pl[u] : u == nh ? lse_own : -INFINITY;
+      auto x_of = [&](int sl) { return sl < nh ? pl[sl] : sl == nh ? lse_own : -INFINITY; };
+      float m = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) m = fmaxf(m, x16[u]);
+      for (int sl = 16; sl < nsel; ++sl) m = fmaxf(m, x_of(sl));
+      float su[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        su[u] = x16[u] > -INFINITY ? __builtin_amdgcn_exp2f((x16[u] - m) * kLog2e) : 0.f;
+      for (int i0 = 16; i0 < nsel; i0 += 16) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float x = x_of(i0 + u);
+          if (x > -INFINITY) su[u] += __builtin_amdgcn_exp2f((x - m) * kLog2e);
+        }
+      }
+#pragma unroll
+      for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+        for (int u = 0; u < w; ++u) su[u] += su[u + w];
+      const float L = m + logf(su[0]);
+      if (hh == 0) {
+        float wt[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          wt[u] = u < nh && x16[u] > -INFINITY ? __builtin_amdgcn_exp2f((x16[u] - L) * kLog2e)
+                                               : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; u += 4)
+          *(float4 *)(base + MergeLds::W + n * 64 + 4 * u) =
+              make_float4(wt[u], wt[u + 1], wt[u + 2], wt[u + 3]);
+        *(float *)(base + MergeLds::L + 4 * n) = L;
+        *(float *)(base + MergeLds::WO + 4 * n) = __builtin_amdgcn_exp2f((lse_own - L) * kLog2e);
+      }
+    }
+  }
+  __syncthreads();
+  // phase B
+  const int g = lane >> 4, j = lane & 15;
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
+  bool ok[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ok[i] = wave_row0 + g + 4 * i < nrows;
+  const __bf16 *po = (const __bf16 *)a.part_o + 8 * j;
+  auto weight = [&](int i, int sl) {
+    const int n = g + 4 * i;
+    if (sl < 16) return *(const float *)(base + MergeLds::W + n * 64 + 4 * sl);
+    const float x = a.part_lse[slot0_of(wave_row0 + n) + sl];
+    const float L = *(const float *)(base + MergeLds::L + 4 * n);
+    return x > -INFINITY ? __builtin_amdgcn_exp2f((x - L) * kLog2e) : 0.f;
+  };
+  for (int sl = 0; sl < nh; sl += kBatch) {
+    float w[kBatch][8];
+    bf16x8 v[kBatch][8];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w[b][i] = ok[i] && sl + b < nh ? weight(i, sl + b) : 0.f;
+        v[b][i] = w[b][i] != 0.f
+                      ? *(const bf16x8 *)(po + (slot0_of(wave_row0 + g + 4 * i) + sl + b) * kHeadDim)
+                      : bf16x8{};
+      }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(w[b][i], (float)v[b][i][c], acc[i][c]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (!ok[i]) continue;
+    const int n = g + 4 * i;
+    const float wo = *(const float *)(base + MergeLds::WO + 4 * n);
+    const bf16x8 vo = *(const bf16x8 *)(base + MergeLds::OWN + n * 256 + 16 * j);
+    bf16x8 res;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) res[c] = (__bf16)fmaf(wo, (float)vo[c], acc[i][c]);
+    const int64_t t = t0 + wave_row0 + n;
+    *(bf16x8 *)((__bf16 *)a.out + t * a.os.t + hq * a.os.h + 8 * j) = res;
+    if (j == 0 && a.lse) a.lse[(int64_t)hq * a.T + t] = *(const float *)(base + MergeLds::L + 4 * n);
+  }
+}
+
 template <class Pol> struct LdsBytes {
   static constexpr int value = 2 * (kKeyTile * Pol::KP + kHeadDim * Pol::VP) * (int)sizeof(typename Pol::T);
 };
@@ -671,6 +811,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   int qpos = 0, qfirst = 0;     // causal modes: positions relative to kbeg
   const T *vt0;
   float kn_run;                 // largest key norm over the keys of the run
+  int nsel = 0;                 // own block: the row's slots (the own block's is the last)
 
   if (MODE == MODE_HIST) {
     // XCD-aware order: workgroup i runs on XCD i % 8; give every XCD a
@@ -696,7 +837,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     kn_run = a.knorm[(int64_t)p * a.NBb + gb];
     vstep = kKeyTile;
     vstride = a.B;
-  } else if (MODE == MODE_DIAG) {
+  } else if (MODE == MODE_DIAG || MODE == MODE_OWN_MERGE) {
     // Work item w runs over (kv head of the pass, block, query tile with the
     // most keys first, query head of the group). Workgroup i runs on XCD
     // i % 8 and every XCD takes a contiguous run of w, so the tiles that read
@@ -724,7 +865,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     const int kend = min(bi.z, qfirst + ROWS);
     nkt = (kend + kKeyTile - 1) / kKeyTile;
     kbeg = bi.y;
-    const int nsel = min(a.topk, bi.w + 1);  // own block is the last chosen slot
+    nsel = min(a.topk, bi.w + 1);  // own block is the last chosen slot
     slot = (t * a.Hp + hl) * a.topk + nsel - 1;
     vt0 = (const T *)a.vt + ((int64_t)(g - a.g0) * a.NBb + gb) * kHeadDim * a.B;
     kn_run = a.knorm[(int64_t)(g - a.g0) * a.NBb + gb];  // the whole block: a valid bound
@@ -779,8 +920,14 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.f / lt;
   const float lse = (m + __log2f(lt)) * kLn2;
+  if constexpr (MODE == MODE_OWN_MERGE) {
+    static_assert(std::is_same<T, __bf16>::value, "merged own block: bf16 only");
+    static_assert(Pol::kThreads / 64 * MergeLds::WAVE <= LdsBytes<Pol>::value, "merge LDS");
+    merge_own(a, lds, o, inv, lse, t - (valid ? r : 0), wave * 32, nrows, hq, hq - a.h0, nsel);
+    return;
+  }
   if (!valid) return;
-  if (MODE != MODE_DENSE) {
+  if constexpr (MODE != MODE_DENSE) {
     T *dst = (T *)a.part_o + slot * kHeadDim + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -838,6 +985,19 @@ hipError_t launch_attn_diag(const Problem &pb, const Work &w, const void *q, con
     attn_kernel<PolBf16Own, MODE_DIAG><<<dim3((unsigned)grid), PolBf16Own::kThreads, 0, s>>>(a);
   else
     attn_kernel<PolF32, MODE_DIAG><<<dim3((unsigned)grid), PolF32::kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_own_merge(const Problem &pb, const Work &w, const void *q, const void *k,
+                                int g0, void *out, float *lse, hipStream_t s) {
+  if (!pb.bf16) return hipErrorInvalidValue;
+  AttnArgs a = base_args(pb, w, q, k, g0);
+  a.out = out;
+  a.lse = lse;
+  const int64_t nq = (pb.B + PolBf16Own::kRows - 1) / PolBf16Own::kRows;
+  const int64_t grid = (pb.Hp * pb.NBb * nq + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  attn_kernel<PolBf16Own, MODE_OWN_MERGE><<<dim3((unsigned)grid), PolBf16Own::kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,14 @@ hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, con
                             int g0, hipStream_t s);
 hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, float *lse,
                         hipStream_t s);
+// bf16: the own-block attention merged with the earlier-block partial results
+// (which must be in part_o / part_lse) into out and lse, with the bits of
+// launch_attn_diag followed by launch_merge.
+hipError_t launch_attn_own_merge(const Problem &pb, const Work &w, const void *q, const void *k,
+                                 int g0, void *out, float *lse, hipStream_t s);
+// NaN into the pass's rows of out and lse when the input check failed.
+hipError_t launch_nan_rows(const Problem &pb, const Work &w, int g0, void *out, float *lse,
+                           hipStream_t s);
 int decode_splits(int S, int Hq, int Hkv, int B, int k, int maxblk);
 hipError_t launch_decode(const Problem &pb, const Work &w, const void *q, const void *kc,
                          const void *vc, void *out, float *lse, hipStream_t s);

@@ -411,7 +411,47 @@ __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_
   if (lane == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = L;
 }
 
+// NaN in every output row of the pass and its lse when the sequence-table
+// scan rejected the input (*status != 0); returns at once otherwise. Chunk c
+// of row (t, hl) is 16 bytes of out.
+template <typename TO>
+__global__ __launch_bounds__(256) void nan_rows_kernel(const int32_t *__restrict__ status,
+                                                       int64_t T_, int h0, int Hp,
+                                                       TO *__restrict__ out, RowHead os,
+                                                       float *__restrict__ lse_out) {
+  if (*status == 0) return;
+  constexpr int N = 16 / sizeof(TO);
+  constexpr int C = kHeadDim / N;
+  TO nan[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) nan[j] = (TO)NAN;
+  const int64_t n = T_ * Hp * C;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / C;
+    const int c = (int)(i % C);
+    const int64_t t = row / Hp;
+    const int hl = (int)(row % Hp);
+    *(uint4 *)(out + t * os.t + (h0 + hl) * os.h + c * N) = *(const uint4 *)nan;
+    if (c == 0 && lse_out) lse_out[(int64_t)(h0 + hl) * T_ + t] = NAN;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_nan_rows(const Problem &pb, const Work &w, int g0, void *out, float *lse,
+                           hipStream_t s) {
+  const int64_t chunks = pb.T * pb.Hp * (pb.bf16 ? 16 : 32);
+  if (chunks == 0) return hipSuccess;
+  const dim3 grid((unsigned)std::min<int64_t>((chunks + 255) / 256, 1024));
+  const int h0 = g0 * pb.G;
+  if (pb.bf16)
+    nan_rows_kernel<__bf16><<<grid, 256, 0, s>>>(w.status, pb.T, h0, pb.Hp, (__bf16 *)out, pb.os,
+                                                 lse);
+  else
+    nan_rows_kernel<float><<<grid, 256, 0, s>>>(w.status, pb.T, h0, pb.Hp, (float *)out, pb.os,
+                                                lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_u32(uint32_t *p, uint32_t value, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

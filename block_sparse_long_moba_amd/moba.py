@@ -23,7 +23,8 @@ EXPORTS = ["moba_status_string", "moba_last_error", "moba_workspace_status", "mo
            "moba_fwd_workspace_size",
            "moba_seqtable", "moba_meanpool", "moba_gate", "moba_minmaxpool", "moba_gate_window",
            "moba_gate_pooled", "moba_dispatch", "moba_attn_fwd", "moba_attn_fwd_diag",
-           "moba_attn_fwd_hist", "moba_merge", "moba_fwd_ex", "moba_fwd_gated",
+           "moba_attn_fwd_hist", "moba_merge", "moba_attn_prep", "moba_attn_fwd_own_merge",
+           "moba_fwd_ex", "moba_fwd_gated",
            "moba_fwd_strided", "moba_fwd", "moba_fwd_noalloc",
            "moba_decode_workspace_size", "moba_decode_prepare", "moba_decode",
            "moba_bwd_plan", "moba_bwd_workspace_size", "moba_bwd", "moba_bwd_delta",
@@ -111,6 +112,8 @@ def lib():
             "moba_attn_fwd_diag": ([P, P, P, S, I32, I32, F, LP, P, I32, P], I32),
             "moba_attn_fwd_hist": ([P, P, S, I32, I32, F, LP, P, I32, P], I32),
             "moba_merge": ([S, I32, I32, LP, P, I32, P, P, P], I32),
+            "moba_attn_prep": ([P, P, S, I32, I32, LP, P, I32, P], I32),
+            "moba_attn_fwd_own_merge": ([P, P, S, I32, I32, F, LP, P, I32, P, P, P], I32),
             "moba_fwd_ex": ([P, P, P, P, S, I32, I32, F, P, P, P, Z, P], I32),
             "moba_fwd_gated": ([P, P, P, P, S, I32, I32, ctypes.POINTER(Gate), F, P, P, P, Z,
                                 P], I32),
@@ -251,6 +254,20 @@ def moba_merge(shape, block_size, topk, layout, workspace, out, lse=None, kv_hea
     _check(lib().moba_merge(ctypes.byref(shape), block_size, topk, ctypes.byref(layout),
                             _ptr(workspace), kv_head_begin, _ptr(out), _ptr(lse),
                             _stream(stream)))
+
+
+def moba_attn_prep(k, v, shape, block_size, topk, layout, workspace, kv_head_begin=0,
+                   stream=None):
+    _check(lib().moba_attn_prep(_ptr(k), _ptr(v), ctypes.byref(shape), block_size, topk,
+                                ctypes.byref(layout), _ptr(workspace), kv_head_begin,
+                                _stream(stream)))
+
+
+def moba_attn_fwd_own_merge(q, k, shape, block_size, topk, layout, workspace, out, lse=None,
+                            kv_head_begin=0, softmax_scale=0.0, stream=None):
+    _check(lib().moba_attn_fwd_own_merge(_ptr(q), _ptr(k), ctypes.byref(shape), block_size, topk,
+                                         softmax_scale, ctypes.byref(layout), _ptr(workspace),
+                                         kv_head_begin, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def _contiguous(**tensors):

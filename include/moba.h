@@ -290,7 +290,7 @@ moba_status_t moba_attn_fwd(const void *q, const void *k, const void *v,
 /* The two halves of moba_attn_fwd, for callers that time or overlap them:
  * _diag transposes the pass's values into vt and runs the own-block (causal)
  * attention; _hist runs the earlier-block attention over the dispatched bins
- * and needs vt from _diag of the same pass. */
+ * and needs vt from _diag (or moba_attn_prep) of the same pass. */
 moba_status_t moba_attn_fwd_diag(const void *q, const void *k, const void *v,
                                  const moba_shape_t *shape, int32_t block_size, int32_t topk,
                                  float softmax_scale, const moba_layout_t *layout,
@@ -308,6 +308,24 @@ moba_status_t moba_attn_fwd_hist(const void *q, const void *k, const moba_shape_
 moba_status_t moba_merge(const moba_shape_t *shape, int32_t block_size, int32_t topk,
                          const moba_layout_t *layout, void *workspace, int32_t kv_head_begin,
                          void *out, float *lse, hipStream_t stream);
+
+/* Steps 3 and 4 with the own block last, as moba_fwd runs them: _prep
+ * transposes the pass's values into vt and takes the largest key norm of
+ * every block; moba_attn_fwd_hist (after _prep) writes the earlier-block
+ * partial results; _own_merge then runs the own-block (causal) attention and
+ * combines it with those partial results into out and lse (lse may be NULL),
+ * with the same bits as moba_attn_fwd_diag followed by moba_merge. For bf16
+ * it is one kernel and the own block's partial result is never stored; for
+ * float32 it runs those two stages. Like moba_merge it writes NaN to the
+ * pass's rows of out and lse when moba_seqtable rejected cu_seqlens. */
+moba_status_t moba_attn_prep(const void *k, const void *v, const moba_shape_t *shape,
+                             int32_t block_size, int32_t topk, const moba_layout_t *layout,
+                             void *workspace, int32_t kv_head_begin, hipStream_t stream);
+moba_status_t moba_attn_fwd_own_merge(const void *q, const void *k, const moba_shape_t *shape,
+                                      int32_t block_size, int32_t topk, float softmax_scale,
+                                      const moba_layout_t *layout, void *workspace,
+                                      int32_t kv_head_begin, void *out, float *lse,
+                                      hipStream_t stream);
 
 /* ---- Whole forward pass. */
 

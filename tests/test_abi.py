@@ -104,6 +104,19 @@ def test_entry_points_reject_null_arguments_without_a_device():
     assert L.moba_gate(fake, ctypes.byref(sh), 4096, 12, ctypes.byref(lay1), fake, 1, null) == 1
     assert L.moba_merge(ctypes.byref(sh), 4096, 12, ctypes.byref(lay), fake, 0, null, null,
                         null) == 1
+    # the merged own-block stage: null out, bad scale, kv_head_begin off the pass
+    assert L.moba_attn_fwd_own_merge(fake, fake, ctypes.byref(sh), 4096, 12, 0.0,
+                                     ctypes.byref(lay), fake, 0, null, null, null) == 1
+    assert b"out" in L.moba_last_error()
+    assert L.moba_attn_fwd_own_merge(fake, fake, ctypes.byref(sh), 4096, 12, -1.0,
+                                     ctypes.byref(lay), fake, 0, fake, null, null) == 1
+    assert L.moba_attn_fwd_own_merge(fake, fake, ctypes.byref(sh), 4096, 12, 0.0,
+                                     ctypes.byref(lay1), fake, 1, fake, null, null) == 1
+    # the value-transpose stage: null v, mismatched layout
+    assert L.moba_attn_prep(fake, null, ctypes.byref(sh), 4096, 12, ctypes.byref(lay), fake, 0,
+                            null) == 1
+    assert L.moba_attn_prep(fake, fake, ctypes.byref(sh), 4096, 12, ctypes.byref(other), fake, 0,
+                            null) == 1
     # dense: bad scale / too small workspace
     assert L.moba_dense_causal_fwd(fake, fake, fake, fake, ctypes.byref(sh), float("nan"), fake,
                                    null, null, 0, null) == 1
@@ -218,6 +231,8 @@ def test_bwd_plan_and_validation():
                                 ctypes.byref(f), fake, 0, fake, fake, null) == 1
     assert L.moba_attn_fwd_hist(fake, fake, ctypes.byref(sh), 4096, 12, 0.0, ctypes.byref(b),
                                 fake, 0, null) == 1
+    assert L.moba_attn_fwd_own_merge(fake, fake, ctypes.byref(sh), 4096, 12, 0.0,
+                                     ctypes.byref(b), fake, 0, fake, null, null) == 1
     assert L.moba_attn_bwd_dq(fake, fake, fake, fake, fake, ctypes.byref(sh), 4096, 12, 0.0,
                               ctypes.byref(b), fake, 0, 4, null) == 1
     # the gate and dispatch stages take either plan: the layout check passes and
