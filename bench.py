@@ -44,8 +44,8 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "eb4a426cee6eecb874f39d456c0845415c8612aff9314202e15bc3200a9f5704",
-    "fetch_kib": 20846990.8, "write_kib": 25350336.9,
+    "sha256": "985d6a8102c6bc2c867e349d86a58d22b9a143d4f543ac8afecae468e6589e8a",
+    "fetch_kib": 19616342.1, "write_kib": 25350207.3,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }
 

@@ -796,11 +796,11 @@ template <> struct LdsBytes<PolBf16Own> {
   static constexpr int value = Direct<PolBf16Own::kStages>::BYTES;
 };
 
+// One work item of the attention kernel: bx stands for the workgroup index.
 template <class Pol, int MODE>
-__global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const AttnArgs a) {
+__device__ __forceinline__ void attn_tile(const AttnArgs &a, char *lds, const uint32_t bx) {
   constexpr int ROWS = Pol::kRows;
   using T = typename Pol::T;
-  __shared__ __attribute__((aligned(1024))) char lds[LdsBytes<Pol>::value];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
   const int r = wave * 32 + n;  // this lane's query row inside the tile
@@ -815,12 +815,13 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
 
   if (MODE == MODE_HIST) {
     // XCD-aware order: workgroup i runs on XCD i % 8; give every XCD a
-    // contiguous run of tiles so the tiles of one block share its L2.
+    // contiguous run of tiles so the tiles of one block share its L2 (bx is
+    // the workgroup's index, or for bf16 one of its consecutive tiles).
     const uint32_t ntiles = a.tile_off[a.nbins];
     const uint32_t per = (ntiles + 7) >> 3;
-    const uint32_t jj = blockIdx.x >> 3;
+    const uint32_t jj = bx >> 3;
     if (jj >= per) return;
-    const uint32_t tile = (blockIdx.x & 7) * per + jj;
+    const uint32_t tile = (bx & 7) * per + jj;
     if (tile >= ntiles) return;
     const int4 rec = a.tile_rec[tile];
     const int p = (int)((uint32_t)rec.z / a.NBb);
@@ -845,9 +846,9 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     const int nq = (a.B + ROWS - 1) / ROWS;
     const uint32_t total = (uint32_t)(a.Hp * a.NBb * nq);
     const uint32_t per = (total + 7) >> 3;
-    const uint32_t jj = blockIdx.x >> 3;
+    const uint32_t jj = bx >> 3;
     if (jj >= per) return;
-    const uint32_t wi = (blockIdx.x & 7) * per + jj;
+    const uint32_t wi = (bx & 7) * per + jj;
     if (wi >= total) return;
     uint32_t rest = wi / (uint32_t)a.G;
     const int qt = nq - 1 - (int)(rest % (uint32_t)nq);
@@ -873,7 +874,7 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
     vstride = a.B;
   } else {  // MODE_DENSE
     // query tiles from the last (most keys) to the first
-    const int4 bi = a.qtiles[a.NBq - 1 - (int64_t)blockIdx.x];
+    const int4 bi = a.qtiles[a.NBq - 1 - (int64_t)bx];
     if (bi.x < 0) return;
     hq = blockIdx.y;
     g = hq / a.G;
@@ -948,6 +949,23 @@ __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const At
   }
 }
 
+// Earlier-block tiles per workgroup (bf16): a workgroup starts its next tile
+// while the partial results of the previous one are still being written.
+constexpr uint32_t kHistTilesPerWg = 2;
+
+template <class Pol, int MODE>
+__global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[LdsBytes<Pol>::value];
+  if constexpr (MODE == MODE_HIST && std::is_same<typename Pol::T, __bf16>::value) {
+    // workgroup i takes tiles j, j + 1 of XCD i % 8's range, j = 2 (i / 8)
+    for (uint32_t it = 0; it < kHistTilesPerWg; ++it)
+      attn_tile<Pol, MODE>(a, lds,
+                           ((blockIdx.x >> 3) * kHistTilesPerWg + it) << 3 | (blockIdx.x & 7));
+  } else {
+    attn_tile<Pol, MODE>(a, lds, blockIdx.x);
+  }
+}
+
 AttnArgs base_args(const Problem &pb, const Work &w, const void *q, const void *k, int g0) {
   AttnArgs a{};
   a.q = q; a.k = k; a.vt = w.vt; a.knorm = w.knorm;
@@ -1005,7 +1023,8 @@ hipError_t launch_attn_hist(const Problem &pb, const Work &w, const void *q, con
                             hipStream_t s) {
   if (pb.k <= 1) return hipSuccess;
   const AttnArgs a = base_args(pb, w, q, k, g0);
-  const int64_t grid = (w.max_tiles + 7) / 8 * 8;
+  const int64_t per = (w.max_tiles + 7) / 8;  // tiles per XCD, at most
+  const int64_t grid = pb.bf16 ? 8 * ((per + kHistTilesPerWg - 1) / kHistTilesPerWg) : 8 * per;
   return launch_mode<MODE_HIST>(pb.bf16, dim3((unsigned)grid), a, s);
 }
 
