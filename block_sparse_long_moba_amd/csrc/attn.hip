@@ -322,11 +322,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base,
                                            kBufferWord3);
 }
 
-__device__ __forceinline__ void wait_loads_and_sync() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
 // Wait until at most N vector memory loads of this wave are outstanding.
 // (Also waits for every LDS and scalar-cache access of the wave. Written
 // with the builtin so the compiler knows what is still pending afterwards.)
@@ -365,12 +360,16 @@ __device__ __forceinline__ float q_bound(const PolBf16::Q &qr, float c2) {
 
 // kn_run: the largest key norm over the run's tiles; qnc2 = c2 |q| of this
 // lane's query, so that qnc2 * kn_run bounds every scaled score of the run.
-template <int MODE, int NW, int NS, int A>
+// pre() runs after the prologue's loads are issued and returns how many
+// loads it issued itself (0 or NPRE per lane); those may stay in flight
+// until the end of the first body.
+template <int MODE, int NW, int NS, int A, int NPRE = 0, class Pre = int (*)()>
 __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, uint32_t kstride,
                                              int64_t rows_after, const __bf16 *vt0, int64_t vstep,
                                              uint32_t vstride, int nkt, const PolBf16::Q &qr,
                                              int qfirst, int qpos, float c2, float kn_run,
-                                             float qnc2, floatx16 (&o)[4], float &m, float &l) {
+                                             float qnc2, floatx16 (&o)[4], float &m, float &l,
+                                             Pre &&pre = nullptr) {
   constexpr bool CAUSAL = MODE != MODE_HIST;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
@@ -537,7 +536,11 @@ __device__ __forceinline__ void tiles_direct(char *lds, const __bf16 *ktile0, ui
   issue_k(0, D::K(0));
   if (nkt > 1) issue_k(1, D::K(1));
   issue_v(0, D::V(0));
-  wait_loads_and_sync();
+  int npre = 0;
+  if constexpr (NPRE > 0) npre = pre();
+  if (NPRE > 0 && npre) wait_vm<NPRE>();  // only pre()'s loads may be in flight
+  else wait_vm<0>();
+  __syncthreads();
   // the prologue's share: V^T tiles 1 .. A-1 and K tiles 2 .. A
 #pragma unroll
   for (int i = 1; i < A; ++i) {
@@ -791,7 +794,12 @@ __device__ __forceinline__ void merge_own(const AttnArgs &a, char *lds, const fl
 template <class Pol> struct LdsBytes {
   static constexpr int value = 2 * (kKeyTile * Pol::KP + kHeadDim * Pol::VP) * (int)sizeof(typename Pol::T);
 };
-template <> struct LdsBytes<PolBf16> { static constexpr int value = Direct<PolBf16::kStages>::BYTES; };
+// bf16: the tile buffers, then (earlier blocks) 8 KiB per wave where the
+// next tile's query rows land
+constexpr int kQStage = Direct<PolBf16::kStages>::BYTES;
+template <> struct LdsBytes<PolBf16> {
+  static constexpr int value = kQStage + PolBf16::kThreads / 64 * 8192;
+};
 template <> struct LdsBytes<PolBf16Own> {
   static constexpr int value = Direct<PolBf16Own::kStages>::BYTES;
 };
@@ -949,18 +957,98 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, char *lds, const ui
   }
 }
 
-// Earlier-block tiles per workgroup (bf16): a workgroup starts its next tile
-// while the partial results of the previous one are still being written.
+// Earlier-block tiles per workgroup (bf16).
 constexpr uint32_t kHistTilesPerWg = 2;
+
+typedef __attribute__((address_space(1))) const void *global_ptr_t;
+
+// One earlier-block tile (bf16): rec is its record, slot this lane's row's
+// slot; the query rows come from q, or (q_lds) from the wave's staging area
+// where the previous tile gathered them. With next_slot >= 0 (uniform
+// next != 0) the tile gathers the next tile's query rows (lane's row:
+// next_slot) into the staging area, behind its own first loads. Piece j of
+// lane l is chunk 2 j + hh of the lane's row, at 1024 j + 16 l: the MFMA
+// operand layout, read back without exchange between lanes.
+__device__ __forceinline__ void hist_tile(const AttnArgs &a, char *lds, const int4 rec,
+                                          int64_t slot, bool q_lds, bool next, int64_t next_slot) {
+  using Pol = PolBf16;
+  using T = __bf16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5;
+  const int r = wave * 32 + (lane & 31);
+  char *const qst = lds + kQStage + wave * 8192;
+  const int p = (int)((uint32_t)rec.z / a.NBb);
+  const int64_t gb = (uint32_t)rec.z % a.NBb;
+  const int nrows = rec.y;
+  const int nkt = a.B / kKeyTile;
+  const int64_t kbeg = rec.w;
+  const T *vt0 = (const T *)a.vt + ((int64_t)p * a.NBb + gb) * kHeadDim * a.B;
+  const float kn_run = a.knorm[(int64_t)p * a.NBb + gb];  // bins and norms share p * NBb + block
+  auto row_of = [&](int64_t sl) {
+    const int64_t th = sl / a.topk;
+    return (const T *)a.q + th / a.Hp * a.qs.t + (a.h0 + (int)(th % a.Hp)) * a.qs.h;
+  };
+  Pol::Q qr;
+  if (q_lds) {
+#pragma unroll
+    for (int j = 0; j < kHeadDim / 16; ++j) qr.v[j] = *(const bf16x8 *)(qst + 1024 * j + 16 * lane);
+  } else {
+    Pol::load_q(qr, row_of(slot), hh);
+  }
+  const T *ktile = (const T *)a.k + (a.g0 + p) * a.ks.h + kbeg * a.ks.t;
+  floatx16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  tiles_direct<MODE_HIST, Pol::kThreads / 64, Pol::kStages, Pol::kLoadAhead, kHeadDim / 16>(
+      lds, ktile, (uint32_t)a.ks.t, a.T - kbeg, vt0, (int64_t)kKeyTile, (uint32_t)a.B, nkt, qr, 0,
+      0, a.scale_log2, kn_run, q_bound(qr, a.scale_log2), o, m, l, [&]() {
+        if (!next) return 0;
+        const T *row = row_of(next_slot) + 8 * hh;
+#pragma unroll
+        for (int j = 0; j < kHeadDim / 16; ++j)
+          __builtin_amdgcn_global_load_lds((global_ptr_t)(row + 16 * j),
+                                           (lds_ptr_t)(qst + 1024 * j), 16, 0, 0);
+        return kHeadDim / 16;
+      });
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.f / lt;
+  if (r < nrows) {
+    T *dst = (T *)a.part_o + slot * kHeadDim + 4 * hh;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int aa = 0; aa < 4; ++aa)
+        store4<T>(dst + 32 * dt + 8 * aa, o[dt][4 * aa] * inv, o[dt][4 * aa + 1] * inv,
+                  o[dt][4 * aa + 2] * inv, o[dt][4 * aa + 3] * inv);
+    if (hh == 0) a.part_lse[slot] = (m + __log2f(lt)) * kLn2;
+  }
+}
 
 template <class Pol, int MODE>
 __global__ __launch_bounds__(Pol::kThreads, Pol::kOcc) void attn_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[LdsBytes<Pol>::value];
   if constexpr (MODE == MODE_HIST && std::is_same<typename Pol::T, __bf16>::value) {
-    // workgroup i takes tiles j, j + 1 of XCD i % 8's range, j = 2 (i / 8)
-    for (uint32_t it = 0; it < kHistTilesPerWg; ++it)
-      attn_tile<Pol, MODE>(a, lds,
-                           ((blockIdx.x >> 3) * kHistTilesPerWg + it) << 3 | (blockIdx.x & 7));
+    // Workgroup i takes tiles j, j + 1 of XCD x's range (x = i % 8,
+    // j = 2 (i / 8)): XCD-aware, so the tiles of one block run together on
+    // one XCD and share its L2. Both records and both items of each lane's
+    // row are read at the start; the second tile's query rows are gathered
+    // while the first tile runs, and its loads start while the first tile's
+    // partial results are still being written.
+    const uint32_t ntiles = a.tile_off[a.nbins];
+    const uint32_t per = (ntiles + 7) >> 3;
+    const uint32_t j = (blockIdx.x >> 3) * kHistTilesPerWg;
+    const uint32_t tile = (blockIdx.x & 7) * per + j;
+    if (j >= per || tile >= ntiles) return;
+    const bool second = j + 1 < per && tile + 1 < ntiles;
+    const int r = (int)(threadIdx.x >> 6) * 32 + (int)(threadIdx.x & 31);
+    const int4 rec0 = a.tile_rec[tile];
+    const int4 rec1 = second ? a.tile_rec[tile + 1] : rec0;
+    const int64_t slot0 = a.items[(uint32_t)rec0.x + min(r, rec0.y - 1)];
+    const int64_t slot1 = a.items[(uint32_t)rec1.x + min(r, rec1.y - 1)];
+    hist_tile(a, lds, rec0, slot0, false, second, slot1);
+    if (second) hist_tile(a, lds, rec1, slot1, true, false, 0);
   } else {
     attn_tile<Pol, MODE>(a, lds, blockIdx.x);
   }
