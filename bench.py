@@ -44,7 +44,7 @@ MEASURED_TRAFFIC = {
     "workload": "gqa32x8_t1m_b4096_k12_bf16",
     "sources": ["block_sparse_long_moba_amd/csrc/attn.hip",
                 "block_sparse_long_moba_amd/csrc/moba_internal.h"],
-    "sha256": "f28b2f8b1fa3c55644583aaaa02cefa6859f813f3a8d7a85fa1d9fd914f89a97",
+    "sha256": "1fe1c69cc251278854d90efb0865020158c4184c46a379604063f8adcc8aa746",
     "fetch_kib": 21416819.1, "write_kib": 25368006.1,
     "fetch_factor": 1.99998, "write_factor": 1.0,
 }

@@ -822,9 +822,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs &a, char *lds, const ui
   int nsel = 0;                 // own block: the row's slots (the own block's is the last)
 
   if (MODE == MODE_HIST) {
-    // XCD-aware order: workgroup i runs on XCD i % 8; give every XCD a
-    // contiguous run of tiles so the tiles of one block share its L2 (bx is
-    // the workgroup's index, or for bf16 one of its consecutive tiles).
+    // (float32; bf16 runs hist_tile.) XCD-aware order: workgroup i runs on
+    // XCD i % 8; give every XCD a contiguous run of tiles so the tiles of
+    // one block share its L2.
     const uint32_t ntiles = a.tile_off[a.nbins];
     const uint32_t per = (ntiles + 7) >> 3;
     const uint32_t jj = bx >> 3;
