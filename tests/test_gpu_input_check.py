@@ -139,6 +139,27 @@ def test_malformed_cu_seqlens(bad, check_env):
         moba.moba_dense_causal_fwd(q, k, v, cud)
 
 
+def test_malformed_cu_seqlens_strided_output(check_env):
+    """The NaN written for rejected cu_seqlens reaches every pass's output
+    rows through the output strides (an output inside a wider buffer, one kv
+    head per pass), and nothing outside them."""
+    import torch
+    inp, q, k, v, cu = inputs()
+    T, hq = q.shape[0], q.shape[1]
+    cud = torch.tensor([0, 3000, 2500, T], dtype=torch.int32, device="cuda")
+    sh = moba.shape_of(q, k, cud)
+    ws = torch.empty(moba.moba_fwd_workspace_size(sh, B, K, 1), dtype=torch.uint8,
+                     device="cuda")
+    buf = torch.full((T, hq + 2, 128), 7.0, dtype=q.dtype, device="cuda")
+    out = buf[:, 1:hq + 1]
+    lse = torch.zeros((hq, T), dtype=torch.float32, device="cuda")
+    os.environ["MOBA_CHECK"] = "0"
+    moba.moba_fwd_strided(q, k, v, cud, B, K, ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert all_nan(out, lse)
+    assert bool((buf[:, 0] == 7.0).all()) and bool((buf[:, hq + 1] == 7.0).all())
+
+
 def test_backward_and_decode_with_an_understated_hint():
     import torch
     inp, q, k, v, cu = inputs()
