@@ -338,7 +338,7 @@ template <typename TO>
 __global__ __launch_bounds__(256) void merge_kernel(const TO *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
                                                     const int32_t *__restrict__ cu, int S,
-                                                    int64_t T_, int Hq, int h0, int Hp, int B,
+                                                    int64_t T_, int h0, int Hp, int B,
                                                     int k, const int32_t *__restrict__ status,
                                                     TO *__restrict__ out, RowHead os,
                                                     float *__restrict__ lse_out) {
@@ -525,11 +525,11 @@ hipError_t launch_merge(const Problem &pb, const Work &w, int g0, void *out, flo
   const int h0 = g0 * pb.G;
   if (pb.bf16)
     merge_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)w.part_o, w.part_lse, cu, pb.S,
-                                              pb.T, pb.Hq, h0, pb.Hp, pb.B, pb.k, w.status,
+                                              pb.T, h0, pb.Hp, pb.B, pb.k, w.status,
                                               (__bf16 *)out, pb.os, lse);
   else
     merge_kernel<float><<<grid, 256, 0, s>>>((const float *)w.part_o, w.part_lse, cu, pb.S, pb.T,
-                                             pb.Hq, h0, pb.Hp, pb.B, pb.k, w.status, (float *)out,
+                                             h0, pb.Hp, pb.B, pb.k, w.status, (float *)out,
                                              pb.os, lse);
   return hipGetLastError();
 }
