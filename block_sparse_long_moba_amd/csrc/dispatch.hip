@@ -10,8 +10,9 @@
 // gate's matrix-core kernel already adds its own and marks them counted, and
 // then this pass returns at once), one exclusive scan (items, and tiles of
 // the attention kernel's query rows), and a scatter that reserves a range
-// per (workgroup, bin) and fills it from LDS cursors; a record per tile
-// follows the scan. Item order inside a bin is unspecified; every consumer
+// per (workgroup, bin) and fills it, through an LDS staging area grouped by
+// bin where the workgroup's entries fit (else from LDS cursors, one scattered
+// store per item); a record per tile follows the scan. Item order inside a bin is unspecified; every consumer
 // treats a bin's items independently.
 #include "moba_internal.h"
 
@@ -144,6 +145,101 @@ __device__ uint32_t scan1024(uint32_t x, uint32_t *wsum) {
   return r;
 }
 
+// Scatter with the workgroup's items staged in LDS, grouped by bin, so that
+// each (workgroup, bin) range of items is written by consecutive lanes to
+// consecutive addresses. A workgroup of 1024 threads takes R rows of one
+// block (R * Hp * k <= kStageEntries); each thread keeps its kStagePer idx
+// entries in registers. The LDS histogram's atomics return each entry's rank
+// within its bin; an exclusive scan of the counts gives every bin's start in
+// the staging area, one global atomic per (workgroup, bin) its range in
+// items, and the entry is placed at start + rank. The staged entries are then
+// written out in staging order.
+constexpr int kStageThreads = 1024;
+constexpr int kStagePer = 32;                               // idx entries per thread
+constexpr int kStageEntries = kStageThreads * kStagePer;    // 32768 (128 KiB staged)
+constexpr int kStageBins = 2048;                            // local bins (P * c)
+constexpr int kStageFBits = 15;                             // bits of a local entry index
+
+__global__ __launch_bounds__(kStageThreads) void dispatch_staged_kernel(
+    const int32_t *__restrict__ idx, const int4 *__restrict__ info, int64_t NBb, int Hp, int G,
+    int k, int R, Div by_kG, Div by_P, const uint32_t *__restrict__ bin_off,
+    uint32_t *__restrict__ cursor, uint32_t *__restrict__ items) {
+  const int64_t gb = blockIdx.x;
+  const int4 bi = info[gb];
+  const int r0 = (int)blockIdx.y * R;
+  if (bi.x < 0 || r0 >= bi.z) return;
+  const int c = bi.w;
+  if (c == 0 || k == 1) return;  // no earlier blocks to dispatch
+  const int P = Hp / G;
+  const int nbins = P * c;
+  if (nbins > kStageBins) return;  // never: the launcher picks this kernel only when they fit
+  __shared__ uint32_t start[kStageBins];  // counts, then each bin's first staging slot
+  __shared__ uint32_t delta[kStageBins];  // item position - staging slot, per bin
+  __shared__ uint32_t stage[kStageEntries];
+  __shared__ uint32_t wsum[16];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nbins; i += kStageThreads) start[i] = 0;
+  __syncthreads();
+  const int rows = min(R, bi.z - r0);
+  const int64_t f0 = (bi.y + (int64_t)r0) * Hp * k;
+  const uint32_t nf = (uint32_t)(rows * Hp * k);  // <= kStageEntries
+  const int32_t *run = idx + f0;
+  int32_t j[kStagePer];
+#pragma unroll
+  for (int u = 0; u < kStagePer; ++u) {
+    const uint32_t f = (uint32_t)(u * kStageThreads + tid);
+    j[u] = f < nf ? run[f] : -1;
+  }
+  // (local bin, rank within the bin) of each entry; ~0 for no earlier block
+  uint32_t br[kStagePer];
+#pragma unroll
+  for (int u = 0; u < kStagePer; ++u) {
+    br[u] = ~0u;
+    if (j[u] >= 0 && j[u] < c) {
+      const uint32_t f = (uint32_t)(u * kStageThreads + tid);
+      const uint32_t rg = by_kG.div(f);
+      const uint32_t bin = (rg - by_P.div(rg) * (uint32_t)P) * (uint32_t)c + (uint32_t)j[u];
+      br[u] = (bin << 16) | atomicAdd(&start[bin], 1u);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the counts: two bins per thread
+  const uint32_t c0 = 2 * tid < nbins ? start[2 * tid] : 0u;
+  const uint32_t c1 = 2 * tid + 1 < nbins ? start[2 * tid + 1] : 0u;
+  const uint32_t incl = scan1024(c0 + c1, wsum);
+  const uint32_t s0 = incl - c0 - c1;
+  const int64_t first = gb - c;
+  if (2 * tid < nbins) {
+    start[2 * tid] = s0;
+    if (c0) {
+      const int64_t b = (int64_t)((2 * tid) / c) * NBb + first + (2 * tid) % c;
+      delta[2 * tid] = bin_off[b] + atomicAdd(&cursor[b], c0) - s0;
+    }
+  }
+  if (2 * tid + 1 < nbins) {
+    start[2 * tid + 1] = s0 + c0;
+    if (c1) {
+      const int64_t b = (int64_t)((2 * tid + 1) / c) * NBb + first + (2 * tid + 1) % c;
+      delta[2 * tid + 1] = bin_off[b] + atomicAdd(&cursor[b], c1) - (s0 + c0);
+    }
+  }
+  if (tid == kStageThreads - 1) wsum[0] = incl;  // entries staged
+  __syncthreads();
+  const uint32_t nstaged = wsum[0];
+#pragma unroll
+  for (int u = 0; u < kStagePer; ++u)
+    if (br[u] != ~0u) {
+      const uint32_t bin = br[u] >> 16;
+      stage[start[bin] + (br[u] & 0xffffu)] =
+          (bin << kStageFBits) | (uint32_t)(u * kStageThreads + tid);
+    }
+  __syncthreads();
+  for (uint32_t s = tid; s < nstaged; s += kStageThreads) {
+    const uint32_t e = stage[s];
+    items[delta[e >> kStageFBits] + s] = (uint32_t)(f0 + (e & ((1u << kStageFBits) - 1u)));
+  }
+}
+
 // Exclusive scans of the bin counts (item offsets) and of their tile counts
 // (tiles of `rows` query rows); resets the scatter cursors.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const uint32_t *__restrict__ count,
@@ -219,6 +315,17 @@ hipError_t launch_dispatch(const Problem &pb, const Work &w, hipStream_t s) {
       w.tile_off, w.bin_off, w.blk_info, pb.NBb, nbins, w.max_tiles, (uint32_t)pb.rows,
       w.tile_rec);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int per_row = pb.Hp * pb.k;
+  if (per_row <= kStageEntries && (int64_t)pb.P * pb.maxblk <= kStageBins) {
+    // as many rows per workgroup as the staging area holds, spread evenly
+    const int rmax = kStageEntries / per_row;
+    const int nwg = (pb.B + rmax - 1) / rmax;
+    const int R = (pb.B + nwg - 1) / nwg;
+    dispatch_staged_kernel<<<dim3((unsigned)pb.NBb, (unsigned)nwg), kStageThreads, 0, s>>>(
+        w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k, R, by_kG, by_P, w.bin_off, w.cursor,
+        w.items);
+    return hipGetLastError();
+  }
   dispatch_kernel<true><<<grid, 256, lds, s>>>(w.idx, w.blk_info, pb.NBb, pb.Hp, pb.G, pb.k, by_kG,
                                              by_P, w.counted, w.bin_count, w.bin_off, w.cursor,
                                              w.items);

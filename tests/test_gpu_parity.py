@@ -202,6 +202,62 @@ def test_stages_meanpool_gate_dispatch_partials():
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
+def dispatch_expected(gidx, cu_seqlens, B, k, G, NBb):
+    """(bin, item) pairs the dispatch must produce from a pass's selection:
+    every slot holding an earlier block of its row's sequence, in the bin of
+    (kv head of the pass, global block)."""
+    T, Hp, _ = gidx.shape
+    first = oracle.block_first(cu_seqlens, B)
+    seq_of = np.searchsorted(cu_seqlens, np.arange(T), side="right") - 1
+    own = (np.arange(T) - cu_seqlens[seq_of]) // B  # the row's own block
+    j = gidx.astype(np.int64)
+    ok = (j >= 0) & (j < own[:, None, None])
+    t_i, h_i, s_i = np.nonzero(ok)
+    bins = (h_i // G) * NBb + first[seq_of[t_i]] + j[t_i, h_i, s_i]
+    items = (t_i * Hp + h_i) * k + s_i
+    return bins.astype(np.int64), items.astype(np.int64)
+
+
+@pytest.mark.parametrize("case", [
+    # lengths, Hq, Hkv, B, k, kv heads per pass
+    ([20000, 3001], 32, 8, 512, 8, 8),   # 256 entries per row: 128 rows per staged workgroup
+    ([9000], 8, 2, 256, 4, 1),           # 32 entries per row: whole blocks per staged workgroup
+    ([140000], 4, 2, 64, 3, 2),          # 2 x 2188 bins: the per-item scatter
+], ids=["staged_128rows", "staged_wholeblock", "many_bins"])
+def test_dispatch_regroups_the_selection(case):
+    """The dispatch's bins hold exactly the selection's earlier-block slots."""
+    import torch
+    lengths, hq, hkv, B, k, P = case
+    note("case %s" % (case,))
+    inp = host_inputs(lengths, hq, hkv, "bf16", B, k, 41)
+    d = Dev(inp, B, k, kv_heads_per_pass=P)
+    sh, lay = d.shape, d.lay
+    T = inp.q.shape[0]
+    Hp, G = lay.q_heads_per_pass, hq // hkv
+    NBb = lay.num_blocks_bound
+    nbins = lay.kv_heads_per_pass * NBb
+    moba.moba_seqtable(d.cu, sh, B, lay, d.ws)
+    moba.moba_meanpool(d.kk, sh, B, lay, d.ws)
+    for g0 in range(0, hkv, lay.kv_heads_per_pass):
+        moba.moba_gate(d.q, sh, B, k, lay, d.ws, g0)
+        moba.moba_dispatch(sh, B, k, lay, d.ws, g0)
+        torch.cuda.synchronize()
+        gidx = d.view(lay.idx_offset, T * Hp * k, torch.int32).view(T, Hp, k).cpu().numpy()
+        bins = d.view(lay.bins_offset, 2 * nbins + 1, torch.int32).cpu().numpy().view(np.uint32)
+        count, off = bins[:nbins].astype(np.int64), bins[nbins:2 * nbins + 1].astype(np.int64)
+        assert np.all(np.diff(off) == count)
+        eb, ei = dispatch_expected(gidx, inp.cu_seqlens, B, k, G, NBb)
+        assert int(off[-1]) == len(ei)
+        items = d.view(lay.items_offset, max(len(ei), 1), torch.int32).cpu().numpy()
+        items = items.view(np.uint32)[:len(ei)].astype(np.int64)
+        got_bin = np.repeat(np.arange(nbins), count)
+        assert np.array_equal(np.bincount(eb, minlength=nbins), count)
+        got = np.sort(got_bin * (T * Hp * k) + items)
+        want = np.sort(eb * (T * Hp * k) + ei)
+        assert np.array_equal(got, want)
+        note("pass %d: %d items in %d bins" % (g0, len(ei), int((count > 0).sum())))
+
+
 def test_pass_size_and_determinism():
     import torch
     inp = host_inputs([3000, 1100], 16, 4, "bf16", 256, 4, 31)
