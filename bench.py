@@ -143,6 +143,9 @@ def main():
                     "when q, k and v together are below 4 GiB)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured copy and GEMM ceilings")
+    ap.add_argument("--max-workspace-gib", type=float, default=48.0,
+                    help="largest forward workspace: the kv heads per pass are halved "
+                    "from all of them until the workspace fits")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: there is no multi-GPU path (the forward pass would "
@@ -212,7 +215,7 @@ def forward_bench(args, name, headline):
     q, kk, v, cu = (to_device(x) for x in (inp.q, inp.k, inp.v, inp.cu_seqlens))
     shape = moba.shape_of(q, kk, cu, max_seqlen=max(w.lengths))
     P = Hkv
-    while P > 1 and moba.moba_fwd_workspace_size(shape, B, k, P) > (48 << 30):
+    while P > 1 and moba.moba_fwd_workspace_size(shape, B, k, P) > args.max_workspace_gib * 2**30:
         P //= 2
     lay = moba.moba_plan(shape, B, k, P)
     ws = torch.empty(lay.total_bytes, dtype=torch.uint8, device="cuda")
