@@ -16,6 +16,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "moba_internal.h"
 
@@ -163,6 +164,22 @@ __global__ __launch_bounds__(256) void decode_gate_kernel(const T *__restrict__ 
   }
 }
 
+// Sum over each row of 16 lanes by DPP (in-register lane exchange): pairs,
+// quads, then the two quads of each half (mirror within 8) and the two halves
+// (mirror within 16). Each step adds two equal-valued operands in either
+// order, so every lane of the row ends with the same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value,
+                                                      0xf, 0xf, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror: the other quad
+  x += dpp(x, std::integral_constant<int, 0x140>{});  // row_mirror: the other half row
+  return x;
+}
+
 // Attention: one workgroup per (sequence, kv head g, block j <= c). 16 lanes
 // cover one key row (8 dims each, 256 contiguous bytes); 16 key groups walk
 // the block's rows (the own block up to the query's row) with an online
@@ -235,21 +252,42 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
         for (int e = 0; e < 8; ++e) qv[qi][e] *= scale_log2;  // scores in log2 units
       }
     }
-    auto consume = [&](const float (&kf)[8], const float (&vf)[8]) {
+    // one online-softmax update per group of NU keys: their scores, one
+    // maximum, one rescale of the state, then the NU weighted values (rows
+    // are unpacked from their loaded form one at a time)
+    using Raw = typename Row8<T>::Raw;
+    auto consume = [&](auto nu_c, const Raw *kr, const Raw *vr) {
+      constexpr int NU = decltype(nu_c)::value;
 #pragma unroll
       for (int qi = 0; qi < MH; ++qi) {
         if (qi >= nq) break;
-        float d = 0.f;
+        float d[NU];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[qi][e], kf[e], d);
+        for (int u = 0; u < NU; ++u) {
+          float kf[8];
+          Row8<T>::unpack(kr[u], kf);
+          float x = 0.f;
 #pragma unroll
-        for (int o = kDecKeyLanes / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, kDecKeyLanes);
-        const float mn = fmaxf(m[qi], d);
+          for (int e = 0; e < 8; ++e) x = fmaf(qv[qi][e], kf[e], x);
+          d[u] = row16_sum(x);
+        }
+        float mn = m[qi];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) mn = fmaxf(mn, d[u]);
         const float alpha = __builtin_amdgcn_exp2f(m[qi] - mn);
-        const float p = __builtin_amdgcn_exp2f(d - mn);
-        l[qi] = l[qi] * alpha + p;
+        float ps = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[qi][e] = fmaf(acc[qi][e], alpha, p * vf[e]);
+        for (int e = 0; e < 8; ++e) acc[qi][e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          const float p = __builtin_amdgcn_exp2f(d[u] - mn);
+          ps += p;
+          float vf[8];
+          Row8<T>::unpack(vr[u], vf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[qi][e] = fmaf(p, vf[e], acc[qi][e]);
+        }
+        l[qi] = fmaf(l[qi], alpha, ps);
         m[qi] = mn;
       }
     };
@@ -257,25 +295,18 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
     constexpr int U = 4;
     int key = kg;
     for (; key + (U - 1) * kDecGroups < nk; key += U * kDecGroups) {
-      typename Row8<T>::Raw kr[U], vr[U];
+      Raw kr[U], vr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         kr[u] = Row8<T>::load_raw(kb + (int64_t)(key + u * kDecGroups) * kstride);
         vr[u] = Row8<T>::load_raw(vb + (int64_t)(key + u * kDecGroups) * kstride);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float kf[8], vf[8];
-        Row8<T>::unpack(kr[u], kf);
-        Row8<T>::unpack(vr[u], vf);
-        consume(kf, vf);
-      }
+      consume(std::integral_constant<int, U>{}, kr, vr);
     }
     for (; key < nk; key += kDecGroups) {
-      float kf[8], vf[8];
-      Row8<T>::load(kb + (int64_t)key * kstride, kf);
-      Row8<T>::load(vb + (int64_t)key * kstride, vf);
-      consume(kf, vf);
+      const Raw kr = Row8<T>::load_raw(kb + (int64_t)key * kstride);
+      const Raw vr = Row8<T>::load_raw(vb + (int64_t)key * kstride);
+      consume(std::integral_constant<int, 1>{}, &kr, &vr);
     }
 #pragma unroll
     for (int qi = 0; qi < MH; ++qi) {
