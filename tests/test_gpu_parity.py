@@ -93,6 +93,9 @@ SMALL = [
     ([8192],                 4,  1, "bf16",  64, 33, 65),
     ([8192],                 4,  2, "bf16",  64, 17, 66),
     ([6000],                 2,  2, "fp32",  64, 33, 67),
+    # 32 query heads x top-k 5 = 160 idx entries per row: the staged
+    # dispatch splits each 256-row block over two workgroups of 128 rows
+    ([3000, 1000],          32,  8, "bf16", 256,  5, 68),
 ]
 
 
